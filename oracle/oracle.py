@@ -1,0 +1,374 @@
+"""Float64 CPU oracle for the block-FP8 mixture-of-experts expert computation.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may use this module. The HIP library never calls it, it imports nothing from the
+library, and the two share no code: the only thing both sides see is the seeded inputs.
+
+It is deliberately plain numpy: a 256-entry e4m3 table built from the closed form,
+whole-expert dequantisation, float64 matrix products, an explicit loop over (token, slot)
+pairs, and a second, dense all-experts loop. Nothing is blocked, fused or reordered.
+
+Sources (the three pages; each function names the passage it follows):
+  [gather] gaudi-cookbook, fixes page "fp8-moe-gather": sections Problem, The fix.
+  [tpu]    tpu-inference PR #3040 "Add another fused EP MoE kernels": review of the w1
+           weight/scale DMA (gate half first, up half second).
+  [cpu]    FreeToken PR #662 "serve block-fp8 experts on the cpu and hybrid backends": the
+           PR body (bank format, e4m3 exactness), commit "honor padded fp8 scale strides",
+           commit "add float64 parity reference", the final description (Kernels).
+
+Pins (tests/test_oracle_*.py, run without a GPU):
+  e4m3_lut          closed form vs the fp16-bit identity of [cpu] Kernels, vs torch's
+                    float8_e4m3fn, bf16 carries every finite code, range 2^-9..448.
+  e4m3_encode       vs torch's float8_e4m3fn cast on every midpoint +-1 ulp and at random;
+                    saturation and signed zero by definition.
+  quantize_rows     hand-checked rows (power-of-two amax, zero row).
+  dequant_expert    padded-stride invariance with NaN in the padding; power-of-two codes
+                    with unit scales give exact small integers; a pure-Python scalar loop.
+  route             brute-force sort by (-logit, id); k=E gives the full softmax.
+  sort_pairs        brute-force stable counting sort.
+  forward           pure-Python scalar loops on tiny shapes; dense == gathered;
+                    unrouted experts contribute exactly zero; E=1,k=1 is a textbook SwiGLU
+                    FFN (torch); expert permutation and token independence invariants.
+  w8a8 flags        parity unpinned beyond the self-consistency checks: the ambiguity
+                    window is an analysis bound (documented), not a value the pages give.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 128
+E4M3_MAX = 448.0
+
+
+# ----------------------------------------------------------------------------- e4m3
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP e4m3fn byte: sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+
+    Exponent field 0 is subnormal, m * 2^-9; 0x7F and 0xFF are NaN; everything else is
+    2^(e-7) * (1 + m/8). The range 2^-9..448 is the one [cpu] PR body gives for e4m3.
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        mag = m * 2.0 ** -9
+    else:
+        mag = 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return -mag if s else mag
+
+
+_LUT = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+_POS = _LUT[:0x7F].copy()  # codes 0x00..0x7E: the non-negative finite values, increasing
+
+
+def e4m3_lut() -> np.ndarray:
+    """The 256-entry decode table ([cpu] PR body: the scalar tier decodes through one)."""
+    return _LUT.copy()
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round float32 values to the nearest finite e4m3 value; return the codes.
+
+    Ties go to the even mantissa, magnitudes past 448 saturate to 448, and the sign of
+    zero is kept. The step between neighbours is 2^(e-3) in the binade [2^e, 2^(e+1)) for
+    e >= -6 and 2^-9 below 2^-6 (the subnormals), so rounding is an integer rounding of
+    |v| / step. Pinned against torch's float8_e4m3fn cast.
+    """
+    v32 = np.asarray(v, dtype=np.float32)
+    a = np.abs(v32.astype(np.float64))
+    a = np.minimum(a, E4M3_MAX)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, -6)
+    step = np.ldexp(1.0, e - 3)
+    r = np.rint(a / step) * step  # np.rint rounds half to even
+    idx = np.searchsorted(_POS, r)
+    if not np.array_equal(_POS[np.minimum(idx, 0x7E)], r):
+        raise AssertionError("rounded value is not an e4m3 value")
+    codes = idx.astype(np.uint8) | (np.signbit(v32).astype(np.uint8) << 7)
+    return codes
+
+
+def e4m3_midpoint_distance(v32: np.ndarray):
+    """Distance from |v| to the midpoint of its bracketing e4m3 pair, and that pair's step.
+
+    Used for the W8A8 ambiguity flags: a value within the fp32 drift window of a midpoint
+    may round either way. Values at or past 448 have no midpoint above them.
+    """
+    a = np.abs(np.asarray(v32, dtype=np.float64))
+    hi_idx = np.clip(np.searchsorted(_POS, a, side="right"), 1, 0x7E)
+    lo, hi = _POS[hi_idx - 1], _POS[hi_idx]
+    dist = np.abs(a - 0.5 * (lo + hi))
+    dist = np.where(a >= E4M3_MAX, np.inf, dist)
+    return dist, hi - lo
+
+
+# ----------------------------------------------------------------------------- banks
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 is the upper half of an fp32 word."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _scales_f64(bank: dict) -> np.ndarray:
+    if bank["scale_dtype"] == "bf16":
+        return bf16_to_f64(bank["scales"])
+    return np.asarray(bank["scales"], dtype=np.float32).astype(np.float64)
+
+
+def block_scales(bank: dict, e: int) -> np.ndarray:
+    """Scale grid [ceil(N/128), ceil(K/128)] of expert e, read through the explicit strides.
+
+    The scale of block (n//128, k//128) sits at e*expert_stride + (n//128)*row_stride +
+    k//128; the row stride may exceed ceil(K/128) ([cpu] commit "honor padded fp8 scale
+    strides": the stride is read off the bank, never recomputed).
+    """
+    s = _scales_f64(bank)
+    rows, cols = -(-bank["N"] // BLOCK), -(-bank["K"] // BLOCK)
+    base = e * bank["scale_expert_stride"]
+    r = np.arange(rows)[:, None] * bank["scale_row_stride"]
+    c = np.arange(cols)[None, :]
+    return s[base + r + c]
+
+
+def dequant_expert(bank: dict, e: int) -> np.ndarray:
+    """Expert e of a bank as float64 [N, K]: LUT[code] times its 128x128 block's scale.
+
+    [cpu] PR body: fp8-e4m3 row-major [rows, K], K contiguous per output row, one scale
+    per 128x128 block; the scale multiplies the decoded value.
+    """
+    N, K = bank["N"], bank["K"]
+    start = e * bank["expert_stride_bytes"]
+    codes = np.asarray(bank["codes"][start:start + N * K], dtype=np.uint8).reshape(N, K)
+    S = block_scales(bank, e)
+    S_full = np.repeat(np.repeat(S, BLOCK, axis=0)[:N], BLOCK, axis=1)[:, :K]
+    return _LUT[codes] * S_full
+
+
+# ----------------------------------------------------------------------------- routing
+
+def route(logits, top_k: int):
+    """Top-k experts per token and their renormalised softmax weights.
+
+    Experts are ordered by the key (-logit, expert id) on the fp32 logits, so ties go to
+    the lower id and slot 0 holds the largest logit. The weights are the softmax over the
+    selected logits, which equals the full softmax renormalised over the top-k, computed
+    in float64 as exp(l_j - l_0) / sum_i exp(l_i - l_0) with the sum taken in slot order.
+    Returns ids int32 [T, k], float64 weights [T, k] and the same rounded to fp32.
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    expert = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((expert, -lg[t].astype(np.float64)))[:top_k]
+        ids[t] = order
+        sel = lg[t, order].astype(np.float64)
+        ex = np.exp(sel - sel[0])
+        tot = 0.0
+        for j in range(top_k):
+            tot += ex[j]
+        w[t] = ex / tot
+    return ids, w, w.astype(np.float32)
+
+
+def sort_pairs(ids, E: int):
+    """Pair p = t*k + j grouped by expert, stable within an expert.
+
+    Returns counts [E], offsets [E+1] (exclusive prefix sums) and sorted_pairs [T*k].
+    """
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable").astype(np.int32)
+    return counts, offsets, order
+
+
+def gathered_count(T: int, E: int, top_k: int) -> int:
+    """g = min(E, T*top_k): the static number of expert slots on the gather path ([gather] The fix)."""
+    return min(E, T * top_k)
+
+
+# ----------------------------------------------------------------------------- activations
+
+def quantize_rows(x32):
+    """Dynamic per-row e4m3 quantisation, emulated exactly in fp32.
+
+    One scale per row: s = amax / 448 (fp32 division, correctly rounded), s = 1 for an
+    all-zero row, codes = e4m3_encode(x / s) with the division in fp32. The dequantised
+    row is LUT[code] * s. Rows are tokens for the gate/up GEMM and (token, slot) pairs
+    for the down GEMM ([gather] Who is affected: dynamic activation scales).
+    """
+    x = np.asarray(x32, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    v = (x / s[:, None]).astype(np.float32)
+    return e4m3_encode(v), s
+
+
+def silu(g):
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def _silu_grad(g):
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return sig * (1.0 + g * (1.0 - sig))
+
+
+# ----------------------------------------------------------------------------- forward
+
+def _expert_cache(w13: dict, w2: dict):
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = (dequant_expert(w13, e), dequant_expert(w2, e))
+        return cache[e]
+    return get
+
+
+# Drift window for the W8A8 re-quantisation of h. An fp32 evaluation of a K-term dot
+# product drifts from the exact value by about 2^-24 * sqrt(K) * (root sum of squares of
+# the terms); the window is SAFETY times that, plus 16 fp32 ulps of |h| for the
+# elementwise SiLU and product. Sequential fp32 summation over K=2048 reaches about 1.06
+# times the estimate at its worst and 128-blocked summation about 0.15 times, so SAFETY
+# leaves a margin of four over the least favourable order. It is an analysis bound, not
+# a value from the pages.
+SAFETY = 4.0
+U32 = 2.0 ** -24
+
+
+def h_drift(W13, xrow, g, u, h):
+    """Estimated fp32 drift of each h_i = silu(g_i) * u_i (see SAFETY)."""
+    I = g.shape[0]
+    K = xrow.shape[0]
+    sg = np.sqrt(((W13[:I] * xrow) ** 2).sum(axis=1))
+    su = np.sqrt(((W13[I:] * xrow) ** 2).sum(axis=1))
+    dg = np.abs(_silu_grad(g) * u) * sg
+    du = np.abs(silu(g)) * su
+    return SAFETY * U32 * (math.sqrt(K) * (dg + du) + 16.0 * np.abs(h))
+
+
+def _expert_mlp(W13, W2, xrow, act_mode: int):
+    """One (token, expert) pair: a = W13 x, h = silu(a[:I]) * a[I:], y = W2 h.
+
+    Gate rows are 0..I-1 and up rows I..2I-1 ([tpu] review of the w1 DMA: gate half
+    first, up half second). act_mode 1 re-quantises h per pair before the down GEMM and
+    flags the elements of h whose rounding an fp32 evaluation could decide either way:
+    |v - midpoint| <= drift(h_i)/s + |v| * drift(h_r)/amax, where r is the row's argmax
+    (the second term is the scale moving with amax).
+    """
+    I = W13.shape[0] // 2
+    a = W13 @ xrow
+    g, u = a[:I], a[I:]
+    h = silu(g) * u
+    if act_mode == 0:
+        return W2 @ h, None
+    h32 = h.astype(np.float32)
+    q, s = quantize_rows(h32[None, :])
+    q, s = q[0], s[0]
+    h_deq = _LUT[q] * np.float64(s)
+    d = h_drift(W13, xrow, g, u, h)
+    amax = float(np.max(np.abs(h32)))
+    r = int(np.argmax(np.abs(h32)))
+    v = (h32 / np.float32(s)).astype(np.float64)
+    dist, step = e4m3_midpoint_distance(v)
+    rho = d / float(s) + (np.abs(v) * d[r] / amax if amax > 0 else 0.0)
+    flags = dist <= rho
+    extra = dict(h_codes=q, h_scale=s, flags=flags, step=step)
+    return W2 @ h_deq, extra
+
+
+def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
+    """Gathered formulation: out[t] = sum_j w_tj * expert_{ids[t,j]}(x_t).
+
+    hidden_bf16: uint16 bf16 bits [T, H]; logits: fp32 [T, E]; w13: bank with N = 2I,
+    K = H; w2: bank with N = H, K = I (dicts as produced by the generators' numpy()).
+    act_mode 0 is W8A16 (x exact, h float64); act_mode 1 is W8A8: x quantised per token
+    and h per pair, both in fp32 emulation ([gather] The fix: the routed experts are
+    gathered, up/gate run as one GEMM and the down projection follows).
+    Returns a dict with out (float64 [T, H]), routing, and for act_mode 1 the x and h
+    quantisation and the per-output allowance for ambiguous h roundings.
+    """
+    x = bf16_to_f64(hidden_bf16)
+    T, H = x.shape
+    E = np.asarray(logits).shape[1]
+    ids, w, w32 = route(logits, top_k)
+    counts, offsets, sorted_pairs = sort_pairs(ids, E)
+    res = dict(ids=ids, w=w, w32=w32, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
+    if act_mode == 1:
+        xq, xs = quantize_rows(x.astype(np.float32))
+        x_used = _LUT[xq] * xs.astype(np.float64)[:, None]
+        res.update(x_codes=xq, x_scales=xs)
+    else:
+        x_used = x
+    get = _expert_cache(w13, w2)
+    out = np.zeros((T, H), dtype=np.float64)
+    allowance = np.zeros((T, H), dtype=np.float64)
+    n_flag = 0
+    h_codes, h_scales = {}, {}
+    for t in range(T):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            W13, W2 = get(e)
+            y, extra = _expert_mlp(W13, W2, x_used[t], act_mode)
+            out[t] += w[t, j] * y
+            if extra is not None:
+                f = extra["flags"]
+                n_flag += int(f.sum())
+                if f.any():
+                    amt = np.where(f, extra["step"] * float(extra["h_scale"]), 0.0)
+                    allowance[t] += abs(w[t, j]) * (np.abs(W2) @ amt)
+                h_codes[t * top_k + j] = extra["h_codes"]
+                h_scales[t * top_k + j] = extra["h_scale"]
+    res["out"] = out
+    if act_mode == 1:
+        res.update(allowance=allowance, n_flagged=n_flag, n_h=T * top_k * (w13["N"] // 2),
+                   h_codes=h_codes, h_scales=h_scales)
+    return res
+
+
+def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
+    """Dense all-experts formulation: out[t] = sum_e C[t, e] * expert_e(x_t).
+
+    C is the [T, E] combine matrix, zero off the routes. Every expert is evaluated on
+    every token, as the stock op reads every local expert ([gather] Problem). Returns the
+    float64 output [T, H].
+    """
+    x = bf16_to_f64(hidden_bf16)
+    T, H = x.shape
+    E = np.asarray(logits).shape[1]
+    ids, w, _ = route(logits, top_k)
+    C = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        for j in range(top_k):
+            C[t, ids[t, j]] = w[t, j]
+    if act_mode == 1:
+        xq, xs = quantize_rows(x.astype(np.float32))
+        x_used = _LUT[xq] * xs.astype(np.float64)[:, None]
+    else:
+        x_used = x
+    out = np.zeros((T, H), dtype=np.float64)
+    for e in range(E):
+        W13, W2 = dequant_expert(w13, e), dequant_expert(w2, e)
+        for t in range(T):
+            y, _ = _expert_mlp(W13, W2, x_used[t], act_mode)
+            out[t] += C[t, e] * y
+    return out
+
+
+def routed_experts(ids) -> np.ndarray:
+    """Distinct experts a routing touches (their bytes are what the gather path reads)."""
+    return np.unique(np.asarray(ids).ravel())

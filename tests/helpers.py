@@ -1,0 +1,75 @@
+"""Helpers shared by the tests: host views of generated cases and tolerance checks.
+
+Nothing here computes any part of the method; it converts tensors and measures errors.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# max|err| / max|ref| bar for floating-point outputs against the float64 oracle
+REL_TOL = 2e-3
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def case_numpy(case) -> dict:
+    return dict(
+        hidden=bf16_bits(case.hidden),
+        logits=case.logits.detach().cpu().numpy(),
+        w13=case.w13.numpy(),
+        w2=case.w2.numpy(),
+        top_k=case.top_k,
+    )
+
+
+def read_golden(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def torch_e4m3_table() -> np.ndarray:
+    """Decode of all 256 bytes by torch's float8_e4m3fn dtype (a library routine)."""
+    c = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x| (8 significant bits)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    return np.where(a > 0, np.ldexp(1.0, ex - 1 - 8), 0.0)
+
+
+def rel_err(out, ref) -> float:
+    ref = np.asarray(ref, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(out - ref))) / (den if den > 0 else 1.0)
+
+
+def rel_err_bf16(out, ref) -> float:
+    """Error beyond the bf16 output rounding, relative to max|ref|.
+
+    Rounding an exact result to bf16 alone moves it by up to half a bf16 ulp, which is
+    up to 2^-8 of the value and so more than the 2e-3 bar; that rounding is subtracted
+    before the comparison.
+    """
+    ref = np.asarray(ref, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    slack = bf16_half_ulp(np.maximum(np.abs(out), np.abs(ref)))
+    excess = np.maximum(0.0, np.abs(out - ref) - slack)
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(excess)) / (den if den > 0 else 1.0)

@@ -1,0 +1,254 @@
+"""Pins for the oracle's routing, sort and forward (CPU only).
+
+Each check is independent of the oracle's own code: brute-force Python loops with
+torch's float8 decode, library routines (torch, scipy) on special cases, and
+invariants that any correct implementation satisfies.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import bf16_bits, case_numpy, torch_e4m3_table
+
+
+def _bf16_to_float_list(bits):
+    t = torch.from_numpy(np.asarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def brute_route(logits_row, k):
+    E = len(logits_row)
+    order = sorted(range(E), key=lambda e: (-float(logits_row[e]), e))[:k]
+    ex = [math.exp(float(logits_row[e]) - float(logits_row[order[0]])) for e in order]
+    tot = sum(ex)
+    return order, [v / tot for v in ex]
+
+
+def brute_forward(hidden_bits, logits, w13, w2, k):
+    """Scalar loops: per-element decode (torch's float8 table), per-element scale lookup."""
+    tab = torch_e4m3_table()
+    x = _bf16_to_float_list(hidden_bits)
+    T, H = x.shape
+
+    def scale_of(bank, e, n, kk):
+        idx = e * bank["scale_expert_stride"] + (n // 128) * bank["scale_row_stride"] + kk // 128
+        v = bank["scales"][idx]
+        if bank["scale_dtype"] == "bf16":
+            return float(_bf16_to_float_list(np.array([v]))[0])
+        return float(v)
+
+    def weight(bank, e, n, kk):
+        c = int(bank["codes"][e * bank["expert_stride_bytes"] + n * bank["K"] + kk])
+        return tab[c] * scale_of(bank, e, n, kk)
+
+    I = w13["N"] // 2
+    out = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        order, ws = brute_route(logits[t], k)
+        for e, wt in zip(order, ws):
+            a = []
+            for n in range(2 * I):
+                acc = 0.0
+                for kk in range(H):
+                    acc += weight(w13, e, n, kk) * x[t][kk]
+                a.append(acc)
+            h = [a[i] / (1.0 + math.exp(-a[i])) * a[I + i] for i in range(I)]
+            for n in range(H):
+                acc = 0.0
+                for i in range(I):
+                    acc += weight(w2, e, n, i) * h[i]
+                out[t][n] += wt * acc
+    return np.array(out)
+
+
+def _tiny_case(T=2, E=4, top_k=2, scale_dtype=torch.float32, seed=1, pad="none"):
+    return W.make_case("tiny", T=T, seed=seed, E=E, H=256, I=128, top_k=top_k,
+                       scale_dtype=scale_dtype, pad=pad)
+
+
+def test_route_matches_bruteforce_with_ties():
+    g = np.random.default_rng(2)
+    logits = (np.round(g.normal(0, 1, (64, 16)) * 2) / 2).astype(np.float32)  # many ties
+    logits[0] = 0.5  # all tied: the lowest ids win
+    logits[1, :] = -0.0
+    logits[1, 3] = 0.0  # -0 and +0 compare equal
+    ids, w, w32 = O.route(logits, 5)
+    for t in range(64):
+        order, ws = brute_route(logits[t], 5)
+        assert list(ids[t]) == order
+        assert np.allclose(w[t], ws, rtol=1e-15, atol=0)
+    assert list(ids[0]) == [0, 1, 2, 3, 4]
+    assert list(ids[1]) == [0, 1, 2, 3, 4]
+    assert np.array_equal(w32, w.astype(np.float32))
+
+
+def test_route_k_equals_E_is_full_softmax():
+    g = np.random.default_rng(3)
+    logits = g.normal(0, 2, (20, 8)).astype(np.float32)
+    ids, w, _ = O.route(logits, 8)
+    sm = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for t in range(20):
+        assert np.allclose(w[t], sm[t, ids[t]], rtol=1e-13, atol=0)
+        assert np.all(np.diff(logits[t, ids[t]]) <= 0)
+
+
+def test_route_is_renormalised_full_softmax():
+    g = np.random.default_rng(4)
+    logits = g.normal(0, 1.5, (30, 256)).astype(np.float32)
+    ids, w, _ = O.route(logits, 8)
+    sm = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for t in range(30):
+        p = sm[t, ids[t]]
+        assert np.allclose(w[t], p / p.sum(), rtol=1e-12, atol=0)
+
+
+def test_sort_pairs_bruteforce():
+    g = np.random.default_rng(5)
+    E = 12
+    ids = np.stack([g.choice(E, 3, replace=False) for _ in range(40)]).astype(np.int32)
+    counts, offsets, sp = O.sort_pairs(ids, E)
+    flat = ids.ravel()
+    want = []
+    for e in range(E):
+        want += [p for p in range(flat.size) if flat[p] == e]
+    assert list(sp) == want
+    assert list(counts) == [int((flat == e).sum()) for e in range(E)]
+    assert offsets[0] == 0 and list(np.diff(offsets)) == list(counts)
+
+
+@pytest.mark.parametrize("scale_dtype", [torch.float32, torch.bfloat16])
+def test_forward_matches_scalar_loops(scale_dtype):
+    c = _tiny_case(scale_dtype=scale_dtype, pad="slab16")
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    ref = brute_forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("act_mode", [0, 1])
+def test_dense_equals_gathered(act_mode):
+    c = W.make_case("tiny", T=5, seed=7)
+    n = case_numpy(c)
+    g = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=act_mode)["out"]
+    d = O.forward_dense(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=act_mode)
+    assert np.max(np.abs(g - d)) <= 1e-12 * np.max(np.abs(d))
+
+
+def test_unrouted_experts_contribute_nothing():
+    c = W.make_case("tiny", T=2, seed=8)
+    n = case_numpy(c)
+    base = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    used = set(int(e) for e in base["ids"].ravel())
+    for bank in (n["w13"], n["w2"]):
+        for e in range(c.E):
+            if e in used:
+                continue
+            s = e * bank["expert_stride_bytes"]
+            bank["codes"][s:s + bank["N"] * bank["K"]] = 0x7F  # NaN codes
+            s = e * bank["scale_expert_stride"]
+            bank["scales"][s:s + bank["scale_expert_stride"]] = np.nan
+    assert len(used) < c.E
+    again = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    assert np.array_equal(base["out"], again["out"])
+
+
+def test_single_expert_is_swiglu():
+    """E=1, k=1: out = W2 (silu(Wg x) * (Wu x)), with torch doing dequant and products."""
+    c = _tiny_case(T=3, E=1, top_k=1, scale_dtype=torch.bfloat16)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], 1)
+
+    def deq(bank):
+        codes = bank.codes.view(bank.E, -1)[0, : bank.N * bank.K].view(bank.N, bank.K)
+        vals = codes.view(torch.float8_e4m3fn).to(torch.float64)
+        s = bank.scales.view(bank.E, -1)[0].view(-1, bank.scale_row_stride)[:, : bank.scale_cols]
+        s = s.to(torch.float64).repeat_interleave(128, 0)[: bank.N].repeat_interleave(128, 1)[:, : bank.K]
+        return vals * s
+
+    W13, W2 = deq(c.w13), deq(c.w2)
+    x = c.hidden.to(torch.float64)
+    I = c.I
+    g = x @ W13[:I].T
+    u = x @ W13[I:].T
+    y = (torch.nn.functional.silu(g) * u) @ W2.T
+    assert np.max(np.abs(res["out"] - y.numpy())) <= 1e-12 * float(y.abs().max())
+    assert np.all(res["w"] == 1.0)
+
+
+def test_expert_permutation_invariance():
+    c = W.make_case("tiny", T=4, seed=9)
+    n = case_numpy(c)
+    base = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)["out"]
+    perm = np.random.default_rng(0).permutation(c.E)  # new expert i is old expert perm[i]
+
+    def permute(bank):
+        b = dict(bank)
+        cs, ss = bank["expert_stride_bytes"], bank["scale_expert_stride"]
+        b["codes"] = np.concatenate([bank["codes"][p * cs:(p + 1) * cs] for p in perm])
+        b["scales"] = np.concatenate([bank["scales"][p * ss:(p + 1) * ss] for p in perm])
+        return b
+
+    out = O.forward(n["hidden"], n["logits"][:, perm], permute(n["w13"]), permute(n["w2"]), c.top_k)["out"]
+    assert np.array_equal(out, base)
+
+
+def test_token_independence():
+    c = W.make_case("tiny", T=6, seed=10)
+    n = case_numpy(c)
+    full = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)["out"]
+    for t in (0, 3, 5):
+        one = O.forward(n["hidden"][t:t + 1], n["logits"][t:t + 1], n["w13"], n["w2"], c.top_k)["out"]
+        assert np.array_equal(one[0], full[t])
+
+
+def test_w8a8_matches_torch_quantised_reference():
+    """act_mode 1 against torch: fp32 division for scales, torch's e4m3 cast for codes."""
+    c = _tiny_case(T=3, E=4, top_k=2, scale_dtype=torch.bfloat16)
+    c = W.make_case("decode", T=3, seed=2, E=4, H=256, I=128, top_k=2)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=1)
+
+    def deq(bank, e):
+        codes = bank.codes.view(bank.E, -1)[e, : bank.N * bank.K].view(bank.N, bank.K)
+        vals = codes.view(torch.float8_e4m3fn).to(torch.float64)
+        s = bank.scales.view(bank.E, -1)[e].view(-1, bank.scale_row_stride)[:, : bank.scale_cols]
+        s = s.to(torch.float64).repeat_interleave(128, 0)[: bank.N].repeat_interleave(128, 1)[:, : bank.K]
+        return vals * s
+
+    def q(x32):
+        s = x32.abs().amax(dim=-1, keepdim=True) / torch.tensor(448.0)
+        codes = (x32 / s).to(torch.float8_e4m3fn)
+        return codes, s
+
+    x32 = c.hidden.to(torch.float32)
+    xq, xs = q(x32)
+    assert np.array_equal(xq.view(torch.uint8).numpy(), res["x_codes"])
+    xd = xq.to(torch.float64) * xs.to(torch.float64)
+    out = torch.zeros((c.T, c.H), dtype=torch.float64)
+    ids = torch.from_numpy(res["ids"].astype(np.int64))
+    w = torch.from_numpy(res["w"])
+    I = c.I
+    for t in range(c.T):
+        for j in range(c.top_k):
+            e = int(ids[t, j])
+            W13, W2 = deq(c.w13, e), deq(c.w2, e)
+            a = W13 @ xd[t]
+            h = torch.nn.functional.silu(a[:I]) * a[I:]
+            hq, hs = q(h.to(torch.float32))
+            assert np.array_equal(hq.view(torch.uint8).numpy(), res["h_codes"][t * c.top_k + j])
+            out[t] += w[t, j] * (W2 @ (hq.to(torch.float64) * hs.to(torch.float64)))
+    assert np.max(np.abs(res["out"] - out.numpy())) <= 1e-12 * float(out.abs().max())
+
+
+def test_w8a8_ambiguity_flags_are_rare_on_gaussian_banks():
+    c = W.make_case("decode", T=2, seed=3, E=16, H=512, I=256, top_k=4)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=1)
+    assert res["n_flagged"] <= 0.01 * res["n_h"]
+    assert np.all(res["allowance"] >= 0)
