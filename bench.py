@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-FP8 MoE expert path on one MI355X.
+
+Default workload: single-stream decode, E=256 experts, H=2048, I=512, top_k=8, T=1, bf16
+hidden and output, fp8-e4m3 banks with bf16 128x128 block scales (rows padded to 16 B).
+The metric is routed-weight GB/s: the bytes of the distinct experts each forward routes
+to (codes plus their block scales), divided by the time per forward.
+
+A step is one whole forward (route, sort, GEMM1 + silu*up, GEMM2 + combine) over one
+batch of synthetic input already resident in HBM. Steps rotate over 64 pre-drawn
+routings and 4 replicas of the banks (about 3.2 GB), so the 256 MB Infinity Cache cannot
+serve a routed expert from an earlier step. The steps are captured into one HIP graph
+(64 forwards) and replayed back to back.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel's algorithmic bytes per launch over its mean duration,
+                timed with HIP events recorded around it on its own stream
+                (moe_fp8_block_forward_timed), against the 8 TB/s HBM peak;
+  cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--workload decode|sweep|large|prefill] [--T T]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-weight GB/s (% HBM peak) at decode; prefill tokens/s (% fp8 MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+CPU_REFERENCE_GBS = 53.7  # block-fp8 CPU MoE kernel, 2x Xeon Gold 6526Y (FreeToken PR #662)
+
+WORKLOADS = {
+    "decode": dict(T=1, desc="single-stream decode"),
+    "sweep": dict(T=12, desc="Zipf(1.1) popularity"),
+    "large": dict(T=1, desc="large-expert decode"),
+    "prefill": dict(T=4096, desc="prefill grouped GEMM"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--sets", type=int, default=64)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-steps", type=int, default=64, help="steps timed per kernel with events")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers from the HIP runtime (events the library records on its stream)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out[i] = ev.value
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_fp8_mixture_top_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path; runs on more than one GPU are not part of this "
+              "benchmark (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_fp8_mixture_top_amd as M
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = args.workload
+    T = args.T or WORKLOADS[wl]["T"]
+    shp = W.SHAPES[wl]
+    E, H, I, k = shp["E"], shp["H"], shp["I"], shp["top_k"]
+    S, R = args.sets, args.replicas
+    if wl == "large":
+        R = min(R, 1)  # 11.3 GB per replica; 256 experts x 44 MB already exceed the cache
+    print(f"[bench] workload {wl} T={T} E={E} H={H} I={I} top_k={k}: drawing {R} bank replicas, {S} input sets",
+          file=sys.stderr, flush=True)
+
+    banks = [W.make_banks(wl, seed=args.seed + 100 * r, device=dev) for r in range(R)]
+    cases = [W.make_case(wl, T=T, seed=args.seed + 1000 + i, device=dev, banks=banks[i % R]) for i in range(S)]
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    nbytes = max(M.workspace_size(T, E, H, I, k), 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    w13_b, w2_b = banks[0][0].expert_bytes, banks[0][1].expert_bytes
+
+    # routed experts of every set (their bytes are the metric's numerator)
+    d_e = []
+    for c in cases:
+        r = M.route(c.logits, k, sort=False)
+        d_e.append(int(torch.unique(r["ids"]).numel()))
+    torch.cuda.synchronize()
+    step_bytes = [d * (w13_b + w2_b) for d in d_e]
+
+    def step(i):
+        c = cases[i]
+        return M.forward(c.hidden, c.logits, c.w13, c.w2, k, out=outs[i], workspace=ws)[1]
+
+    info = step(0)
+    torch.cuda.synchronize()
+    print(f"[bench] path {info['path']}, {info['kernels']} kernels per forward", file=sys.stderr, flush=True)
+
+    # one graph of S forwards, plus S single-forward graphs for a remainder
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(S):
+            step(i)
+    singles = []
+    for i in range(S):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        singles.append(g)
+
+    def run(nsteps):
+        for _ in range(nsteps // S):
+            graph.replay()
+        for i in range(nsteps % S):
+            singles[i].replay()
+
+    def bytes_of(nsteps):
+        full, rem = divmod(nsteps, S)
+        return full * sum(step_bytes) + sum(step_bytes[:rem])
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    run(args.warmup)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    run(K)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / K
+    total_bytes = bytes_of(K)
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    tok_s = K * T / (ms * 1e-3)
+
+    # per-kernel durations: HIP events around every kernel, recorded by the library on the
+    # stream the kernels run on; a spin kernel first lets the host enqueue everything before
+    # the GPU reaches it, so no host gap falls inside a bracket
+    hip = Hip()
+    nk = info["kernels"]
+    KS = min(args.kernel_steps, S)
+    evs = [hip.events(2 * nk) for _ in range(KS)]
+    kinds = (ctypes.c_int32 * nk)()
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e8))
+    from block_fp8_mixture_top_amd import _lib as L
+
+    for i in range(KS):
+        c = cases[i]
+        b13, b2 = M.bank_struct(c.w13), M.bank_struct(c.w2)
+        o = M.make_opts()
+        ri = L.RunInfo()
+        L.check(M.lib().moe_fp8_block_forward_timed(
+            ctypes.c_void_p(c.hidden.data_ptr()), ctypes.c_void_p(c.logits.data_ptr()), ctypes.byref(b13),
+            ctypes.byref(b2), T, E, H, I, k, ctypes.c_void_p(outs[i].data_ptr()), L.MOE_BF16,
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None, None, ctypes.byref(o), ctypes.byref(ri),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), evs[i], 2 * nk, kinds))
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for j in range(nk):
+        name = L.KERNEL_NAMES.get(kinds[j], str(kinds[j]))
+        d = [hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(KS)]
+        per_kernel.setdefault(name, []).append(float(np.mean(d)))
+    for e_ in evs:
+        hip.destroy(e_)
+    per_kernel = {n: sum(v) for n, v in per_kernel.items()}  # ms per forward, summed over a kind's kernels
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+
+    mean_de = float(np.mean(d_e))
+    if info["path"] == "mfma":
+        flops = 6.0 * T * k * H * I
+        achieved = flops * (2.0 / 3.0 if dom == "gemm1" else 1.0 / 3.0) / (dom_ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / FP8_PEAK_TFLOPS, 4))
+    else:
+        # algorithmic bytes of one launch of the dominant kernel
+        if dom == "gemm1":
+            kb = mean_de * w13_b + T * H * 2 + T * k * I * 4
+        elif dom == "gemm2":
+            kb = mean_de * w2_b + T * k * I * 4 + T * H * 2
+        else:
+            kb = None
+        achieved = kb / (dom_ms * 1e-3) / 1e9 if kb else None
+        roofline = dict(bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
+    roofline["kernel"] = dom
+    roofline["kernel_ms"] = round(dom_ms, 5)
+    roofline["traffic"] = committed_traffic(dom, wl)
+    roofline["kernels_ms"] = {n: round(v, 5) for n, v in per_kernel.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline and wl != "prefill":
+        cpu = cpu_baseline(cases, k, args.cpu_seconds, w13_b + w2_b)
+
+    if wl == "prefill":
+        value, unit = tok_s, "tokens/s"
+    else:
+        value, unit = gbs, "GB/s"
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / CPU_REFERENCE_GBS, 2) if unit == "GB/s" and wl == "decode" else None,
+        "dtype": "fp8e4m3 x bf16 -> fp32" if info["path"] != "mfma" else "fp8e4m3 x fp8e4m3 -> fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl}: E={E} H={H} I={I} top_k={k} T={T}, bf16 hidden/out, fp8-e4m3 banks with "
+                        f"{banks[0][0].scale_dtype} 128x128 block scales",
+            "path": info["path"],
+            "kernels_per_forward": nk,
+            "routed_experts_mean": mean_de,
+            "routed_bytes_per_step": round(total_bytes / K),
+            "bank_replicas": R,
+            "input_sets": S,
+            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(tok_s, 1),
+            "wall_s": round(wall, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cases, k, seconds, expert_bytes):
+    """The float64 oracle (gathered formulation) on this host, on as many of the sets as
+    fit in about `seconds`; GB/s over the same routed bytes."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+
+    def host_bank(bank, experts):
+        codes = np.zeros(bank.codes.numel(), dtype=np.uint8)
+        st = bank.expert_stride_bytes
+        for e in experts:
+            codes[e * st:(e + 1) * st] = bank.codes[e * st:(e + 1) * st].cpu().numpy()
+        sc = bank.scales.cpu()
+        scales = sc.view(torch.int16).numpy().view(np.uint16) if bank.scale_dtype == "bf16" else sc.numpy()
+        return dict(codes=codes, scales=scales, scale_dtype=bank.scale_dtype, E=bank.E, N=bank.N, K=bank.K,
+                    expert_stride_bytes=st, scale_row_stride=bank.scale_row_stride,
+                    scale_expert_stride=bank.scale_expert_stride)
+
+    spent, nbytes, n = 0.0, 0, 0
+    for c in cases:
+        if spent >= seconds:
+            break
+        hid = c.hidden.cpu().view(torch.int16).numpy().view(np.uint16)
+        lg = c.logits.cpu().numpy()
+        ids, _, _ = O.route(lg, k)
+        used = [int(e) for e in O.routed_experts(ids)]
+        w13, w2 = host_bank(c.w13, used), host_bank(c.w2, used)
+        t0 = time.perf_counter()
+        O.forward(hid, lg, w13, w2, k)
+        spent += time.perf_counter() - t0
+        nbytes += len(used) * expert_bytes
+        n += 1
+    return {
+        "value": round(nbytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"{n} forwards of the same workload (float64 gathered oracle, {spent:.1f} s)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+"""Block-FP8 mixture-of-experts expert computation on MI355X (gfx950).
+
+A thin binding of the C ABI in include/moe_fp8_block.h: it checks tensor dtypes and
+devices, passes raw device pointers and torch's current HIP stream, and raises MoeError
+on a non-zero status. Every step of the computation runs in the library's HIP kernels;
+this module only marshals arguments. PyTorch supplies device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import (  # noqa: F401
+    MOE_BF16,
+    MOE_F32,
+    PATH_AUTO,
+    PATH_GATHER,
+    PATH_MFMA,
+    PATH_NAMES,
+    PATH_STREAM,
+    MoeError,
+)
+
+__all__ = [
+    "abi_version", "lib", "make_opts", "select_path", "route_workspace_size", "route", "workspace_size",
+    "forward", "quantize_rows", "decode_e4m3", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
+    "PATH_STREAM", "PATH_MFMA", "PATH_NAMES",
+]
+
+
+def lib() -> ctypes.CDLL:
+    return L.load()
+
+
+def abi_version() -> int:
+    return lib().moe_fp8_block_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_opts(force_path: Optional[int] = None, gate_ratio: Optional[float] = None,
+              mfma_min_tokens_per_expert: Optional[int] = None) -> L.Opts:
+    o = L.Opts()
+    L.check(lib().moe_fp8_block_default_opts(ctypes.byref(o)))
+    if force_path is not None:
+        o.force_path = int(force_path)
+    if gate_ratio is not None:
+        o.gate_ratio = float(gate_ratio)
+    if mfma_min_tokens_per_expert is not None:
+        o.mfma_min_tokens_per_expert = int(mfma_min_tokens_per_expert)
+    return o
+
+
+def _info_dict(info: L.RunInfo) -> dict:
+    return dict(path=PATH_NAMES[info.path], path_id=info.path, act_mode=info.act_mode, slots=info.slots,
+                kernels=info.kernels)
+
+
+def select_path(T: int, E: int, top_k: int, **opts) -> dict:
+    """The gate's decision for these sizes (host only)."""
+    info = L.RunInfo()
+    o = make_opts(**opts)
+    L.check(lib().moe_fp8_block_select_path(T, E, top_k, ctypes.byref(o), ctypes.byref(info)))
+    return _info_dict(info)
+
+
+def bank_struct(bank) -> L.Bank:
+    """A moe_fp8_bank from an object with codes/scales tensors and the stride fields."""
+    _need(bank.codes, "bank.codes", torch.uint8)
+    if bank.scales.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("bank.scales must be bfloat16 or float32")
+    if bank.scales.device != bank.codes.device or not bank.scales.is_contiguous():
+        raise ValueError("bank.scales must be contiguous and on the codes' device")
+    b = L.Bank()
+    b.codes = bank.codes.data_ptr()
+    b.expert_stride_bytes = int(bank.expert_stride_bytes)
+    b.scales = bank.scales.data_ptr()
+    b.scale_dtype = L.MOE_BF16 if bank.scales.dtype == torch.bfloat16 else L.MOE_F32
+    b.reserved = 0
+    b.scale_row_stride = int(bank.scale_row_stride)
+    b.scale_expert_stride = int(bank.scale_expert_stride)
+    return b
+
+
+def route_workspace_size(T: int, E: int, top_k: int) -> int:
+    return int(lib().moe_fp8_block_route_workspace_size(T, E, top_k))
+
+
+def route(logits: torch.Tensor, top_k: int, sort: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Top-k routing (and the token-to-expert sort) on the GPU."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    res = dict(ids=ids, weights=w)
+    counts = offsets = sorted_pairs = None
+    nbytes = 0
+    if sort:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        sorted_pairs = torch.empty(T * top_k, dtype=torch.int32, device=dev)
+        nbytes = route_workspace_size(T, E, top_k)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        res.update(counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
+    L.check(lib().moe_fp8_block_route(
+        _ptr(logits), T, E, top_k, _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets), _ptr(sorted_pairs),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(logits)))
+    return res
+
+
+def workspace_size(T: int, E: int, H: int, I: int, top_k: int, **opts) -> int:
+    o = make_opts(**opts)
+    return int(lib().moe_fp8_block_workspace_size(T, E, H, I, top_k, ctypes.byref(o)))
+
+
+def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out_dtype=torch.bfloat16,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            return_routing: bool = False, **opts):
+    """The expert computation for T tokens. Returns (out [T, H], info dict).
+
+    w13 / w2 are banks (objects with codes, scales, expert_stride_bytes, scale_row_stride,
+    scale_expert_stride); opts are force_path, gate_ratio, mfma_min_tokens_per_expert.
+    With return_routing the info dict also holds the ids and weights tensors.
+    """
+    _need(hidden, "hidden", torch.bfloat16)
+    dev = hidden.device
+    _need(logits, "logits", torch.float32, dev)
+    T, H = hidden.shape
+    E = logits.shape[1]
+    if logits.shape[0] != T:
+        raise ValueError("hidden and logits disagree on T")
+    I = w2.K
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H] float32 or bfloat16")
+    _need(out, "out", out.dtype, dev)
+    o = make_opts(**opts)
+    nbytes = int(lib().moe_fp8_block_workspace_size(T, E, H, I, top_k, ctypes.byref(o)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    b13, b2 = bank_struct(w13), bank_struct(w2)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    info = L.RunInfo()
+    L.check(lib().moe_fp8_block_forward(
+        _ptr(hidden), _ptr(logits), ctypes.byref(b13), ctypes.byref(b2), T, E, H, I, top_k, _ptr(out),
+        L.MOE_BF16 if out.dtype == torch.bfloat16 else L.MOE_F32, _ptr(workspace), workspace.numel(),
+        _ptr(ids), _ptr(w), ctypes.byref(o), ctypes.byref(info), _stream(hidden)))
+    d = _info_dict(info)
+    if return_routing:
+        d.update(ids=ids, weights=w)
+    return out, d
+
+
+def quantize_rows(x: torch.Tensor):
+    """Per-row dynamic e4m3 of a bf16 [rows, cols] tensor -> (codes uint8, scales float32)."""
+    _need(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    L.check(lib().moe_fp8_block_quantize_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def decode_e4m3(codes: torch.Tensor) -> torch.Tensor:
+    _need(codes, "codes", torch.uint8)
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    L.check(lib().moe_fp8_block_decode_e4m3(_ptr(codes), _ptr(out), codes.numel(), _stream(codes)))
+    return out
+
+
+def encode_e4m3(x: torch.Tensor) -> torch.Tensor:
+    _need(x, "x", torch.float32)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    L.check(lib().moe_fp8_block_encode_e4m3(_ptr(x), _ptr(out), x.numel(), _stream(x)))
+    return out

@@ -1,0 +1,441 @@
+// The C ABI: argument checks (all before any HIP call), the gather/grouped gate, workspace
+// carving and kernel dispatch. Declared in include/moe_fp8_block.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe_fp8_block.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_CHECK(expr, what)                   \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+moe_opts defaults() {
+  moe_opts o;
+  o.gate_ratio = 0.4f;
+  o.force_path = MOE_PATH_AUTO;
+  o.mfma_min_tokens_per_expert = 32;
+  o.reserved = 0;
+  return o;
+}
+
+int check_sizes(int T, int E, int top_k) {
+  if (T < 0) return fail(MOE_ERR_ARG, "T must be >= 0 (got %d)", T);
+  if (E < 1 || E > MOE_FP8_BLOCK_MAX_EXPERTS)
+    return fail(MOE_ERR_ARG, "E must be in [1, %d] (got %d)", MOE_FP8_BLOCK_MAX_EXPERTS, E);
+  if (top_k < 1 || top_k > E || top_k > MOE_FP8_BLOCK_MAX_TOPK)
+    return fail(MOE_ERR_ARG, "top_k must be in [1, min(E, %d)] (got %d, E=%d)", MOE_FP8_BLOCK_MAX_TOPK, top_k, E);
+  if ((int64_t)T * top_k > (int64_t)(1 << 28)) return fail(MOE_ERR_ARG, "T*top_k too large");
+  return MOE_OK;
+}
+
+int check_opts(const moe_opts* o) {
+  if (!(std::isfinite(o->gate_ratio) && o->gate_ratio >= 0.0f))
+    return fail(MOE_ERR_ARG, "gate_ratio must be finite and >= 0");
+  if (o->force_path < MOE_PATH_AUTO || o->force_path > MOE_PATH_MFMA)
+    return fail(MOE_ERR_ARG, "force_path %d is not a moe_path", o->force_path);
+  if (o->mfma_min_tokens_per_expert < 1) return fail(MOE_ERR_ARG, "mfma_min_tokens_per_expert must be >= 1");
+  if (o->reserved != 0) return fail(MOE_ERR_ARG, "moe_opts.reserved must be 0");
+  return MOE_OK;
+}
+
+// The gate (gaudi-cookbook "fp8-moe-gather", The fix): gather while T*top_k <= ratio*E.
+int gate(int T, int E, int top_k, const moe_opts& o) {
+  if (o.force_path != MOE_PATH_AUTO) return o.force_path;
+  const double P = (double)T * top_k;
+  if (P <= (double)o.gate_ratio * E) return MOE_PATH_GATHER;
+  if (P >= (double)o.mfma_min_tokens_per_expert * E) return MOE_PATH_MFMA;
+  return MOE_PATH_STREAM;
+}
+
+bool mfma_supported(int H, int I) {
+  const int nt = I / 64;
+  return (nt == 2 || nt == 4 || nt == 6 || nt == 8) && H % 128 == 0;
+}
+
+// Path actually run: the gate's choice, moved off a path the shapes do not fit only when
+// the caller left the choice to the gate.
+int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* path) {
+  int p = gate(T, E, top_k, o);
+  const bool forced = o.force_path != MOE_PATH_AUTO;
+  if (p == MOE_PATH_MFMA && !mfma_supported(H, I)) {
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs I in {128,256,384,512} (got I=%d)", I);
+    p = MOE_PATH_STREAM;
+  }
+  if (p == MOE_PATH_GATHER && !moe::gemm2_gather_supported(top_k, I)) {
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "GATHER path needs top_k*I <= 16384 (got %d*%d)", top_k, I);
+    p = MOE_PATH_STREAM;
+  }
+  *path = p;
+  return MOE_OK;
+}
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  }
+};
+
+// Workspace layout; offsets into the caller's buffer.
+struct Layout {
+  size_t ids, w, counts, offsets, sorted, act, n_act, tile_off, scratch;
+  size_t h, y, xq, xs, hq, hs, acc;
+  size_t total;
+};
+
+Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
+  Layout L{};
+  Carve c;
+  const size_t P = (size_t)T * top_k;
+  const size_t slots = P < (size_t)E ? P : (size_t)E;
+  L.ids = c.take(P * 4);
+  L.w = c.take(P * 4);
+  L.counts = c.take((size_t)E * 4);
+  L.offsets = c.take((size_t)(E + 1) * 4);
+  L.sorted = c.take(P * 4);
+  L.act = c.take((slots > 0 ? slots : 1) * 4);
+  L.n_act = c.take(4);
+  L.tile_off = c.take((size_t)(E + 1) * 4);
+  L.scratch = c.take(moe::sort_scratch_bytes((int)P, E));
+  if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) L.h = c.take(P * (size_t)I * 4);
+  if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);
+  if (path == MOE_PATH_MFMA) {
+    L.xq = c.take((size_t)T * H);
+    L.xs = c.take((size_t)T * 4);
+    L.hq = c.take(P * (size_t)I);
+    L.hs = c.take(P * 4);
+    L.acc = c.take((size_t)T * H * 4);
+  }
+  L.total = c.off;
+  return L;
+}
+
+int check_bank(const moe_fp8_bank* b, const char* name, int E, int64_t N, int64_t K) {
+  if (!b) return fail(MOE_ERR_ARG, "%s is NULL", name);
+  if (!b->codes || !b->scales) return fail(MOE_ERR_ARG, "%s.codes/scales is NULL", name);
+  if (b->scale_dtype != MOE_F32 && b->scale_dtype != MOE_BF16)
+    return fail(MOE_ERR_ARG, "%s.scale_dtype %d is not MOE_F32/MOE_BF16", name, b->scale_dtype);
+  if (b->reserved != 0) return fail(MOE_ERR_ARG, "%s.reserved must be 0", name);
+  if (!aligned16(b->codes)) return fail(MOE_ERR_ALIGN, "%s.codes must be 16-byte aligned", name);
+  if (b->expert_stride_bytes % 16 != 0)
+    return fail(MOE_ERR_ALIGN, "%s.expert_stride_bytes must be a multiple of 16 (got %lld)", name,
+                (long long)b->expert_stride_bytes);
+  if (b->expert_stride_bytes < N * K)
+    return fail(MOE_ERR_STRIDE, "%s.expert_stride_bytes %lld < N*K = %lld", name, (long long)b->expert_stride_bytes,
+                (long long)(N * K));
+  const int64_t rows = cdiv(N, 128), cols = cdiv(K, 128);
+  if (b->scale_row_stride < cols)
+    return fail(MOE_ERR_STRIDE, "%s.scale_row_stride %lld < ceil(K/128) = %lld", name,
+                (long long)b->scale_row_stride, (long long)cols);
+  const int64_t need = (rows - 1) * b->scale_row_stride + cols;
+  if (b->scale_expert_stride < need)
+    return fail(MOE_ERR_STRIDE, "%s.scale_expert_stride %lld < %lld (the unpadded extent)", name,
+                (long long)b->scale_expert_stride, (long long)need);
+  (void)E;
+  return MOE_OK;
+}
+
+moe::BankArg bank_arg(const moe_fp8_bank* b) {
+  moe::BankArg a;
+  a.codes = b->codes;
+  a.expert_stride = b->expert_stride_bytes;
+  a.scales = b->scales;
+  a.scale_bf16 = b->scale_dtype == MOE_BF16;
+  a.srow = b->scale_row_stride;
+  a.sexp = b->scale_expert_stride;
+  return a;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+// Enqueues the kernels of one call in order, optionally bracketing kernel i with the
+// caller's events 2i and 2i+1 and naming it in kinds[i].
+struct Runner {
+  hipStream_t s;
+  void* const* ev;
+  int nev;
+  int32_t* kinds;
+  int n = 0;
+
+  template <class F>
+  hipError_t run(int kind, F&& launch) {
+    const bool timed = ev != nullptr && 2 * n + 1 < nev;
+    if (timed) {
+      hipError_t e = hipEventRecord((hipEvent_t)ev[2 * n], s);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch();
+    if (e == hipSuccess && timed) e = hipEventRecord((hipEvent_t)ev[2 * n + 1], s);
+    if (kinds != nullptr && n < nev / 2) kinds[n] = kind;
+    ++n;
+    return e;
+  }
+};
+
+#define RUN(kind, call, what) HIP_CHECK(R.run(kind, [&]() { return (call); }), what)
+
+int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, const moe_fp8_bank* w2,
+                 int T, int E, int H, int I, int top_k, void* out, int out_dtype, void* workspace,
+                 size_t workspace_bytes, int32_t* ids_out, float* weights_out, const moe_opts* opts,
+                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds);
+
+}  // namespace
+
+extern "C" {
+
+int moe_fp8_block_abi_version(void) { return MOE_FP8_BLOCK_ABI_VERSION; }
+
+const char* moe_fp8_block_last_error(void) { return g_err.c_str(); }
+
+int moe_fp8_block_default_opts(moe_opts* opts) {
+  if (!opts) return fail(MOE_ERR_ARG, "opts is NULL");
+  *opts = defaults();
+  return ok();
+}
+
+int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe_run_info* info) {
+  if (!info) return fail(MOE_ERR_ARG, "info is NULL");
+  int st = check_sizes(T, E, top_k);
+  if (st) return st;
+  const moe_opts o = opts ? *opts : defaults();
+  if ((st = check_opts(&o))) return st;
+  const int p = gate(T, E, top_k, o);
+  info->path = p;
+  info->act_mode = p == MOE_PATH_MFMA ? 1 : 0;
+  const int64_t P = (int64_t)T * top_k;
+  info->slots = (int)(P < E ? P : E);
+  info->kernels = 0;
+  return ok();
+}
+
+size_t moe_fp8_block_route_workspace_size(int T, int E, int top_k) {
+  if (check_sizes(T, E, top_k)) return 0;
+  const size_t P = (size_t)T * top_k;
+  const size_t slots = P < (size_t)E ? P : (size_t)E;
+  Carve c;
+  c.take((slots > 0 ? slots : 1) * 4);
+  c.take(4);
+  c.take(moe::sort_scratch_bytes((int)P, E));
+  return c.off;
+}
+
+int moe_fp8_block_route(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_pairs, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int st = check_sizes(T, E, top_k);
+  if (st) return st;
+  if (T == 0) return ok();
+  const bool any_sort = counts || offsets || sorted_pairs;
+  const bool all_sort = counts && offsets && sorted_pairs;
+  if (any_sort && !all_sort) return fail(MOE_ERR_ARG, "counts, offsets and sorted_pairs must all be set or all NULL");
+  if (!logits || !ids || !weights) return fail(MOE_ERR_ARG, "logits, ids and weights must be non-NULL");
+  const int P = T * top_k;
+  const int slots = P < E ? P : E;
+  const size_t need = moe_fp8_block_route_workspace_size(T, E, top_k);
+  if (all_sort && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_CHECK(moe::launch_route_topk(logits, T, E, top_k, ids, weights, s), "route_topk launch");
+  if (all_sort) {
+    Carve c;
+    const size_t o_act = c.take((size_t)slots * 4);
+    const size_t o_n = c.take(4);
+    const size_t o_scr = c.take(moe::sort_scratch_bytes(P, E));
+    for (int st = 0; st < moe::sort_kernel_count(P); ++st)
+      HIP_CHECK(moe::launch_sort_stage(st, ids, P, E, counts, offsets, sorted_pairs, at<int32_t>(workspace, o_act),
+                                       at<int32_t>(workspace, o_n), slots, 0, nullptr, at<void>(workspace, o_scr), s),
+                "sort launch");
+  }
+  return ok();
+}
+
+size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const moe_opts* opts) {
+  if (check_sizes(T, E, top_k) || H <= 0 || I <= 0) return 0;
+  const moe_opts o = opts ? *opts : defaults();
+  if (check_opts(&o)) return 0;
+  int path = 0;
+  if (resolve_path(T, E, H, I, top_k, o, &path)) return 0;
+  return layout_for(path, T, E, H, I, top_k).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, const moe_fp8_bank* w2,
+                 int T, int E, int H, int I, int top_k, void* out, int out_dtype, void* workspace,
+                 size_t workspace_bytes, int32_t* ids_out, float* weights_out, const moe_opts* opts,
+                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds) {
+  int st = check_sizes(T, E, top_k);
+  if (st) return st;
+  if (H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "H and I must be positive (got H=%d, I=%d)", H, I);
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (got H=%d, I=%d)", H, I);
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
+  const moe_opts o = opts ? *opts : defaults();
+  if ((st = check_opts(&o))) return st;
+  if ((st = check_bank(w13, "w13", E, 2 * (int64_t)I, H))) return st;
+  if ((st = check_bank(w2, "w2", E, H, I))) return st;
+  int path = 0;
+  if ((st = resolve_path(T, E, H, I, top_k, o, &path))) return st;
+  const int64_t P = (int64_t)T * top_k;
+  if (info) {
+    info->path = path;
+    info->act_mode = path == MOE_PATH_MFMA ? 1 : 0;
+    info->slots = (int)(P < E ? P : E);
+    info->kernels = 0;
+  }
+  if (T == 0) return ok();
+  if (!hidden || !logits || !out) return fail(MOE_ERR_ARG, "hidden, logits and out must be non-NULL");
+  if (!aligned16(hidden)) return fail(MOE_ERR_ALIGN, "hidden must be 16-byte aligned");
+  const Layout L = layout_for(path, T, E, H, I, top_k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  const int slots = (int)(P < E ? P : E);
+  int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, L.ids);
+  float* w = weights_out ? weights_out : at<float>(workspace, L.w);
+  int32_t* counts = at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* act = at<int32_t>(workspace, L.act);
+  int32_t* n_act = at<int32_t>(workspace, L.n_act);
+  int32_t* tile_off = at<int32_t>(workspace, L.tile_off);
+  const int out_bf16 = out_dtype == MOE_BF16;
+  const moe::BankArg b13 = bank_arg(w13), b2 = bank_arg(w2);
+  Runner R{s, events, n_events, kinds};
+
+  RUN(MOE_K_ROUTE, moe::launch_route_topk(logits, T, E, top_k, ids, w, s), "route_topk launch");
+  const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
+  for (int st = 0; st < moe::sort_kernel_count((int)P); ++st)
+    RUN(MOE_K_SORT,
+        moe::launch_sort_stage(st, ids, (int)P, E, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off,
+                               at<void>(workspace, L.scratch), s),
+        "sort launch");
+  const moe::Plan plan{ids, w, counts, offsets, sorted, act, tile_off};
+
+  if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) {
+    float* h = at<float>(workspace, L.h);
+    RUN(MOE_K_GEMM1, moe::launch_gemm1_w8a16(hidden, b13, plan, slots, H, I, top_k, h, s), "gemm1 launch");
+    if (path == MOE_PATH_GATHER) {
+      RUN(MOE_K_GEMM2, moe::launch_gemm2_gather(h, b2, ids, w, T, H, I, top_k, out, out_bf16, s), "gemm2 launch");
+    } else {
+      float* y = at<float>(workspace, L.y);
+      RUN(MOE_K_GEMM2, moe::launch_gemm2_expert(h, b2, plan, slots, H, I, top_k, y, s), "gemm2 launch");
+      RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
+    }
+  } else {
+    uint8_t* xq = at<uint8_t>(workspace, L.xq);
+    float* xs = at<float>(workspace, L.xs);
+    uint8_t* hq = at<uint8_t>(workspace, L.hq);
+    float* hs = at<float>(workspace, L.hs);
+    float* acc = out_bf16 ? at<float>(workspace, L.acc) : (float*)out;
+    RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
+    RUN(MOE_K_ZERO, moe::launch_zero_f32(acc, (size_t)T * H, s), "zero launch");
+    RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hq, hs, s),
+        "gemm1 mfma launch");
+    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, top_k, acc, s), "gemm2 mfma launch");
+    if (out_bf16) RUN(MOE_K_FINALIZE, moe::launch_finalize(acc, (size_t)T * H, out, 1, s), "finalize launch");
+  }
+  if (info) info->kernels = R.n;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+
+int moe_fp8_block_forward(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
+                          const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out, int out_dtype,
+                          void* workspace, size_t workspace_bytes, int32_t* ids_out, float* weights_out,
+                          const moe_opts* opts, moe_run_info* info, void* stream) {
+  return forward_impl(hidden, logits, w13, w2, T, E, H, I, top_k, out, out_dtype, workspace, workspace_bytes, ids_out,
+                      weights_out, opts, info, stream, nullptr, 0, nullptr);
+}
+
+int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
+                                const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
+                                int out_dtype, void* workspace, size_t workspace_bytes, int32_t* ids_out,
+                                float* weights_out, const moe_opts* opts, moe_run_info* info, void* stream,
+                                void* const* events, int n_events, int32_t* kinds) {
+  if (n_events < 0 || (n_events > 0 && events == nullptr)) return fail(MOE_ERR_ARG, "events/n_events inconsistent");
+  for (int i = 0; kinds != nullptr && i < n_events / 2; ++i) kinds[i] = 0;
+  return forward_impl(hidden, logits, w13, w2, T, E, H, I, top_k, out, out_dtype, workspace, workspace_bytes, ids_out,
+                      weights_out, opts, info, stream, events, n_events, kinds);
+}
+
+int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales, void* stream) {
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_ARG, "rows must be >= 0 and cols > 0");
+  if (cols % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 16 (got %d)", cols);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(MOE_ERR_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes)) return fail(MOE_ERR_ALIGN, "x and codes must be 16-byte aligned");
+  HIP_CHECK(moe::launch_quant_rows_bf16(x, rows, cols, codes, scales, (hipStream_t)stream), "quant launch");
+  return ok();
+}
+
+int moe_fp8_block_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream) {
+  if (n < 0) return fail(MOE_ERR_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!codes || !out) return fail(MOE_ERR_ARG, "codes and out must be non-NULL");
+  HIP_CHECK(moe::launch_decode_e4m3(codes, out, n, (hipStream_t)stream), "decode launch");
+  return ok();
+}
+
+int moe_fp8_block_encode_e4m3(const float* x, uint8_t* codes, int64_t n, void* stream) {
+  if (n < 0) return fail(MOE_ERR_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!x || !codes) return fail(MOE_ERR_ARG, "x and codes must be non-NULL");
+  HIP_CHECK(moe::launch_encode_e4m3(x, codes, n, (hipStream_t)stream), "encode launch");
+  return ok();
+}
+
+}  // extern "C"

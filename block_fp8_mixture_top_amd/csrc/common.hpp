@@ -1,0 +1,98 @@
+// Device helpers shared by the kernels: e4m3 conversion, bf16, wave64 reductions, scales.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kScaleBlock = 128;  // one scale per 128x128 block of a bank
+constexpr float kE4M3Max = 448.0f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two e4m3 codes (bytes 0,1 when HI is false, bytes 2,3 when true) of a 32-bit word to
+// float with gfx950's conversion instruction, which reads OCP e4m3fn (bias 7). The decode
+// is exact: every e4m3 value is a float.
+template <bool HI>
+__device__ __forceinline__ f32x2 dec2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// Four codes of a word -> four floats.
+__device__ __forceinline__ void dec4(uint32_t w, float* o) {
+  f32x2 lo = dec2<false>(w);
+  f32x2 hi = dec2<true>(w);
+  o[0] = lo.x;
+  o[1] = lo.y;
+  o[2] = hi.x;
+  o[3] = hi.y;
+}
+
+// Float -> e4m3 code: round to nearest even, saturate at +-448 (clamped first, so the
+// instruction never sees an out-of-range value), sign of zero kept.
+__device__ __forceinline__ uint8_t enc1(float v) {
+  float c = __builtin_fminf(__builtin_fmaxf(v, -kE4M3Max), kE4M3Max);
+  // keep -0: fmin/fmax of -0 with +-448 returns -0
+  int packed = __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false);
+  return (uint8_t)(packed & 0xFF);
+}
+
+// Two floats -> two codes in the low half of a word.
+__device__ __forceinline__ uint32_t enc2(float a, float b) {
+  float ca = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+  float cb = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Low and high bf16 halves of a word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// A block scale as float.
+__device__ __forceinline__ float load_scale(const void* base, int is_bf16, int64_t idx) {
+  if (is_bf16) return bf16_to_f32(((const uint16_t*)base)[idx]);
+  return ((const float*)base)[idx];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// silu(g) = g / (1 + e^-g), in float.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// 16-byte global load kept as four words.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+
+// Non-temporal 16-byte load for weight bytes that are read once.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+}  // namespace moe

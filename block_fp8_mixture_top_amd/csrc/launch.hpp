@@ -1,0 +1,81 @@
+// Host-side launchers of the kernels (internal to the library; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MAX_EXPERTS 1024
+
+namespace moe {
+
+// Pair counts up to this sort in one workgroup; larger ones use the three-pass sort.
+constexpr int kSmallSortPairs = 4096;
+
+// A bank as the kernels see it.
+struct BankArg {
+  const uint8_t* codes;
+  int64_t expert_stride;  // bytes
+  const void* scales;
+  int scale_bf16;
+  int64_t srow;  // scale row stride, elements
+  int64_t sexp;  // scale expert stride, elements
+};
+
+// Sorted routing produced by the sort and read by the GEMMs.
+struct Plan {
+  const int32_t* ids;     // [P]
+  const float* w;         // [P]
+  const int32_t* counts;  // [E]
+  const int32_t* offsets; // [E+1]
+  const int32_t* sorted;  // [P]
+  const int32_t* act;     // [slots], -1 past the active experts
+  const int32_t* tile_off;// [E+1] or null
+};
+
+size_t sort_scratch_bytes(int P, int E);
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+// The sort is 1 kernel for P <= kSmallSortPairs and 3 otherwise; stage picks which.
+int sort_kernel_count(int P);
+hipError_t launch_sort_stage(int stage, const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted, int32_t* act, int32_t* n_act, int slots, int tile_m,
+                             int32_t* tile_off, void* scratch, hipStream_t s);
+
+// W8A16 GEMM1 + silu(gate)*up over `slots` expert slots: h[p, I] float for every pair p.
+hipError_t launch_gemm1_w8a16(const uint16_t* hidden, const BankArg& w13, const Plan& plan, int slots, int H,
+                              int I, int k, float* h, hipStream_t s);
+
+// Whether the token-major GEMM2 supports this (k, I) (its per-thread register budget).
+bool gemm2_gather_supported(int k, int I);
+
+// Token-major W8A16 GEMM2 with the combine fused: out[t, H].
+hipError_t launch_gemm2_gather(const float* h, const BankArg& w2, const int32_t* ids, const float* w, int T,
+                               int H, int I, int k, void* out, int out_bf16, hipStream_t s);
+
+// Expert-major W8A16 GEMM2: y[p, H] float for every pair.
+hipError_t launch_gemm2_expert(const float* h, const BankArg& w2, const Plan& plan, int slots, int H, int I,
+                               int k, float* y, hipStream_t s);
+
+// out[t, n] = sum_j w[t, j] * y[t*k + j, n], slots summed in order.
+hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, void* out, int out_bf16,
+                          hipStream_t s);
+
+// W8A8 path.
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                                  hipStream_t s);
+constexpr int kMfmaTileM = 32;  // sorted pairs per MFMA tile
+size_t mfma_tiles_bound(int P, int E);
+hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
+                             int P, int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s);
+hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E,
+                             int P, int H, int I, int k, float* acc, hipStream_t s);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+hipError_t launch_finalize(const float* acc, size_t n, void* out, int out_bf16, hipStream_t s);
+
+// Test exports.
+hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
+hipError_t launch_encode_e4m3(const float* x, uint8_t* codes, int64_t n, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,410 @@
+// W8A16 expert GEMMs that stream the routed experts' fp8 rows from HBM.
+//
+// Weights are e4m3 codes, row-major [rows, K] with K contiguous and one scale per 128x128
+// block (FreeToken PR #662, PR body). They are decoded exactly in registers (every e4m3
+// value is a float) and multiplied with bf16 activations, which are exact in float, so each
+// product is exact and only the float summation order differs from an exact evaluation.
+//
+// GEMM1 produces h = silu(gate) * up for every (token, slot) pair; the gate rows are
+// 0..I-1 and the up rows I..2I-1 of the w13 bank (tpu-inference PR #3040, review of the w1
+// weight/scale DMA), and one lane group holds gate row i and up row i together so h_i is
+// formed without another pass. GEMM2 reads h back and applies the down projection; on the
+// gather path it also applies the router weights and sums the slots (the combine).
+//
+// Lane layout: a row of K bytes is cut into 16-byte chunks; a group of LPR lanes covers a
+// row, lane g of the group taking chunks g, g+LPR, ... (MCH of them). A 16-byte chunk never
+// straddles a 128-wide scale block, so each chunk needs one scale.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// sum_i dec(code_i) * x_i over the 16 codes of `c` and the 16 bf16 activations of `x0,x1`.
+__device__ __forceinline__ float dot16_bf16(const u32x4& c, const u32x4& x0, const u32x4& x1) {
+  float acc = 0.0f;
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x2 lo = dec2<false>(cw[q]);
+    const f32x2 hi = dec2<true>(cw[q]);
+    acc = __builtin_fmaf(lo.x, bf16_lo(xw[2 * q]), acc);
+    acc = __builtin_fmaf(lo.y, bf16_hi(xw[2 * q]), acc);
+    acc = __builtin_fmaf(hi.x, bf16_lo(xw[2 * q + 1]), acc);
+    acc = __builtin_fmaf(hi.y, bf16_hi(xw[2 * q + 1]), acc);
+  }
+  return acc;
+}
+
+// sum_i dec(code_i) * v_i over 16 codes and 16 floats.
+__device__ __forceinline__ float dot16_f32(const u32x4& c, const float* v) {
+  float acc = 0.0f;
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x2 lo = dec2<false>(cw[q]);
+    const f32x2 hi = dec2<true>(cw[q]);
+    acc = __builtin_fmaf(lo.x, v[4 * q + 0], acc);
+    acc = __builtin_fmaf(lo.y, v[4 * q + 1], acc);
+    acc = __builtin_fmaf(hi.x, v[4 * q + 2], acc);
+    acc = __builtin_fmaf(hi.y, v[4 * q + 3], acc);
+  }
+  return acc;
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// GEMM1 + silu*up. grid.x: tiles of row pairs, grid.y: expert slots. A lane group owns RP
+// consecutive row pairs (gate i, up I+i) of slot's expert, loads their codes once and
+// applies them to every token routed to that expert.
+template <int LPR, int MCH, int RP>
+__global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden, BankArg w13,
+                                                               Plan plan, int H, int I, int k,
+                                                               float* __restrict__ h) {
+  const int e = plan.act[blockIdx.y];
+  if (e < 0) return;
+  constexpr int GPW = kWave / LPR;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int rows_per_block = (kThreads / kWave) * GPW * RP;
+  const int i0 = blockIdx.x * rows_per_block + (wave * GPW + grp) * RP;
+  const int NC = H / 16;
+  const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
+  const int64_t sb = (int64_t)e * w13.sexp;
+
+  u32x4 cg[RP][MCH], cu[RP][MCH];
+  float sg[RP][MCH], su[RP][MCH];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const int i = i0 + r;
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+      const int c = gl + LPR * m;
+      if (i < I && c < NC) {
+        cg[r][m] = ld16_stream(wb + (size_t)i * H + (size_t)c * 16);
+        cu[r][m] = ld16_stream(wb + (size_t)(I + i) * H + (size_t)c * 16);
+        sg[r][m] = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)(i / kScaleBlock) * w13.srow + c / 8);
+        su[r][m] = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)((I + i) / kScaleBlock) * w13.srow + c / 8);
+      } else {
+        cg[r][m] = u32x4{0, 0, 0, 0};
+        cu[r][m] = u32x4{0, 0, 0, 0};
+        sg[r][m] = 0.0f;
+        su[r][m] = 0.0f;
+      }
+    }
+  }
+  const int beg = plan.offsets[e];
+  const int cnt = plan.counts[e];
+  for (int q = 0; q < cnt; ++q) {
+    const int p = plan.sorted[beg + q];
+    const int t = p / k;
+    const uint8_t* xb = (const uint8_t*)(hidden + (size_t)t * H);
+    u32x4 x0[MCH], x1[MCH];
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+      const int c = gl + LPR * m;
+      if (c < NC) {
+        x0[m] = ld16(xb + (size_t)c * 32);
+        x1[m] = ld16(xb + (size_t)c * 32 + 16);
+      } else {
+        x0[m] = u32x4{0, 0, 0, 0};
+        x1[m] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      float g = 0.0f, u = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MCH; ++m) {
+        g = __builtin_fmaf(sg[r][m], dot16_bf16(cg[r][m], x0[m], x1[m]), g);
+        u = __builtin_fmaf(su[r][m], dot16_bf16(cu[r][m], x0[m], x1[m]), u);
+      }
+      g = group_sum<LPR>(g);
+      u = group_sum<LPR>(u);
+      const int i = i0 + r;
+      if (gl == 0 && i < I) h[(size_t)p * I + i] = silu(g) * u;
+    }
+  }
+}
+
+// Token-major GEMM2 with the combine. grid.x: tiles of ROWS output rows, grid.y: tokens.
+// The k*I/16 chunks of a token's (slot, chunk) space are spread over the workgroup's
+// threads (MC per thread); each thread keeps its h values and its slot's router weight in
+// registers and streams the matching 16 bytes of every output row.
+template <int MC, int ROWS>
+__global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __restrict__ h, BankArg w2,
+                                                                const int32_t* __restrict__ ids,
+                                                                const float* __restrict__ wts, int H, int I,
+                                                                int k, void* __restrict__ out, int out_bf16) {
+  __shared__ float red[kThreads / kWave][ROWS];
+  const int t = blockIdx.y;
+  const int n0 = blockIdx.x * ROWS;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int CPR = I / 16;
+  const int F = k * CPR;
+  float hv[MC][16];
+  const uint8_t* wp[MC];
+  float ws[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    const int f = tid + kThreads * m;
+    if (f < F) {
+      const int j = f / CPR, c = f % CPR;
+      const int e = ids[(size_t)t * k + j];
+      const float* hp = h + ((size_t)t * k + j) * I + (size_t)c * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *(const f32x4*)(hp + 4 * q);
+        hv[m][4 * q + 0] = v.x;
+        hv[m][4 * q + 1] = v.y;
+        hv[m][4 * q + 2] = v.z;
+        hv[m][4 * q + 3] = v.w;
+      }
+      wp[m] = w2.codes + (size_t)e * w2.expert_stride + (size_t)c * 16;
+      ws[m] = wts[(size_t)t * k + j] *
+              load_scale(w2.scales, w2.scale_bf16, (int64_t)e * w2.sexp + (int64_t)(n0 / kScaleBlock) * w2.srow + c / 8);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) hv[m][q] = 0.0f;
+      wp[m] = nullptr;
+      ws[m] = 0.0f;
+    }
+  }
+  u32x4 cw[ROWS][MC];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int n = n0 + r;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      if (wp[m] != nullptr && n < H) cw[r][m] = ld16_stream(wp[m] + (size_t)n * I);
+      else cw[r][m] = u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) acc = __builtin_fmaf(ws[m], dot16_f32(cw[r][m], hv[m]), acc);
+    acc = wave_sum(acc);
+    if (lane == 0) red[wave][r] = acc;
+  }
+  __syncthreads();
+  if (tid < ROWS) {
+    const int n = n0 + tid;
+    if (n < H) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) s += red[w][tid];
+      if (out_bf16) ((uint16_t*)out)[(size_t)t * H + n] = f32_to_bf16(s);
+      else ((float*)out)[(size_t)t * H + n] = s;
+    }
+  }
+}
+
+// Expert-major GEMM2: y[p, n] for every pair p of the slot's expert. grid.x: row tiles,
+// grid.y: expert slots. Same lane layout as GEMM1 with K = I and single rows.
+template <int LPR, int MCH, int RP>
+__global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __restrict__ h, BankArg w2, Plan plan,
+                                                                int H, int I, float* __restrict__ y) {
+  const int e = plan.act[blockIdx.y];
+  if (e < 0) return;
+  constexpr int GPW = kWave / LPR;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int rows_per_block = (kThreads / kWave) * GPW * RP;
+  const int n0 = blockIdx.x * rows_per_block + (wave * GPW + grp) * RP;
+  const int NC = I / 16;
+  const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
+  const int64_t sb = (int64_t)e * w2.sexp;
+  u32x4 cw[RP][MCH];
+  float sw[RP][MCH];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const int n = n0 + r;
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+      const int c = gl + LPR * m;
+      if (n < H && c < NC) {
+        cw[r][m] = ld16_stream(wb + (size_t)n * I + (size_t)c * 16);
+        sw[r][m] = load_scale(w2.scales, w2.scale_bf16, sb + (int64_t)(n / kScaleBlock) * w2.srow + c / 8);
+      } else {
+        cw[r][m] = u32x4{0, 0, 0, 0};
+        sw[r][m] = 0.0f;
+      }
+    }
+  }
+  const int beg = plan.offsets[e];
+  const int cnt = plan.counts[e];
+  for (int q = 0; q < cnt; ++q) {
+    const int p = plan.sorted[beg + q];
+    const float* hp = h + (size_t)p * I;
+    float hv[MCH][16];
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+      const int c = gl + LPR * m;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (c < NC) v = *(const f32x4*)(hp + (size_t)c * 16 + 4 * qq);
+        hv[m][4 * qq + 0] = v.x;
+        hv[m][4 * qq + 1] = v.y;
+        hv[m][4 * qq + 2] = v.z;
+        hv[m][4 * qq + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MCH; ++m) acc = __builtin_fmaf(sw[r][m], dot16_f32(cw[r][m], hv[m]), acc);
+      acc = group_sum<LPR>(acc);
+      const int n = n0 + r;
+      if (gl == 0 && n < H) y[(size_t)p * H + n] = acc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
+                                                           int T, int H, int k, void* __restrict__ out,
+                                                           int out_bf16) {
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (size_t)T * H) return;
+  const size_t t = idx / H, n = idx % H;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s = __builtin_fmaf(w[t * k + j], y[(t * k + j) * H + n], s);
+  if (out_bf16) ((uint16_t*)out)[idx] = f32_to_bf16(s);
+  else ((float*)out)[idx] = s;
+}
+
+// ---- launch helpers: pick the lane layout for a K of `K` bytes per row
+
+struct Layout {
+  int lpr, mch;
+};
+
+Layout pick_layout(int K) {
+  const int nc = K / 16;
+  if (nc >= kWave) return Layout{kWave, (nc + kWave - 1) / kWave};
+  int lpr = 8;
+  while (lpr * 2 <= nc && lpr < kWave) lpr *= 2;
+  return Layout{lpr, (nc + lpr - 1) / lpr};
+}
+
+template <int LPR, int MCH, int RP>
+hipError_t g1(const uint16_t* x, const BankArg& w, const Plan& p, int slots, int H, int I, int k, float* h,
+              hipStream_t s) {
+  const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
+  dim3 grid((I + rows - 1) / rows, slots);
+  hipLaunchKernelGGL((gemm1_w8a16_kernel<LPR, MCH, RP>), grid, dim3(kThreads), 0, s, x, w, p, H, I, k, h);
+  return hipGetLastError();
+}
+
+template <int LPR, int MCH, int RP>
+hipError_t g2e(const float* h, const BankArg& w, const Plan& p, int slots, int H, int I, float* y,
+               hipStream_t s) {
+  const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
+  dim3 grid((H + rows - 1) / rows, slots);
+  hipLaunchKernelGGL((gemm2_expert_kernel<LPR, MCH, RP>), grid, dim3(kThreads), 0, s, h, w, p, H, I, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_w8a16(const uint16_t* hidden, const BankArg& w13, const Plan& plan, int slots, int H,
+                              int I, int k, float* h, hipStream_t s) {
+  const Layout L = pick_layout(H);
+  if (L.lpr == 64) {
+    switch (L.mch) {
+      case 1: return g1<64, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 2: return g1<64, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 3: return g1<64, 3, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 4: return g1<64, 4, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 5: return g1<64, 5, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 6: return g1<64, 6, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 7: return g1<64, 7, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 8: return g1<64, 8, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (L.lpr == 32) return L.mch == 1 ? g1<32, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
+                                     : g1<32, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+  if (L.lpr == 16) return L.mch == 1 ? g1<16, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
+                                     : g1<16, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+  return L.mch == 1 ? g1<8, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
+                    : g1<8, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+}
+
+hipError_t launch_gemm2_expert(const float* h, const BankArg& w2, const Plan& plan, int slots, int H, int I,
+                               int k, float* y, hipStream_t s) {
+  (void)k;
+  const Layout L = pick_layout(I);
+  if (L.lpr == 64) {
+    switch (L.mch) {
+      case 1: return g2e<64, 1, 2>(h, w2, plan, slots, H, I, y, s);
+      case 2: return g2e<64, 2, 2>(h, w2, plan, slots, H, I, y, s);
+      case 3: return g2e<64, 3, 1>(h, w2, plan, slots, H, I, y, s);
+      case 4: return g2e<64, 4, 1>(h, w2, plan, slots, H, I, y, s);
+      case 5: return g2e<64, 5, 1>(h, w2, plan, slots, H, I, y, s);
+      case 6: return g2e<64, 6, 1>(h, w2, plan, slots, H, I, y, s);
+      case 7: return g2e<64, 7, 1>(h, w2, plan, slots, H, I, y, s);
+      case 8: return g2e<64, 8, 1>(h, w2, plan, slots, H, I, y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (L.lpr == 32) return L.mch == 1 ? g2e<32, 1, 2>(h, w2, plan, slots, H, I, y, s)
+                                     : g2e<32, 2, 2>(h, w2, plan, slots, H, I, y, s);
+  if (L.lpr == 16) return L.mch == 1 ? g2e<16, 1, 2>(h, w2, plan, slots, H, I, y, s)
+                                     : g2e<16, 2, 2>(h, w2, plan, slots, H, I, y, s);
+  return L.mch == 1 ? g2e<8, 1, 2>(h, w2, plan, slots, H, I, y, s) : g2e<8, 2, 2>(h, w2, plan, slots, H, I, y, s);
+}
+
+bool gemm2_gather_supported(int k, int I) {
+  const int F = k * (I / 16);
+  return F <= 4 * kThreads;
+}
+
+template <int MC, int ROWS>
+static hipError_t g2g(const float* h, const BankArg& w2, const int32_t* ids, const float* w, int T, int H, int I,
+                      int k, void* out, int out_bf16, hipStream_t s) {
+  dim3 grid((H + ROWS - 1) / ROWS, T);
+  hipLaunchKernelGGL((gemm2_gather_kernel<MC, ROWS>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
+                     out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_gather(const float* h, const BankArg& w2, const int32_t* ids, const float* w, int T,
+                               int H, int I, int k, void* out, int out_bf16, hipStream_t s) {
+  const int F = k * (I / 16);
+  const int mc = (F + kThreads - 1) / kThreads;
+  // rows per workgroup: enough workgroups to cover the chip at small T
+  const bool few = (size_t)T * H < 256 * 8 * 4;
+  switch (mc) {
+    case 1: return few ? g2g<1, 4>(h, w2, ids, w, T, H, I, k, out, out_bf16, s)
+                       : g2g<1, 8>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
+    case 2: return few ? g2g<2, 4>(h, w2, ids, w, T, H, I, k, out, out_bf16, s)
+                       : g2g<2, 8>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
+    case 3:
+    case 4: return few ? g2g<4, 4>(h, w2, ids, w, T, H, I, k, out, out_bf16, s)
+                       : g2g<4, 8>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, void* out, int out_bf16,
+                          hipStream_t s) {
+  const size_t n = (size_t)T * H;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, y, w,
+                     T, H, k, out, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -73,3 +73,22 @@ def rel_err_bf16(out, ref) -> float:
     excess = np.maximum(0.0, np.abs(out - ref) - slack)
     den = float(np.max(np.abs(ref)))
     return float(np.max(excess)) / (den if den > 0 else 1.0)
+
+
+def bank_numpy(bank, experts=None) -> dict:
+    """Host arrays of a bank for the oracle; with ``experts`` only those experts' codes are
+    copied (the rest of the host buffer stays zero and is never read by the oracle)."""
+    if experts is None:
+        return bank.numpy()
+    codes = np.zeros(bank.codes.numel(), dtype=np.uint8)
+    st = bank.expert_stride_bytes
+    for e in sorted(set(int(x) for x in experts)):
+        codes[e * st:(e + 1) * st] = bank.codes[e * st:(e + 1) * st].cpu().numpy()
+    if bank.scale_dtype == "bf16":
+        scales = bank.scales.cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        scales = bank.scales.cpu().numpy()
+    d = dict(codes=codes, scales=scales, scale_dtype=bank.scale_dtype, E=bank.E, N=bank.N, K=bank.K,
+             expert_stride_bytes=st, scale_row_stride=bank.scale_row_stride,
+             scale_expert_stride=bank.scale_expert_stride)
+    return d

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Routing, sort and every integer result must match bit for bit; float outputs must satisfy
+max|out - ref| / max|ref| <= 2e-3 (after the bf16 output rounding for bf16 outputs, and
+with the per-output allowance for e4m3 roundings of h that an fp32 evaluation may decide
+either way on the W8A8 path). Inputs come from the seeded generators; the oracle sees host
+copies of exactly the tensors the library reads.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_top_amd as M
+import oracle as O
+import workloads as W
+from helpers import REL_TOL, bank_numpy, bf16_bits, bf16_half_ulp, rel_err, rel_err_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+PATHS = {"gather": M.PATH_GATHER, "stream": M.PATH_STREAM, "mfma": M.PATH_MFMA}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def oracle_out(case, rows=None, act_mode=0, experts=None):
+    hid = bf16_bits(case.hidden)
+    lg = case.logits.detach().cpu().numpy()
+    if rows is not None:
+        hid, lg = hid[rows], lg[rows]
+    w13 = bank_numpy(case.w13, experts)
+    w2 = bank_numpy(case.w2, experts)
+    return O.forward(hid, lg, w13, w2, case.top_k, act_mode=act_mode)
+
+
+def check_out(out, res, act_mode, what):
+    """The float bar, with bf16 rounding and W8A8 allowance taken out of the error."""
+    ref = res["out"]
+    o = out.detach().float().cpu().numpy().astype(np.float64)
+    den = float(np.max(np.abs(ref)))
+    err = np.abs(o - ref)
+    if out.dtype == torch.bfloat16:
+        err = np.maximum(0.0, err - bf16_half_ulp(np.maximum(np.abs(o), np.abs(ref))))
+    if act_mode == 1:
+        err = np.maximum(0.0, err - res["allowance"])
+    r = float(np.max(err)) / den
+    say(what, f"rel={r:.3e}", f"raw={rel_err(o, ref):.3e}")
+    assert np.isfinite(o).all(), what
+    assert r <= REL_TOL, f"{what}: {r}"
+    return r
+
+
+# ------------------------------------------------------------------- e4m3 conversions
+
+def test_decode_every_code_exactly():
+    say("decode 256 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(DEV)
+    got = M.decode_e4m3(codes).cpu().numpy().astype(np.float64)
+    lut = O.e4m3_lut()
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    assert np.array_equal(got[finite], lut[finite])
+    assert np.array_equal(np.signbit(got[finite]), np.signbit(lut[finite]))
+
+
+def test_encode_matches_oracle():
+    say("encode midpoints")
+    pos = O.e4m3_lut()[:0x7F]
+    mids = 0.5 * (pos[:-1] + pos[1:])
+    m32 = mids.astype(np.float32)
+    g = np.random.default_rng(11)
+    v = np.concatenate([pos, mids, np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(-np.inf)),
+                        g.normal(0, 50, 20000), g.uniform(-600, 600, 5000), [0.0, -0.0, 1e30, -1e30, 2.0 ** -11]])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    got = M.encode_e4m3(torch.from_numpy(v).to(DEV)).cpu().numpy()
+    want = O.e4m3_encode(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_quantize_rows_bit_exact():
+    say("quantize rows")
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(37, 2048, generator=g) * torch.rand(37, 1, generator=g) * 5).to(torch.bfloat16)
+    x[5] = 0
+    x[6, :100] = 300.0
+    codes, scales = M.quantize_rows(x.to(DEV))
+    q, s = O.quantize_rows(O.bf16_to_f64(bf16_bits(x)).astype(np.float32))
+    assert np.array_equal(scales.cpu().numpy(), s)
+    assert np.array_equal(codes.cpu().numpy(), q)
+
+
+# ------------------------------------------------------------------- routing
+
+def _route_check(logits, k, what):
+    say("route", what, tuple(logits.shape), k)
+    r = M.route(logits.to(DEV), k)
+    ids, w, w32 = O.route(logits.cpu().numpy(), k)
+    counts, offsets, sp = O.sort_pairs(ids, logits.shape[1])
+    assert np.array_equal(r["ids"].cpu().numpy(), ids), what
+    gw = r["weights"].cpu().numpy()
+    nbad = int((gw != w32).sum())
+    assert nbad == 0, f"{what}: {nbad} weights differ (max {np.max(np.abs(gw - w32))})"
+    assert np.array_equal(r["counts"].cpu().numpy(), counts), what
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets), what
+    assert np.array_equal(r["sorted_pairs"].cpu().numpy(), sp), what
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("sweep", 1), ("sweep", 12), ("sweep", 64),
+                                    ("large", 16), ("prefill", 4096), ("prefill", 16384)])
+def test_route_bit_exact(name, T):
+    shp = W.SHAPES[name]
+    kind = {"tiny": "normal", "decode": "normal", "sweep": "zipf", "large": "normal", "prefill": "uniform"}[name]
+    std = 1.5 if name == "decode" else 1.0
+    logits = W.make_logits(T, shp["E"], kind, seed=77 + T, std=std)
+    _route_check(logits, shp["top_k"], f"{name} T={T}")
+
+
+def test_route_ties_and_extremes():
+    g = torch.Generator().manual_seed(1)
+    tied = (torch.randn(300, 64, generator=g) * 2).round() / 2
+    tied[0] = 0.25
+    _route_check(tied, 6, "ties")
+    big = torch.randn(70, 1024, generator=g)
+    _route_check(big, 32, "E=1024 k=32")
+    _route_check(torch.randn(5000, 1024, generator=g), 1, "E=1024 k=1 multi-block sort")
+    _route_check(torch.randn(3, 1, generator=g), 1, "E=1")
+
+
+def test_route_empty():
+    r = M.route(torch.empty((0, 16), dtype=torch.float32, device=DEV), 4)
+    assert r["ids"].numel() == 0
+
+
+# ------------------------------------------------------------------- forward parity
+
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("T", [1, 2, 4, 5])
+def test_tiny_forward(path, T):
+    c = W.make_case("tiny", T=T, seed=T).to(DEV)
+    say("tiny", path, "T", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path], return_routing=True)
+    torch.cuda.synchronize()
+    assert info["path"] == path
+    act = 1 if path == "mfma" else 0
+    res = oracle_out(c, act_mode=act)
+    assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
+    check_out(out, res, act, f"tiny {path} T={T}")
+
+
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("pad", ["row16", "slab16"])
+def test_padded_banks(path, pad):
+    """Padded scale strides and expert strides with NaN in every padding byte."""
+    c = W.make_case("decode", T=3, seed=9, E=16, H=640, I=384, top_k=4, pad=pad, code_pad_bytes=48).to(DEV)
+    assert c.w13.scale_row_stride > c.w13.scale_cols or c.w2.scale_row_stride > c.w2.scale_cols
+    say("padded", pad, path)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    act = 1 if path == "mfma" else 0
+    check_out(out, oracle_out(c, act_mode=act), act, f"padded {pad} {path}")
+
+
+def test_decode_workload():
+    """E=256, H=2048, I=512, top_k=8, T=1, bf16 out: the gate picks GATHER."""
+    say("decode T=1")
+    c = W.make_case("decode", T=1, seed=1, device=DEV)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
+    assert info["path"] == "gather" and info["slots"] == 8
+    check_out(out, oracle_out(c), 0, "decode T=1 bf16")
+
+
+@pytest.fixture(scope="module")
+def decode_banks():
+    return W.make_banks("decode", seed=1, device=DEV)
+
+
+@pytest.mark.parametrize("T", [1, 4, 12, 16, 32, 64])
+def test_sweep_auto(decode_banks, T):
+    """Zipf(1.1) popularity over the decode banks; T<=12 gathers, T>=16 streams."""
+    c = W.make_case("sweep", T=T, seed=2, device=DEV, banks=decode_banks)
+    say("sweep", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
+    assert info["path"] == ("gather" if T <= 12 else "stream")
+    check_out(out, oracle_out(c), 0, f"sweep T={T} {info['path']}")
+
+
+@pytest.mark.parametrize("path", ["gather", "stream"])
+def test_sweep_forced(decode_banks, path):
+    c = W.make_case("sweep", T=32 if path == "gather" else 4, seed=3, device=DEV, banks=decode_banks)
+    say("sweep forced", path)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=PATHS[path])
+    assert info["path"] == path
+    check_out(out, oracle_out(c), 0, f"sweep forced {path}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_large_expert_workload(T):
+    """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest
+    hold NaN codes and NaN scales, so reading an unrouted expert would poison the output."""
+    shp = W.SHAPES["large"]
+    logits = W.make_logits(T, shp["E"], "normal", seed=40 + T, device="cpu")
+    ids, _, _ = O.route(logits.numpy(), shp["top_k"])
+    used = O.routed_experts(ids)
+    say("large", T, "experts", len(used))
+    banks = W.make_banks("large", seed=4, device=DEV, experts=used)
+    c = W.make_case("large", T=T, seed=4, device=DEV, banks=banks)
+    c.logits = logits.to(DEV)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert info["path"] == ("gather" if T == 1 else "stream")
+    assert torch.isfinite(out.float()).all()
+    rows = np.array([0]) if T == 1 else np.array([0, 7, T - 1])
+    need = O.routed_experts(ids[rows])
+    check_out(out[torch.from_numpy(rows).to(DEV)], oracle_out(c, rows=rows, experts=need), 0, f"large T={T}")
+
+
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_prefill_sampled(decode_banks, T):
+    """MFMA W8A8 at prefill sizes; the oracle computes sampled tokens one by one."""
+    c = W.make_case("prefill", T=T, seed=6, device=DEV, banks=decode_banks)
+    say("prefill", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16, return_routing=True)
+    torch.cuda.synchronize()
+    assert info["path"] == "mfma" and info["act_mode"] == 1
+    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(T).choice(T, 21, replace=False)]))
+    res = oracle_out(c, rows=rows, act_mode=1)
+    assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
+    assert res["n_flagged"] <= 0.01 * res["n_h"]
+    sub = out[torch.from_numpy(rows).to(DEV)]
+    check_out(sub, res, 1, f"prefill T={T} sampled")
+
+
+def test_mfma_small_sizes_forced(decode_banks):
+    """Forced MFMA with ragged tiles (few tokens per expert) against all rows."""
+    c = W.make_case("decode", T=40, seed=8, device=DEV, banks=decode_banks)
+    say("mfma forced T=40")
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=M.PATH_MFMA)
+    res = oracle_out(c, act_mode=1)
+    check_out(out, res, 1, "mfma T=40")
+
+
+# ------------------------------------------------------------------- properties
+
+@pytest.mark.parametrize("path", ["gather", "stream"])
+def test_bf16_is_rounded_fp32_and_deterministic(decode_banks, path):
+    c = W.make_case("sweep", T=8, seed=12, device=DEV, banks=decode_banks)
+    say("bf16 vs fp32", path)
+    f32a, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=PATHS[path])
+    f32b, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=PATHS[path])
+    b16, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16, force_path=PATHS[path])
+    assert torch.equal(f32a, f32b)
+    assert torch.equal(f32a.to(torch.bfloat16), b16)
+
+
+def test_paths_agree(decode_banks):
+    """GATHER and STREAM (both W8A16) agree to fp32 summation-order differences."""
+    c = W.make_case("sweep", T=12, seed=13, device=DEV, banks=decode_banks)
+    say("gather vs stream")
+    a, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=M.PATH_GATHER)
+    b, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=M.PATH_STREAM)
+    d = (a - b).abs().max().item() / a.abs().max().item()
+    assert d <= 1e-5
+
+
+def test_zero_tokens():
+    c = W.make_case("tiny", T=1, seed=1).to(DEV)
+    out, info = M.forward(c.hidden[:0], c.logits[:0], c.w13, c.w2, c.top_k, out_dtype=torch.float32)
+    assert out.shape == (0, c.H) and info["kernels"] == 0

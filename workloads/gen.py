@@ -165,6 +165,7 @@ def make_bank(
     code_pad_bytes: int = 0,
     pad_fill: float = float("nan"),
     std: float = 0.02,
+    experts=None,
 ) -> FP8Bank:
     """Draw an fp8 block bank expert by expert.
 
@@ -172,7 +173,9 @@ def make_bank(
     kind ``normal``: weights N(0, std) quantised per 128x128 block with scale
     amax/448 (stored in ``scale_dtype``) and torch's e4m3fn cast of weight/scale.
     Scale padding holds ``pad_fill`` (NaN by default, so a reader of padding sees it);
-    ``code_pad_bytes`` of 0x7F (NaN codes) follow each expert's codes.
+    ``code_pad_bytes`` of 0x7F (NaN codes) follow each expert's codes. With ``experts``
+    only those experts are drawn; the others keep NaN codes and NaN scales, so any read
+    of an expert that should not be read poisons the result.
     """
     esz = 2 if scale_dtype == torch.bfloat16 else 4
     rows, cols = -(-N // BLOCK), -(-K // BLOCK)
@@ -183,7 +186,7 @@ def make_bank(
     codes = torch.full((E, estride), 0x7F, dtype=torch.uint8, device=device)
     scales = torch.full((E, rows, rstride), pad_fill, dtype=scale_dtype, device=device)
     finite = finite_e4m3_codes().to(device)
-    for e in range(E):
+    for e in range(E) if experts is None else sorted(set(int(x) for x in experts)):
         g = _gen(device, seed, tensor_id, e)
         if kind == "uniform":
             idx = torch.randint(0, finite.numel(), (N * K,), generator=g, device=device)
@@ -274,7 +277,7 @@ class MoECase:
 
 def make_banks(name: str, seed: int, device="cpu", *, E: Optional[int] = None, H: Optional[int] = None,
                I: Optional[int] = None, pad: Optional[str] = None, code_pad_bytes: int = 0,
-               scale_dtype: Optional[torch.dtype] = None) -> tuple:
+               scale_dtype: Optional[torch.dtype] = None, experts=None) -> tuple:
     """The (w13, w2) banks of a workload; shapes may be overridden for tests."""
     shp = dict(SHAPES[name])
     E = E or shp["E"]
@@ -293,9 +296,9 @@ def make_banks(name: str, seed: int, device="cpu", *, E: Optional[int] = None, H
     # the decode, sweep and prefill workloads share one set of banks
     bank_seed = _seed(seed, _BANK_FAMILY[name])
     w13 = make_bank(E, 2 * I, H, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
-                    tensor_id=_TID_W13, device=device, code_pad_bytes=code_pad_bytes)
+                    tensor_id=_TID_W13, device=device, code_pad_bytes=code_pad_bytes, experts=experts)
     w2 = make_bank(E, H, I, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
-                   tensor_id=_TID_W2, device=device, code_pad_bytes=code_pad_bytes)
+                   tensor_id=_TID_W2, device=device, code_pad_bytes=code_pad_bytes, experts=experts)
     return w13, w2
 
 
