@@ -279,16 +279,18 @@ int moe_fp8_block_route(const float* logits, int T, int E, int top_k, int32_t* i
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   hipStream_t s = (hipStream_t)stream;
-  HIP_CHECK(moe::launch_route_topk(logits, T, E, top_k, ids, weights, s), "route_topk launch");
-  if (all_sort) {
+  if (!all_sort) {
+    HIP_CHECK(moe::launch_route_topk(logits, T, E, top_k, ids, weights, s), "route_topk launch");
+  } else {
     Carve c;
     const size_t o_act = c.take((size_t)slots * 4);
     const size_t o_n = c.take(4);
     const size_t o_scr = c.take(moe::sort_scratch_bytes(P, E));
-    for (int st = 0; st < moe::sort_kernel_count(P); ++st)
-      HIP_CHECK(moe::launch_sort_stage(st, ids, P, E, counts, offsets, sorted_pairs, at<int32_t>(workspace, o_act),
-                                       at<int32_t>(workspace, o_n), slots, 0, nullptr, at<void>(workspace, o_scr), s),
-                "sort launch");
+    for (int st = 0; st < moe::route_kernel_count(P); ++st)
+      HIP_CHECK(moe::launch_route_stage(st, logits, T, E, top_k, ids, weights, counts, offsets, sorted_pairs,
+                                        at<int32_t>(workspace, o_act), at<int32_t>(workspace, o_n), slots, 0,
+                                        nullptr, at<void>(workspace, o_scr), s),
+                "route launch");
   }
   return ok();
 }
@@ -352,18 +354,22 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   const moe::BankArg b13 = bank_arg(w13), b2 = bank_arg(w2);
   Runner R{s, events, n_events, kinds};
 
-  RUN(MOE_K_ROUTE, moe::launch_route_topk(logits, T, E, top_k, ids, w, s), "route_topk launch");
+  // small gather batches route inside GEMM1; everything else routes and sorts first
+  const bool fused = path == MOE_PATH_GATHER && moe::gemm1_fused_route_ok(T, top_k);
   const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
-  for (int st = 0; st < moe::sort_kernel_count((int)P); ++st)
-    RUN(MOE_K_SORT,
-        moe::launch_sort_stage(st, ids, (int)P, E, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off,
-                               at<void>(workspace, L.scratch), s),
-        "sort launch");
+  if (!fused) {
+    for (int st = 0; st < moe::route_kernel_count((int)P); ++st)
+      RUN(st == 0 ? MOE_K_ROUTE : MOE_K_SORT,
+          moe::launch_route_stage(st, logits, T, E, top_k, ids, w, counts, offsets, sorted, act, n_act, slots,
+                                  tile_m, tile_off, at<void>(workspace, L.scratch), s),
+          "route launch");
+  }
   const moe::Plan plan{ids, w, counts, offsets, sorted, act, tile_off};
 
   if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) {
     float* h = at<float>(workspace, L.h);
-    RUN(MOE_K_GEMM1, moe::launch_gemm1_w8a16(hidden, b13, plan, slots, H, I, top_k, h, s), "gemm1 launch");
+    const moe::Gemm1Args g1{hidden, logits, T, E, H, I, top_k, slots, b13, plan, h, fused ? 1 : 0, ids, w};
+    RUN(MOE_K_GEMM1, moe::launch_gemm1_w8a16(g1, s), "gemm1 launch");
     if (path == MOE_PATH_GATHER) {
       RUN(MOE_K_GEMM2, moe::launch_gemm2_gather(h, b2, ids, w, T, H, I, top_k, out, out_bf16, s), "gemm2 launch");
     } else {

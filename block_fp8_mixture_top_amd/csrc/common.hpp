@@ -70,6 +70,74 @@ __device__ __forceinline__ float load_scale(const void* base, int is_bf16, int64
   return ((const float*)base)[idx];
 }
 
+// ---- wave64 reductions on DPP (row shifts within 16-lane rows, then row broadcasts 15 and
+// 31), which stay in the VALU instead of going through LDS like a shuffle. The result is
+// read from lane 63 and is uniform. Call with all 64 lanes active.
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xF, 0xF>(0u, v));  // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xF, 0xF>(0u, v));  // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xF, 0xF>(0u, v));  // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xF, 0xF>(0u, v));  // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xA, 0xF>(0u, v));  // row_bcast:15
+  v = max(v, dpp_u32<0x143, 0xC, 0xF>(0u, v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const uint32_t id = 0xFFFFFFFFu;
+  v = min(v, dpp_u32<0x111, 0xF, 0xF>(id, v));
+  v = min(v, dpp_u32<0x112, 0xF, 0xF>(id, v));
+  v = min(v, dpp_u32<0x114, 0xF, 0xF>(id, v));
+  v = min(v, dpp_u32<0x118, 0xF, 0xF>(id, v));
+  v = min(v, dpp_u32<0x142, 0xA, 0xF>(id, v));
+  v = min(v, dpp_u32<0x143, 0xC, 0xF>(id, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK, BANK_MASK>(0u, __float_as_uint(v)));  // 0u is +0.0f
+}
+
+// Sum over the 64 lanes in a fixed order (deterministic), result uniform.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0x111, 0xF, 0xF>(v);
+  v += dpp_f32<0x112, 0xF, 0xF>(v);
+  v += dpp_f32<0x114, 0xF, 0xF>(v);
+  v += dpp_f32<0x118, 0xF, 0xF>(v);
+  v += dpp_f32<0x142, 0xA, 0xF>(v);
+  v += dpp_f32<0x143, 0xC, 0xF>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Float -> unsigned key whose unsigned order is the float order (NaN excluded). -0 is
+// first turned into +0 (x + 0 does that and nothing else), so the two compare equal as
+// floats do.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

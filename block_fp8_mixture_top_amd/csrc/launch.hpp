@@ -37,15 +37,29 @@ size_t sort_scratch_bytes(int P, int E);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 
-// The sort is 1 kernel for P <= kSmallSortPairs and 3 otherwise; stage picks which.
-int sort_kernel_count(int P);
-hipError_t launch_sort_stage(int stage, const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                             int32_t* sorted, int32_t* act, int32_t* n_act, int slots, int tile_m,
-                             int32_t* tile_off, void* scratch, hipStream_t s);
+// Routing plus the sort: 1 kernel (route and sort in one workgroup) for P <= kSmallSortPairs,
+// else 4 (top-k, then histogram, chunk scan and scatter); stage picks which.
+int route_kernel_count(int P);
+hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* act, int32_t* n_act,
+                              int slots, int tile_m, int32_t* tile_off, void* scratch, hipStream_t s);
 
 // W8A16 GEMM1 + silu(gate)*up over `slots` expert slots: h[p, I] float for every pair p.
-hipError_t launch_gemm1_w8a16(const uint16_t* hidden, const BankArg& w13, const Plan& plan, int slots, int H,
-                              int I, int k, float* h, hipStream_t s);
+// fused: route inside the kernel (gemm1_fused_route_ok(T, k)), writing ids_out/w_out and
+// leaving the sort undone; otherwise the slot's expert and pairs come from plan.
+struct Gemm1Args {
+  const uint16_t* hidden;
+  const float* logits;
+  int T, E, H, I, k, slots;
+  BankArg w13;
+  Plan plan;
+  float* h;
+  int fused;
+  int32_t* ids_out;
+  float* w_out;
+};
+bool gemm1_fused_route_ok(int T, int k);
+hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s);
 
 // Whether the token-major GEMM2 supports this (k, I) (its per-thread register budget).
 bool gemm2_gather_supported(int k, int I);

@@ -9,83 +9,26 @@
 // in which atomics land.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kMaxPerLane = MAX_EXPERTS / kWave;  // logits held per lane (E <= 1024)
-
-// Is (la, ia) ahead of (lb, ib) in the order (descending logit, ascending id)?
-__device__ __forceinline__ bool ahead(float la, int ia, float lb, int ib) {
-  return la > lb || (la == lb && ia < ib);
-}
-
-// One wave per token. Each lane holds E/64 logits; k rounds of a wave-wide arg-max pick
-// the experts in slot order. Lane j keeps slot j.
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                         int k, int32_t* __restrict__ ids,
-                                                         float* __restrict__ weights) {
+// One wave per token.
+template <int PER>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ weights) {
   const int lane = lane_id();
   const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[kMaxPerLane];
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + kWave * i;
-    const float l = e < E ? row[e] : 0.0f;
-    // NaN is outside the contract; reading it as -inf keeps every selected id in [0, E)
-    v[i] = l != l ? -__builtin_inff() : l;
-  }
-  uint32_t taken = 0;
-  float my_l = 0.0f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bl = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !((taken >> i) & 1u) && ahead(v[i], e, bl, bi)) {
-        bl = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ol = __shfl_xor(bl, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (ahead(ol, oi, bl, bi)) {
-        bl = ol;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (lane == j) {
-      my_l = bl;
-      my_id = bi;
-    }
-  }
-  // weights in double: exp(l_j - l_0) / sum over slots in slot order
-  const double l0 = (double)__shfl(my_l, 0, kWave);
-  const double ex = lane < k ? exp((double)my_l - l0) : 0.0;
-  double tot = 0.0;
-  for (int j = 0; j < k; ++j) tot += __shfl(ex, j, kWave);
+  int id;
+  float w;
+  wave_topk<PER>(logits + (size_t)t * E, E, k, id, w);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    weights[(size_t)t * k + lane] = (float)(ex / tot);
+    ids[(size_t)t * k + lane] = id;
+    weights[(size_t)t * k + lane] = w;
   }
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
 }
 
 // Lanes of the wave whose 10-bit key equals this lane's key (E <= 1024).
@@ -159,9 +102,12 @@ __device__ void wave_active_list(const int* counts, int E, int slots, int32_t* a
   }
 }
 
-// Whole sort in one workgroup, for small P. Counts in LDS, offsets by a wave scan, then one
-// wave walks the pairs in rounds of 64 and places each by its rank among equal experts.
-__global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restrict__ ids, int P, int E,
+// Routing and the whole sort in one workgroup, for small P: 16 waves route the tokens, then
+// counts in LDS, offsets by a wave scan, and one wave walks the pairs in rounds of 64,
+// placing each by its rank among equal experts.
+template <int PER>
+__global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ weights,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted, int32_t* act,
@@ -169,11 +115,24 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
                                                           int32_t* tile_off) {
   __shared__ int cnt[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS];
+  __shared__ int sid[kSmallSortPairs];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int nwaves = blockDim.x / kWave;
+  const int P = T * k;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int t = wave; t < T; t += nwaves) {
+    int id;
+    float w;
+    wave_topk<PER>(logits + (size_t)t * E, E, k, id, w);
+    if (lane < k) {
+      sid[t * k + lane] = id;
+      ids[(size_t)t * k + lane] = id;
+      weights[(size_t)t * k + lane] = w;
+    }
+  }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[ids[p]], 1);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[sid[p]], 1);
   __syncthreads();
-  const int wave = threadIdx.x / kWave;
   if (wave == 0) {
     wave_exclusive_offsets(cnt, E, off);
   } else if (wave == 1) {
@@ -187,12 +146,11 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
   if (threadIdx.x == 0) offsets[E] = P;
   __syncthreads();
   if (wave == 0) {
-    const int lane = lane_id();
     // off[] becomes the running insertion point of each expert
     for (int base = 0; base < P; base += kWave) {
       const int p = base + lane;
       const bool valid = p < P;
-      const int e = valid ? ids[p] : 0;
+      const int e = valid ? sid[p] : 0;
       const uint64_t m = match_lanes(e, valid);
       const int rank = __popcll(m & ((1ull << lane) - 1ull));
       const int pos = valid ? off[e] + rank : 0;
@@ -291,32 +249,34 @@ size_t sort_scratch_bytes(int P, int E) {
   return nchunks * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                             hipStream_t s) {
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   const int waves_per_block = 4;
   const int blocks = (T + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(waves_per_block * kWave), 0, s, logits, T, E, k,
-                     ids, w);
+  MOE_TOPK_DISPATCH(E, hipLaunchKernelGGL((route_topk_kernel<PER>), dim3(blocks), dim3(waves_per_block * kWave), 0,
+                                          s, logits, T, E, k, ids, w));
   return hipGetLastError();
 }
 
-int sort_kernel_count(int P) { return P <= kSmallSortPairs ? 1 : 3; }
+int route_kernel_count(int P) { return P <= kSmallSortPairs ? 1 : 4; }
 
-hipError_t launch_sort_stage(int stage, const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                             int32_t* sorted, int32_t* act, int32_t* n_act, int slots, int tile_m,
-                             int32_t* tile_off, void* scratch, hipStream_t s) {
+hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* act, int32_t* n_act,
+                              int slots, int tile_m, int32_t* tile_off, void* scratch, hipStream_t s) {
+  const int P = T * k;
   if (P <= kSmallSortPairs) {
-    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(1024), 0, s, ids, P, E, counts, offsets, sorted, act,
-                       n_act, slots, tile_m, tile_off);
+    MOE_TOPK_DISPATCH(E, hipLaunchKernelGGL((route_plan_kernel<PER>), dim3(1), dim3(1024), 0, s, logits, T, E, k,
+                                            ids, w, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off));
     return hipGetLastError();
   }
   const int nchunks = (P + kChunk - 1) / kChunk;
   int32_t* chunk = (int32_t*)scratch;
   switch (stage) {
     case 0:
+      return launch_route_topk(logits, T, E, k, ids, w, s);
+    case 1:
       hipLaunchKernelGGL(sort_hist_kernel, dim3(nchunks), dim3(kWave), 0, s, ids, P, E, chunk);
       break;
-    case 1:
+    case 2:
       hipLaunchKernelGGL(sort_chunk_scan_kernel, dim3(E), dim3(256), 0, s, chunk, nchunks, E, counts);
       break;
     default:

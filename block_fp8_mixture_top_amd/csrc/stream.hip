@@ -16,6 +16,7 @@
 // straddles a 128-wide scale block, so each chunk needs one scale.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -58,22 +59,96 @@ __device__ __forceinline__ float dot16_f32(const u32x4& c, const float* v) {
 
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR == kWave) {
+    return wave_sum_dpp(v);
+  } else {
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+  }
 }
 
+// Routing done inside GEMM1 for small batches: one token per wave.
+constexpr int kFuseTokens = kThreads / kWave;
+constexpr int kFuseMaxPairs = kFuseTokens * 32;
+
 // GEMM1 + silu*up. grid.x: tiles of row pairs, grid.y: expert slots. A lane group owns RP
-// consecutive row pairs (gate i, up I+i) of slot's expert, loads their codes once and
+// consecutive row pairs (gate i, up I+i) of the slot's expert, loads their codes once and
 // applies them to every token routed to that expert.
-template <int LPR, int MCH, int RP>
-__global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden, BankArg w13,
-                                                               Plan plan, int H, int I, int k,
-                                                               float* __restrict__ h) {
-  const int e = plan.act[blockIdx.y];
-  if (e < 0) return;
+//
+// PER > 0: the workgroup routes the T <= 4 tokens itself (wave_topk with PER logits per
+// lane), marks the routed experts in an LDS bitmap, takes the slot-th one (ascending id)
+// and lists its pairs; workgroup (0, 0) also writes ids and weights for the down GEMM.
+// PER == 0: the slot's expert and pairs come from the sorted plan in global memory.
+template <int LPR, int MCH, int RP, int PER>
+__global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden,
+                                                               const float* __restrict__ logits, int T, int E,
+                                                               BankArg w13, Plan plan, int H, int I, int k,
+                                                               float* __restrict__ h, int32_t* __restrict__ ids_out,
+                                                               float* __restrict__ w_out) {
   constexpr int GPW = kWave / LPR;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
+  int e, cnt;
+  const int32_t* pairs;
+  __shared__ int s_ids[PER > 0 ? kFuseMaxPairs : 1];
+  __shared__ int s_pairs[PER > 0 ? kFuseMaxPairs : 1];
+  __shared__ uint32_t s_bits[MAX_EXPERTS / 32];
+  __shared__ int s_e, s_m;
+  if constexpr (PER > 0) {
+    const int P = T * k;
+    if (threadIdx.x < MAX_EXPERTS / 32) s_bits[threadIdx.x] = 0u;
+    if (wave < T) {
+      int id;
+      float wt;
+      wave_topk<PER>(logits + (size_t)wave * E, E, k, id, wt);
+      if (lane < k) {
+        s_ids[wave * k + lane] = id;
+        if (blockIdx.x == 0 && blockIdx.y == 0) {
+          ids_out[wave * k + lane] = id;
+          w_out[wave * k + lane] = wt;
+        }
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < P) atomicOr(&s_bits[s_ids[threadIdx.x] >> 5], 1u << (s_ids[threadIdx.x] & 31));
+    __syncthreads();
+    if (wave == 0) {
+      const int slot = blockIdx.y;
+      const uint32_t word = lane < MAX_EXPERTS / 32 ? s_bits[lane] : 0u;
+      const int c = __popc(word);
+      const int incl = wave_incl_scan(c);
+      const int total = __shfl(incl, kWave - 1, kWave);
+      if (slot >= total) {
+        if (lane == 0) s_e = -1;
+      } else if (slot >= incl - c && slot < incl) {
+        uint32_t b = word;
+        for (int r = slot - (incl - c); r > 0; --r) b &= b - 1u;
+        s_e = lane * 32 + __builtin_ctz(b);
+      }
+    }
+    __syncthreads();
+    e = s_e;
+    if (e < 0) return;
+    if (wave == 0) {
+      int m = 0;
+      for (int base = 0; base < P; base += kWave) {
+        const int p = base + lane;
+        const bool hit = p < P && s_ids[p] == e;
+        const uint64_t bal = __ballot(hit);
+        if (hit) s_pairs[m + __popcll(bal & ((1ull << lane) - 1ull))] = p;
+        m += __popcll(bal);
+      }
+      if (lane == 0) s_m = m;
+    }
+    __syncthreads();
+    cnt = s_m;
+    pairs = s_pairs;
+  } else {
+    e = plan.act[blockIdx.y];
+    if (e < 0) return;
+    cnt = plan.counts[e];
+    pairs = plan.sorted + plan.offsets[e];
+  }
   const int grp = lane / LPR, gl = lane % LPR;
   const int rows_per_block = (kThreads / kWave) * GPW * RP;
   const int i0 = blockIdx.x * rows_per_block + (wave * GPW + grp) * RP;
@@ -102,10 +177,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       }
     }
   }
-  const int beg = plan.offsets[e];
-  const int cnt = plan.counts[e];
   for (int q = 0; q < cnt; ++q) {
-    const int p = plan.sorted[beg + q];
+    const int p = pairs[q];
     const int t = p / k;
     const uint8_t* xb = (const uint8_t*)(hidden + (size_t)t * H);
     u32x4 x0[MCH], x1[MCH];
@@ -194,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __r
     float acc = 0.0f;
 #pragma unroll
     for (int m = 0; m < MC; ++m) acc = __builtin_fmaf(ws[m], dot16_f32(cw[r][m], hv[m]), acc);
-    acc = wave_sum(acc);
+    acc = wave_sum_dpp(acc);
     if (lane == 0) red[wave][r] = acc;
   }
   __syncthreads();
@@ -299,13 +372,21 @@ Layout pick_layout(int K) {
   return Layout{lpr, (nc + lpr - 1) / lpr};
 }
 
-template <int LPR, int MCH, int RP>
-hipError_t g1(const uint16_t* x, const BankArg& w, const Plan& p, int slots, int H, int I, int k, float* h,
-              hipStream_t s) {
+template <int LPR, int MCH, int RP, int PER>
+hipError_t g1(const Gemm1Args& a, hipStream_t s) {
   const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
-  dim3 grid((I + rows - 1) / rows, slots);
-  hipLaunchKernelGGL((gemm1_w8a16_kernel<LPR, MCH, RP>), grid, dim3(kThreads), 0, s, x, w, p, H, I, k, h);
+  dim3 grid((a.I + rows - 1) / rows, a.slots);
+  hipLaunchKernelGGL((gemm1_w8a16_kernel<LPR, MCH, RP, PER>), grid, dim3(kThreads), 0, s, a.hidden, a.logits, a.T,
+                     a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
   return hipGetLastError();
+}
+
+template <int LPR, int MCH, int RP>
+hipError_t g1r(const Gemm1Args& a, hipStream_t s) {
+  if (!a.fused) return g1<LPR, MCH, RP, 0>(a, s);
+  hipError_t err = hipErrorInvalidValue;
+  MOE_TOPK_DISPATCH(a.E, err = (g1<LPR, MCH, RP, PER>(a, s)));
+  return err;
 }
 
 template <int LPR, int MCH, int RP>
@@ -319,28 +400,26 @@ hipError_t g2e(const float* h, const BankArg& w, const Plan& p, int slots, int H
 
 }  // namespace
 
-hipError_t launch_gemm1_w8a16(const uint16_t* hidden, const BankArg& w13, const Plan& plan, int slots, int H,
-                              int I, int k, float* h, hipStream_t s) {
-  const Layout L = pick_layout(H);
+bool gemm1_fused_route_ok(int T, int k) { return T >= 1 && T <= kFuseTokens && T * k <= kFuseMaxPairs; }
+
+hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s) {
+  const Layout L = pick_layout(a.H);
   if (L.lpr == 64) {
     switch (L.mch) {
-      case 1: return g1<64, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 2: return g1<64, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 3: return g1<64, 3, 1>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 4: return g1<64, 4, 1>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 5: return g1<64, 5, 1>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 6: return g1<64, 6, 1>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 7: return g1<64, 7, 1>(hidden, w13, plan, slots, H, I, k, h, s);
-      case 8: return g1<64, 8, 1>(hidden, w13, plan, slots, H, I, k, h, s);
+      case 1: return g1r<64, 1, 2>(a, s);
+      case 2: return g1r<64, 2, 2>(a, s);
+      case 3: return g1r<64, 3, 1>(a, s);
+      case 4: return g1r<64, 4, 1>(a, s);
+      case 5: return g1r<64, 5, 1>(a, s);
+      case 6: return g1r<64, 6, 1>(a, s);
+      case 7: return g1r<64, 7, 1>(a, s);
+      case 8: return g1r<64, 8, 1>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
-  if (L.lpr == 32) return L.mch == 1 ? g1<32, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
-                                     : g1<32, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
-  if (L.lpr == 16) return L.mch == 1 ? g1<16, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
-                                     : g1<16, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
-  return L.mch == 1 ? g1<8, 1, 2>(hidden, w13, plan, slots, H, I, k, h, s)
-                    : g1<8, 2, 2>(hidden, w13, plan, slots, H, I, k, h, s);
+  if (L.lpr == 32) return L.mch == 1 ? g1r<32, 1, 2>(a, s) : g1r<32, 2, 2>(a, s);
+  if (L.lpr == 16) return L.mch == 1 ? g1r<16, 1, 2>(a, s) : g1r<16, 2, 2>(a, s);
+  return L.mch == 1 ? g1r<8, 1, 2>(a, s) : g1r<8, 2, 2>(a, s);
 }
 
 hipError_t launch_gemm2_expert(const float* h, const BankArg& w2, const Plan& plan, int slots, int H, int I,
