@@ -16,57 +16,12 @@
 // straddles a 128-wide scale block, so each chunk needs one scale.
 #include "common.hpp"
 #include "launch.hpp"
+#include "gemv.hpp"
 #include "topk.hpp"
 
 namespace moe {
 
 namespace {
-
-constexpr int kThreads = 256;
-
-// sum_i dec(code_i) * x_i over the 16 codes of `c` and the 16 bf16 activations of `x0,x1`.
-__device__ __forceinline__ float dot16_bf16(const u32x4& c, const u32x4& x0, const u32x4& x1) {
-  float acc = 0.0f;
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-  const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x2 lo = dec2<false>(cw[q]);
-    const f32x2 hi = dec2<true>(cw[q]);
-    acc = __builtin_fmaf(lo.x, bf16_lo(xw[2 * q]), acc);
-    acc = __builtin_fmaf(lo.y, bf16_hi(xw[2 * q]), acc);
-    acc = __builtin_fmaf(hi.x, bf16_lo(xw[2 * q + 1]), acc);
-    acc = __builtin_fmaf(hi.y, bf16_hi(xw[2 * q + 1]), acc);
-  }
-  return acc;
-}
-
-// sum_i dec(code_i) * v_i over 16 codes and 16 floats.
-__device__ __forceinline__ float dot16_f32(const u32x4& c, const float* v) {
-  float acc = 0.0f;
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x2 lo = dec2<false>(cw[q]);
-    const f32x2 hi = dec2<true>(cw[q]);
-    acc = __builtin_fmaf(lo.x, v[4 * q + 0], acc);
-    acc = __builtin_fmaf(lo.y, v[4 * q + 1], acc);
-    acc = __builtin_fmaf(hi.x, v[4 * q + 2], acc);
-    acc = __builtin_fmaf(hi.y, v[4 * q + 3], acc);
-  }
-  return acc;
-}
-
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (LPR == kWave) {
-    return wave_sum_dpp(v);
-  } else {
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-  }
-}
 
 // Routing done inside GEMM1 for small batches: one token per wave.
 constexpr int kFuseTokens = kThreads / kWave;
@@ -76,9 +31,13 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // consecutive row pairs (gate i, up I+i) of the slot's expert, loads their codes once and
 // applies them to every token routed to that expert.
 //
-// PER > 0: the workgroup routes the T <= 4 tokens itself (wave_topk with PER logits per
-// lane), marks the routed experts in an LDS bitmap, takes the slot-th one (ascending id)
-// and lists its pairs; workgroup (0, 0) also writes ids and weights for the down GEMM.
+// PER > 0 routes inside the kernel (wave_topk_ids with PER logits per lane):
+//   T == 1: every wave routes the token itself, with no barrier; the slot-th expert in
+//   ascending id is the one whose id ranks `slot` among the token's top_k distinct ids.
+//   2 <= T <= 4: one wave per token, an LDS bitmap of routed experts gives the slot-th one
+//   and its pairs.
+// Workgroup (0, 0) writes the ids and weights for the down GEMM; the weights (double exp and
+// sum) are computed after the weight loads are issued, off the critical path.
 // PER == 0: the slot's expert and pairs come from the sorted plan in global memory.
 template <int LPR, int MCH, int RP, int PER>
 __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden,
@@ -88,71 +47,94 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
                                                                float* __restrict__ w_out) {
   constexpr int GPW = kWave / LPR;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  int e, cnt;
-  const int32_t* pairs;
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int NC = H / 16;
+  int e, cnt = 0, single = -1;  // single: the only pair (T == 1)
+  const int32_t* pairs = nullptr;
+  int my_id = 0;
+  float my_l = 0.0f;
+  bool route_wave = false;  // this wave holds a token's routing (lanes < k)
+  int route_tok = 0;
   __shared__ int s_ids[PER > 0 ? kFuseMaxPairs : 1];
   __shared__ int s_pairs[PER > 0 ? kFuseMaxPairs : 1];
   __shared__ uint32_t s_bits[MAX_EXPERTS / 32];
   __shared__ int s_e, s_m;
+  // x of token 0, issued before routing when T == 1
+  u32x4 x0[MCH], x1[MCH];
   if constexpr (PER > 0) {
-    const int P = T * k;
-    if (threadIdx.x < MAX_EXPERTS / 32) s_bits[threadIdx.x] = 0u;
-    if (wave < T) {
-      int id;
-      float wt;
-      wave_topk<PER>(logits + (size_t)wave * E, E, k, id, wt);
-      if (lane < k) {
-        s_ids[wave * k + lane] = id;
-        if (blockIdx.x == 0 && blockIdx.y == 0) {
-          ids_out[wave * k + lane] = id;
-          w_out[wave * k + lane] = wt;
+    if (T == 1) {
+#pragma unroll
+      for (int m = 0; m < MCH; ++m) {
+        const int c = gl + LPR * m;
+        if (c < NC) {
+          x0[m] = ld16((const uint8_t*)hidden + (size_t)c * 32);
+          x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
+        } else {
+          x0[m] = u32x4{0, 0, 0, 0};
+          x1[m] = u32x4{0, 0, 0, 0};
         }
       }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < P) atomicOr(&s_bits[s_ids[threadIdx.x] >> 5], 1u << (s_ids[threadIdx.x] & 31));
-    __syncthreads();
-    if (wave == 0) {
-      const int slot = blockIdx.y;
-      const uint32_t word = lane < MAX_EXPERTS / 32 ? s_bits[lane] : 0u;
-      const int c = __popc(word);
-      const int incl = wave_incl_scan(c);
-      const int total = __shfl(incl, kWave - 1, kWave);
-      if (slot >= total) {
-        if (lane == 0) s_e = -1;
-      } else if (slot >= incl - c && slot < incl) {
-        uint32_t b = word;
-        for (int r = slot - (incl - c); r > 0; --r) b &= b - 1u;
-        s_e = lane * 32 + __builtin_ctz(b);
+      wave_topk_ids<PER>(logits, E, k, my_id, my_l);
+      route_wave = wave == 0;
+      int rank = 0;
+      for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(my_id, j) < my_id ? 1 : 0;
+      const uint64_t hit = __ballot(lane < k && rank == (int)blockIdx.y);
+      if (hit == 0ull) return;  // no such slot (never for T == 1: slots == top_k)
+      single = __builtin_ctzll(hit);
+      e = __builtin_amdgcn_readlane(my_id, single);
+      cnt = 1;
+    } else {
+      const int P = T * k;
+      if (threadIdx.x < MAX_EXPERTS / 32) s_bits[threadIdx.x] = 0u;
+      if (wave < T) {
+        wave_topk_ids<PER>(logits + (size_t)wave * E, E, k, my_id, my_l);
+        route_wave = true;
+        route_tok = wave;
+        if (lane < k) s_ids[wave * k + lane] = my_id;
       }
-    }
-    __syncthreads();
-    e = s_e;
-    if (e < 0) return;
-    if (wave == 0) {
-      int m = 0;
-      for (int base = 0; base < P; base += kWave) {
-        const int p = base + lane;
-        const bool hit = p < P && s_ids[p] == e;
-        const uint64_t bal = __ballot(hit);
-        if (hit) s_pairs[m + __popcll(bal & ((1ull << lane) - 1ull))] = p;
-        m += __popcll(bal);
+      __syncthreads();
+      if ((int)threadIdx.x < P) atomicOr(&s_bits[s_ids[threadIdx.x] >> 5], 1u << (s_ids[threadIdx.x] & 31));
+      __syncthreads();
+      if (wave == 0) {
+        const int slot = blockIdx.y;
+        const uint32_t word = lane < MAX_EXPERTS / 32 ? s_bits[lane] : 0u;
+        const int c = __popc(word);
+        const int incl = wave_incl_scan(c);
+        const int total = __shfl(incl, kWave - 1, kWave);
+        if (slot >= total) {
+          if (lane == 0) s_e = -1;
+        } else if (slot >= incl - c && slot < incl) {
+          uint32_t b = word;
+          for (int r = slot - (incl - c); r > 0; --r) b &= b - 1u;
+          s_e = lane * 32 + __builtin_ctz(b);
+        }
       }
-      if (lane == 0) s_m = m;
+      __syncthreads();
+      e = s_e;
+      if (e < 0) return;
+      if (wave == 0) {
+        int m = 0;
+        for (int base = 0; base < P; base += kWave) {
+          const int p = base + lane;
+          const bool hit = p < P && s_ids[p] == e;
+          const uint64_t bal = __ballot(hit);
+          if (hit) s_pairs[m + __popcll(bal & ((1ull << lane) - 1ull))] = p;
+          m += __popcll(bal);
+        }
+        if (lane == 0) s_m = m;
+      }
+      __syncthreads();
+      cnt = s_m;
+      pairs = s_pairs;
     }
-    __syncthreads();
-    cnt = s_m;
-    pairs = s_pairs;
   } else {
     e = plan.act[blockIdx.y];
     if (e < 0) return;
     cnt = plan.counts[e];
     pairs = plan.sorted + plan.offsets[e];
   }
-  const int grp = lane / LPR, gl = lane % LPR;
   const int rows_per_block = (kThreads / kWave) * GPW * RP;
   const int i0 = blockIdx.x * rows_per_block + (wave * GPW + grp) * RP;
-  const int NC = H / 16;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
   const int64_t sb = (int64_t)e * w13.sexp;
 
@@ -177,20 +159,30 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       }
     }
   }
+  if constexpr (PER > 0) {
+    // the router weights, while the weight codes are in flight
+    if (route_wave && blockIdx.x == 0 && blockIdx.y == 0) {
+      const float wt = wave_topk_weight(my_l, k);
+      if (lane < k) {
+        ids_out[route_tok * k + lane] = my_id;
+        w_out[route_tok * k + lane] = wt;
+      }
+    }
+  }
   for (int q = 0; q < cnt; ++q) {
-    const int p = pairs[q];
-    const int t = p / k;
-    const uint8_t* xb = (const uint8_t*)(hidden + (size_t)t * H);
-    u32x4 x0[MCH], x1[MCH];
+    const int p = single >= 0 ? single : pairs[q];
+    if (single < 0) {
+      const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
 #pragma unroll
-    for (int m = 0; m < MCH; ++m) {
-      const int c = gl + LPR * m;
-      if (c < NC) {
-        x0[m] = ld16(xb + (size_t)c * 32);
-        x1[m] = ld16(xb + (size_t)c * 32 + 16);
-      } else {
-        x0[m] = u32x4{0, 0, 0, 0};
-        x1[m] = u32x4{0, 0, 0, 0};
+      for (int m = 0; m < MCH; ++m) {
+        const int c = gl + LPR * m;
+        if (c < NC) {
+          x0[m] = ld16(xb + (size_t)c * 32);
+          x1[m] = ld16(xb + (size_t)c * 32 + 16);
+        } else {
+          x0[m] = u32x4{0, 0, 0, 0};
+          x1[m] = u32x4{0, 0, 0, 0};
+        }
       }
     }
 #pragma unroll
@@ -356,20 +348,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   for (int j = 0; j < k; ++j) s = __builtin_fmaf(w[t * k + j], y[(t * k + j) * H + n], s);
   if (out_bf16) ((uint16_t*)out)[idx] = f32_to_bf16(s);
   else ((float*)out)[idx] = s;
-}
-
-// ---- launch helpers: pick the lane layout for a K of `K` bytes per row
-
-struct Layout {
-  int lpr, mch;
-};
-
-Layout pick_layout(int K) {
-  const int nc = K / 16;
-  if (nc >= kWave) return Layout{kWave, (nc + kWave - 1) / kWave};
-  int lpr = 8;
-  while (lpr * 2 <= nc && lpr < kWave) lpr *= 2;
-  return Layout{lpr, (nc + lpr - 1) / lpr};
 }
 
 template <int LPR, int MCH, int RP, int PER>

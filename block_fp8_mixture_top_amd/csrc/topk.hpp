@@ -6,43 +6,78 @@
 
 namespace moe {
 
-// Lane j < k receives slot j: the expert with the j-th largest logit (ties to the lower
-// id) and its weight exp(l_j - l_0) / sum_i exp(l_i - l_0), evaluated in double with the
-// sum in slot order and rounded to float. PER = logits held per lane, E <= 64 * PER. A NaN
-// logit reads as -inf, which keeps every id in [0, E). Call with all 64 lanes active.
+// Selection: lane j < k receives slot j, the expert with the j-th largest logit (ties to the
+// lower id), and that logit. PER = logits held per lane, E <= 64 * PER. A NaN logit reads as
+// -inf, which keeps every id in [0, E). Call with all 64 lanes active.
+//
+// Each lane first sorts its PER (key, id) pairs best-first, so its current best is always
+// its head; a round is then one wave-wide max of the heads, a ballot of the lanes holding
+// that key (one lane unless logits tie exactly; the lowest id among tied heads is taken by a
+// min over them), and the winning lane advancing its head.
 template <int PER>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& out_id, float& out_w) {
+__device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
+                                              float& out_l) {
   const int lane = lane_id();
   uint32_t key[PER];
+  int idx[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + kWave * i;
     float f = e < E ? row[e] : 0.0f;
     f = f != f ? -__builtin_inff() : f;
     key[i] = e < E ? order_key(f) : 0u;  // every real logit has a key > 0
+    idx[i] = e;
   }
-  uint32_t taken = 0;
-  float my_l = 0.0f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    uint32_t bk = 0;
-    int bi = 0;
+  // insertion sort, best first: larger key, then lower id (ids rise with i, so a strict
+  // comparison keeps equal keys in id order)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t c = ((taken >> i) & 1u) ? 0u : key[i];
-      if (c > bk) {  // strict: the lowest id of a lane wins its ties
-        bk = c;
-        bi = lane + kWave * i;
-      }
+  for (int i = 1; i < PER; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t tk = sw ? key[j] : key[j - 1];
+      const uint32_t bk = sw ? key[j - 1] : key[j];
+      const int ti = sw ? idx[j] : idx[j - 1];
+      const int bi = sw ? idx[j - 1] : idx[j];
+      key[j - 1] = tk;
+      key[j] = bk;
+      idx[j - 1] = ti;
+      idx[j] = bi;
     }
-    const uint32_t mk = wave_max_u32(bk);
-    const uint32_t wid = wave_min_u32(bk == mk ? (uint32_t)bi : 0xFFFFFFFFu);
-    if ((int)(wid & (kWave - 1)) == lane) taken |= 1u << (wid / kWave);
+  int my_id = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t mk = wave_max_u32(key[0]);
+    const uint64_t cand = __ballot(key[0] == mk);
+    int win;
+    if (__popcll(cand) == 1) {
+      win = __builtin_ctzll(cand);
+    } else {
+      const uint32_t wid = wave_min_u32(key[0] == mk ? (uint32_t)idx[0] : 0xFFFFFFFFu);
+      win = (int)(wid & (kWave - 1));
+    }
+    const int wid = __builtin_amdgcn_readlane(idx[0], win);
     if (lane == j) {
-      my_id = (int)wid;
+      my_id = wid;
       my_l = key_to_float(mk);
     }
+    if (lane == win) {  // advance this lane's head
+#pragma unroll
+      for (int i = 0; i + 1 < PER; ++i) {
+        key[i] = key[i + 1];
+        idx[i] = idx[i + 1];
+      }
+      key[PER - 1] = 0u;
+    }
   }
+  out_id = my_id;
+  out_l = my_l;
+}
+
+// Weights of the selected slots: lane j < k gets exp(l_j - l_0) / sum_i exp(l_i - l_0),
+// evaluated in double with the sum in slot order and rounded to float.
+__device__ __forceinline__ float wave_topk_weight(float my_l, int k) {
+  const int lane = lane_id();
   const double l0 = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
   const double ex = lane < k ? exp((double)my_l - l0) : 0.0;
   double tot = 0.0;
@@ -52,8 +87,15 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), j);
     tot += __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
   }
-  out_id = my_id;
-  out_w = (float)(ex / tot);
+  return (float)(ex / tot);
+}
+
+// Both: ids and weights.
+template <int PER>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& out_id, float& out_w) {
+  float l;
+  wave_topk_ids<PER>(row, E, k, out_id, l);
+  out_w = wave_topk_weight(l, k);
 }
 
 // Dispatch helper: the smallest PER in {1, 2, 4, 8, 16} with 64 * PER >= E.
