@@ -85,18 +85,13 @@ int gate(int T, int E, int top_k, const moe_opts& o) {
   return MOE_PATH_STREAM;
 }
 
-bool mfma_supported(int H, int I) {
-  const int nt = I / 64;
-  return (nt == 2 || nt == 4 || nt == 6 || nt == 8) && H % 128 == 0;
-}
-
 // Path actually run: the gate's choice, moved off a path the shapes do not fit only when
 // the caller left the choice to the gate.
 int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* path) {
   int p = gate(T, E, top_k, o);
   const bool forced = o.force_path != MOE_PATH_AUTO;
-  if (p == MOE_PATH_MFMA && !mfma_supported(H, I)) {
-    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs I in {128,256,384,512} (got I=%d)", I);
+  if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 2048 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
     p = MOE_PATH_STREAM;
   }
   if (p == MOE_PATH_GATHER && !moe::gemm2_gather_supported(top_k, I)) {
@@ -119,7 +114,7 @@ struct Carve {
 // Workspace layout; offsets into the caller's buffer.
 struct Layout {
   size_t ids, w, counts, offsets, sorted, act, n_act, tile_off, scratch;
-  size_t h, y, xq, xs, hq, hs, acc;
+  size_t h, y, xq, xs, hq, hs;
   size_t total;
 };
 
@@ -138,13 +133,12 @@ Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
   L.tile_off = c.take((size_t)(E + 1) * 4);
   L.scratch = c.take(moe::sort_scratch_bytes((int)P, E));
   if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) L.h = c.take(P * (size_t)I * 4);
-  if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);
+  if (path == MOE_PATH_STREAM || path == MOE_PATH_MFMA) L.y = c.take(P * (size_t)H * 4);
   if (path == MOE_PATH_MFMA) {
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
     L.hq = c.take(P * (size_t)I);
     L.hs = c.take(P * 4);
-    L.acc = c.take((size_t)T * H * 4);
   }
   L.total = c.off;
   return L;
@@ -334,6 +328,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   if (T == 0) return ok();
   if (!hidden || !logits || !out) return fail(MOE_ERR_ARG, "hidden, logits and out must be non-NULL");
   if (!aligned16(hidden)) return fail(MOE_ERR_ALIGN, "hidden must be 16-byte aligned");
+  if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out must be 16-byte aligned");
   const Layout L = layout_for(path, T, E, H, I, top_k);
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
@@ -382,13 +377,12 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     float* xs = at<float>(workspace, L.xs);
     uint8_t* hq = at<uint8_t>(workspace, L.hq);
     float* hs = at<float>(workspace, L.hs);
-    float* acc = out_bf16 ? at<float>(workspace, L.acc) : (float*)out;
+    float* y = at<float>(workspace, L.y);
     RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
-    RUN(MOE_K_ZERO, moe::launch_zero_f32(acc, (size_t)T * H, s), "zero launch");
     RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hq, hs, s),
         "gemm1 mfma launch");
-    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, top_k, acc, s), "gemm2 mfma launch");
-    if (out_bf16) RUN(MOE_K_FINALIZE, moe::launch_finalize(acc, (size_t)T * H, out, 1, s), "finalize launch");
+    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, top_k, y, s), "gemm2 mfma launch");
+    RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
   }
   if (info) info->kernels = R.n;
   return ok();

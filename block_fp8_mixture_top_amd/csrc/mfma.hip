@@ -9,13 +9,16 @@
 // One v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 scales) covers exactly one 128-wide
 // K block, so every MFMA result is one block's partial sum and is multiplied by that block's
 // bank scale before it is accumulated (FreeToken PR #662, PR body: one scale per 128x128
-// block). A and B are loaded with the same per-lane K pattern (32 contiguous bytes of a
-// row per lane), so whatever order the unit walks K in, matching A and B bytes meet.
+// block). A and B are read with the same per-lane K pattern (chunks kq and kq + 4 of the
+// block for lanes of K quarter kq), so whatever order the unit walks K in, matching A and
+// B bytes meet.
 //
-// GEMM1 covers all 2I features of a tile of sorted pairs, so the epilogue has the whole h
-// row: silu(gate)*up, row amax, scale and e4m3 codes are produced without writing h in
-// float. GEMM2 multiplies by the pair's h scale and router weight and adds into a float
-// [T, H] accumulator with atomics (the scatter-add combine).
+// Both GEMMs work on tiles of 64 sorted (token, slot) pairs of one expert. Every operand
+// goes global -> LDS with direct loads of 8 rows x 128 contiguous bytes per instruction,
+// through LDS rings a few K blocks ahead of the multiply. GEMM1 covers all 2I features of its
+// tile, so its epilogue has whole h rows: silu(gate)*up, row amax, scale and e4m3 codes are
+// produced without writing h in float. GEMM2 writes each pair's y row in float once; the
+// combine kernel sums the slots of a token in slot order with the router weights.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,22 +33,6 @@ constexpr int kNeutralScale = 127;  // E8M0 2^0
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
   const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, kNeutralScale, 0, kNeutralScale);
-}
-
-__device__ __forceinline__ i32x8 ld32(const uint8_t* p) {
-  const u32x4 lo = *(const u32x4*)p;
-  const u32x4 hi = *(const u32x4*)(p + 16);
-  i32x8 r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
-
-__device__ __forceinline__ i32x8 zero8() {
-  i32x8 r;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r[q] = 0;
-  return r;
 }
 
 // ---------------------------------------------------------------- per-row quantisation
@@ -108,225 +95,389 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
   return x * per + i;
 }
 
+
+// ---------------------------------------------------------------- shared tile machinery
+
+// silu with the hardware exp and reciprocal (about 1 ulp each). h feeds a quantiser whose
+// decisions the parity check already treats as uncertain within the accumulation error of
+// the matrix cores, which is orders of magnitude larger.
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+constexpr int kTM = kMfmaTileM;  // pairs per tile: four 16-row MFMA tiles
+constexpr int kMaxH = 8192;      // bounds the block-scale slabs staged in LDS
+constexpr int kMaxI = 512;       // GEMM1 keeps 64 x I h values in registers
+constexpr int kStages = 3;       // depth of the LDS rings
+constexpr int kRowB = 128;       // bytes of one row in one 128-wide K block
+
+// LDS rows hold one 128-byte K block; 16-byte chunk c of row r sits at chunk position
+// c ^ sw(r), so the 16 consecutive rows one operand read touches (same chunk) fall on
+// distinct banks whether the LDS serves 128 or 256 bytes a clock.
+__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 3)) & 7; }
+
+// One direct global->LDS load: lane j copies 16 bytes from its own address g to
+// lds + 16 j (lds wave-uniform). Issued as 8 rows x 128 contiguous bytes per instruction
+// (lane j: row j/8, chunk position j%8), the pattern the load path serves at full rate;
+// an MFMA operand read straight from global memory would touch 16 rows per instruction.
+// Written as inline asm so that the compiler does not track it: its own LDS-DMA tracking
+// inserts a full vmcnt(0) wait before LDS reads of other ring slots, which would undo the
+// prefetch. Completion is therefore awaited explicitly (wait_vm); waits the compiler adds
+// for its own loads can only be stricter. M0 (the LDS base of the DMA) is set here; these
+// kernels use M0 for nothing else, and the instruction after an M0 write needs one wait state.
+__device__ __forceinline__ void g2lds(const void* g, const uint8_t* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
+}
+
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence. LDS that direct loads fill is covered by each
+// wave's own wait_vm before the barrier; the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 32 operand bytes (chunks kq and kq + 4 of K block) of row r of a swizzled LDS slab.
+__device__ __forceinline__ i32x8 lds_operand(const uint8_t* slab, int r, int kq) {
+  const u32x4 lo = *(const u32x4*)(slab + r * kRowB + ((kq ^ sw(r)) << 4));
+  const u32x4 hi = *(const u32x4*)(slab + r * kRowB + (((kq + 4) ^ sw(r)) << 4));
+  i32x8 o;
+  o[0] = (int)lo.x; o[1] = (int)lo.y; o[2] = (int)lo.z; o[3] = (int)lo.w;
+  o[4] = (int)hi.x; o[5] = (int)hi.y; o[6] = (int)hi.z; o[7] = (int)hi.w;
+  return o;
+}
+
+// The block scales of one expert's bank as float in LDS: s[row_block * cols + col_block].
+__device__ __forceinline__ void stage_scales(float* s, const BankArg& b, int64_t sb, int rows, int cols) {
+  for (int q = threadIdx.x; q < rows * cols; q += 256)
+    s[q] = load_scale(b.scales, b.scale_bf16, sb + (int64_t)(q / cols) * b.srow + q % cols);
+}
+
 // ---------------------------------------------------------------- GEMM1
 
-constexpr int kTM = kMfmaTileM;  // pairs per tile (two 16-row MFMA tiles)
+// One workgroup per (expert, 64-pair tile), 4 waves. NP = I/128 passes; in pass ps wave w
+// owns gate features ps*128 + 32w .. +32 (two 16-row MFMA tiles) and the matching up
+// features, for all 64 pairs. Every K block of every pass is a stage of a 3-deep LDS ring:
+// each wave copies in the 64 weight rows it multiplies, and the four waves together copy
+// the tile's 64 token rows of x. One barrier per stage. A = weight rows (features),
+// B = token rows, so lane (r16, kq) of a 16x16 result holds features 4kq..4kq+3 of token r16.
+template <int NP>
+__global__ __launch_bounds__(256, 1) void gemm1_mfma_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                            BankArg w13, Plan plan, int E, int H, int I, int k,
+                                                            int nblocks, uint8_t* __restrict__ hq,
+                                                            float* __restrict__ hs) {
+  constexpr int G = 2;                   // gate tiles per wave per pass (and as many up tiles)
+  constexpr int NF = 2 * G;              // weight tiles per wave per pass
+  constexpr int WB = 64 * kRowB;         // one wave's weight rows of a stage
+  constexpr int XB = kTM * kRowB;        // the tile's x rows of a stage
+  constexpr int SB = 4 * WB + XB;        // one stage
+  constexpr int LPW = 8 + 2;             // direct loads per wave per stage
+  __shared__ __align__(16) uint8_t ring[kStages * SB];
+  __shared__ float s_sc[(2 * kMaxI / 128) * (kMaxH / 128)];
+  __shared__ float s_amax[4][kTM];
+  __shared__ int s_tok[kTM];
 
-// grid: one workgroup per (expert, 32-pair tile), 4 waves. Wave w owns gate features
-// [w*I/4, (w+1)*I/4) and the up features I + the same range: NT 16-feature MFMA tiles each.
-template <int NT>
-__global__ __launch_bounds__(256) void gemm1_mfma_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
-                                                         BankArg w13, Plan plan, int E, int H, int I, int k,
-                                                         int nblocks, uint8_t* __restrict__ hq,
-                                                         float* __restrict__ hs) {
-  __shared__ float amax_w[4][kTM];
   const int tile = xcd_tile(blockIdx.x, nblocks);
   if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
   const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM;
   const int pos_end = plan.offsets[e + 1];
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int r16 = lane & 15, kq = lane >> 4;  // row within a 16-tile, K quarter (32 bytes)
-
-  // B operand rows: the tokens of the two pair tiles
-  const uint8_t* xrow[2];
-  bool tok_ok[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = pos0 + tt * 16 + r16;
-    tok_ok[tt] = pos < pos_end;
-    const int t = tok_ok[tt] ? plan.sorted[pos] / k : 0;
-    xrow[tt] = xq + (size_t)t * H;
-  }
-  const int fbase = wave * (I / 4);  // first gate feature of this wave
+  const int nvalid = pos_end - pos0 < kTM ? pos_end - pos0 : kTM;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int r16 = lane & 15, kq = lane >> 4;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
-  const int64_t sb = (int64_t)e * w13.sexp;
-
-  f32x4 accg[NT][2], accu[NT][2];
-#pragma unroll
-  for (int f = 0; f < NT; ++f)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      accg[f][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      accu[f][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
   const int nkb = H / 128;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int kofs = kb * 128 + kq * 32;
-    i32x8 b[2];
+
+  // token of each tile row (rows past the expert's pairs repeat the first token; their
+  // results are never stored)
+  if ((int)threadIdx.x < kTM)
+    s_tok[threadIdx.x] = plan.sorted[pos0 + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0)] / k;
+  stage_scales(s_sc, w13, (int64_t)e * w13.sexp, 2 * I / 128, nkb);
+  __syncthreads();
+  float xsc[4];  // x scale of token tt*16 + r16
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) b[tt] = tok_ok[tt] ? ld32(xrow[tt] + kofs) : zero8();
+  for (int tt = 0; tt < 4; ++tt) xsc[tt] = xs[s_tok[tt * 16 + r16]];
+
+  // direct-load sources. Weight instruction i covers rows 8i .. 8i+7 of the wave's 64
+  // (rows 0..31 gate, 32..63 up); pass ps adds 128 rows and K block kb adds kb*128 bytes.
+  const int lr = lane >> 3, lc = lane & 7;
+  uint32_t woff[8];
 #pragma unroll
-    for (int f = 0; f < NT; ++f) {
-      const int rg = fbase + f * 16;  // gate rows rg..rg+15, up rows I+rg..
-      const i32x8 ag = ld32(wb + (size_t)(rg + r16) * H + kofs);
-      const i32x8 au = ld32(wb + (size_t)(I + rg + r16) * H + kofs);
-      const float sg = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)(rg / kScaleBlock) * w13.srow + kb);
-      const float su = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)((I + rg) / kScaleBlock) * w13.srow + kb);
+  for (int i = 0; i < 8; ++i) {
+    const int b = i * 8 + lr;
+    const int row = (b < 32 ? 0 : I - 32) + wave * 32 + b;
+    woff[i] = (uint32_t)row * (uint32_t)H + (uint32_t)((lc ^ sw(b)) << 4);
+  }
+  // x instruction i covers tile rows 16w + 8i .. +7
+  const uint8_t* xsrc[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 pg = mfma_fp8(ag, b[tt]);
-        const f32x4 pu = mfma_fp8(au, b[tt]);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 16 + i * 8 + lr;
+    xsrc[i] = xq + (size_t)s_tok[r] * H + ((lc ^ sw(r)) << 4);
+  }
+  const int total = NP * nkb;
+  auto issue = [&](int st) {
+    const int ps = st / nkb, kb = st - ps * nkb;
+    uint8_t* slot = ring + (st % kStages) * SB;
+    const uint8_t* src = wb + (size_t)ps * 128 * H + kb * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + wave * WB + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) g2lds(xsrc[i] + kb * 128, slot + 4 * WB + (wave * 16 + i * 8) * kRowB);
+  };
+  issue(0);
+  if (total > 1) issue(1);
+
+  float hkeep[NP][G][4][4];
+  float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    f32x4 acc[NF][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[f][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int st = ps * nkb + kb;
+      // this wave's loads of stage st are in; after the barrier everyone's are, and every
+      // wave is done with stage st - 1, whose slot the next issue refills
+      if (st + 1 < total) wait_vm<LPW>();
+      else wait_vm<0>();
+      bar();
+      if (st + 2 < total) issue(st + 2);
+      const uint8_t* slot = ring + (st % kStages) * SB;
+      const uint8_t* sw_ = slot + wave * WB;
+      const uint8_t* sx_ = slot + 4 * WB;
+      i32x8 bx[4], wa[NF];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) bx[tt] = lds_operand(sx_, tt * 16 + r16, kq);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) wa[f] = lds_operand(sw_, f * 16 + r16, kq);
+      // one scale per K block for the gate rows of this pass, one for the up rows
+      const float sg = s_sc[ps * nkb + kb];
+      const float su = s_sc[(ps + NP) * nkb + kb];
+      // software pipelined: MFMA j + 1 is issued before the scale FMAs of MFMA j
+      f32x4 pp = mfma_fp8(wa[0], bx[0]);
+#pragma unroll
+      for (int j = 0; j < NF * 4; ++j) {
+        const int f = j / 4, tt = j % 4;
+        f32x4 nx;
+        if (j + 1 < NF * 4) nx = mfma_fp8(wa[(j + 1) / 4], bx[(j + 1) % 4]);
+        const float sc = f < G ? sg : su;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[f][tt][q] = __builtin_fmaf(sc, pp[q], acc[f][tt][q]);
+        if (j + 1 < NF * 4) pp = nx;
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < G; ++f)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          accg[f][tt][q] = __builtin_fmaf(sg, pg[q], accg[f][tt][q]);
-          accu[f][tt][q] = __builtin_fmaf(su, pu[q], accu[f][tt][q]);
+          const float g = acc[f][tt][q] * xsc[tt];
+          const float u = acc[f + G][tt][q] * xsc[tt];
+          const float v = silu_fast(g) * u;
+          hkeep[ps][f][tt][q] = v;
+          am[tt] = __builtin_fmaxf(am[tt], __builtin_fabsf(v));
         }
-      }
-    }
   }
-
-  // epilogue: D[feature 4*kq + q][token r16]; h = silu(g) * u with the x scale applied
-  float xsc[2];
+  // row amax over the four K-quarter lane groups, then over the waves
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = pos0 + tt * 16 + r16;
-    xsc[tt] = tok_ok[tt] ? xs[plan.sorted[pos] / k] : 0.0f;
-  }
-  float hv[NT][2][4];
-  float am[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int f = 0; f < NT; ++f)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float g = accg[f][tt][q] * xsc[tt];
-        const float u = accu[f][tt][q] * xsc[tt];
-        const float v = silu(g) * u;
-        hv[f][tt][q] = v;
-        am[tt] = __builtin_fmaxf(am[tt], __builtin_fabsf(v));
-      }
-  // per-token max over the 4 K-quarter lane groups, then over the 4 waves
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < 4; ++tt) {
     am[tt] = __builtin_fmaxf(am[tt], __shfl_xor(am[tt], 16, kWave));
     am[tt] = __builtin_fmaxf(am[tt], __shfl_xor(am[tt], 32, kWave));
-    if (kq == 0) amax_w[wave][tt * 16 + r16] = am[tt];
+    if (kq == 0) s_amax[wave][tt * 16 + r16] = am[tt];
   }
   __syncthreads();
-  float sc[2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < 4; ++tt) {
     const int r = tt * 16 + r16;
-    const float a = __builtin_fmaxf(__builtin_fmaxf(amax_w[0][r], amax_w[1][r]),
-                                    __builtin_fmaxf(amax_w[2][r], amax_w[3][r]));
-    sc[tt] = a > 0.0f ? a / kE4M3Max : 1.0f;
-  }
+    const int pos = pos0 + r;
+    if (pos >= pos_end) continue;
+    const float a = __builtin_fmaxf(__builtin_fmaxf(s_amax[0][r], s_amax[1][r]),
+                                    __builtin_fmaxf(s_amax[2][r], s_amax[3][r]));
+    const float s = a > 0.0f ? a / kE4M3Max : 1.0f;
+    const float rs = 1.0f / s;  // codes of v * (1/s): within 1 ulp of v / s
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = pos0 + tt * 16 + r16;
-    if (!tok_ok[tt]) continue;
+    for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-    for (int f = 0; f < NT; ++f) {
-      const int i = fbase + f * 16 + kq * 4;
-      const uint32_t lo = enc2(hv[f][tt][0] / sc[tt], hv[f][tt][1] / sc[tt]);
-      const uint32_t hi = enc2(hv[f][tt][2] / sc[tt], hv[f][tt][3] / sc[tt]);
-      *(uint32_t*)(hq + (size_t)pos * I + i) = lo | (hi << 16);
-    }
-    if (wave == 0 && kq == 0) hs[pos] = sc[tt];
+      for (int f = 0; f < G; ++f) {
+        const int i = ps * 128 + wave * (16 * G) + f * 16 + kq * 4;
+        const float* v = hkeep[ps][f][tt];
+        const uint32_t lo = enc2(v[0] * rs, v[1] * rs);
+        const uint32_t hi = enc2(v[2] * rs, v[3] * rs);
+        *(uint32_t*)(hq + (size_t)pos * I + i) = lo | (hi << 16);
+      }
+    if (wave == 0 && kq == 0) hs[pos] = s;
   }
 }
 
 // ---------------------------------------------------------------- GEMM2
 
-// grid.x: (expert, 32-pair tile), grid.y: H / (64*NF). A = h codes (pairs as rows), B = w2
-// rows; each of the 4 waves covers NF 16-feature MFMA tiles.
-// D[pair 4*kq + q][feature r16]: a wave's 16 lanes of one K quarter hold 16 consecutive
-// features of one pair, so its atomics touch 64 contiguous bytes per pair row.
-template <int NF>
-__global__ __launch_bounds__(256) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
-                                                         BankArg w2, Plan plan, int E, int H, int I, int k,
-                                                         int nblocks, float* __restrict__ acc_out) {
-  constexpr int kFeat = 4 * 16 * NF;  // output features per workgroup
+// One workgroup per (expert, 64-pair tile), 4 waves. The tile's h codes (64 x I) are copied
+// to LDS once: A = h (pairs as rows). B = w2 rows (features). The H outputs go in chunks of
+// 256; wave w owns features 64w .. 64w+64 of each chunk (FT = 4 MFMA tiles; a last chunk
+// of 128 has work for waves 0 and 1 only), so lane (r16, kq) of a result holds pairs
+// 4kq..4kq+3 of feature r16. Each wave streams its own w2 rows, (chunk, K block) after
+// (chunk, K block), through a private 3-deep LDS ring and so never waits for the others.
+// Each pair's y row = s_h * W2 h is written once, in float; the combine kernel applies the
+// router weights.
+template <int KB>  // I / 128
+__global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
+                                                            BankArg w2, Plan plan, int E, int H, int I, int k,
+                                                            int nblocks, float* __restrict__ y) {
+  constexpr int FT = 4;
+  constexpr int NCH = 4 * FT * 16;
+  constexpr int WB = 64 * kRowB;  // one wave's w2 rows of a stage
+  constexpr int HB = kTM * kRowB; // the h tile's rows of one K block
+  __shared__ __align__(16) uint8_t sH[KB * HB];
+  __shared__ __align__(16) uint8_t ring[4 * kStages * WB];
+  __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
+  (void)k;
+
   const int tile = xcd_tile(blockIdx.x, nblocks);
   if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
   const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM;
   const int pos_end = plan.offsets[e + 1];
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int nvalid = pos_end - pos0 < kTM ? pos_end - pos0 : kTM;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int r16 = lane & 15, kq = lane >> 4;
-  const int n_base = blockIdx.y * kFeat + wave * (kFeat / 4);
   const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
-  const int64_t sb = (int64_t)e * w2.sexp;
+  const int lr = lane >> 3, lc = lane & 7;
 
-  bool ok[2];
-  const uint8_t* arow[2];
+  // h tile: 8 * KB instructions of 8 rows x 128 bytes, 2 * KB per wave (rows past the
+  // expert's pairs copy the tile's first row; their results are never stored)
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int pos = pos0 + tt * 16 + r16;
-    ok[tt] = pos < pos_end;
-    arow[tt] = hq + (size_t)(ok[tt] ? pos : pos0) * I;
+  for (int i = 0; i < 2 * KB; ++i) {
+    const int q = wave * 2 * KB + i;
+    const int kb = q >> 3, r = (q & 7) * 8 + lr;
+    const int rr = r < nvalid ? r : 0;
+    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), sH + kb * HB + (q & 7) * 1024);
   }
-  f32x4 acc[2][NF];
+  // chunks holding features of this wave: those with c * NCH + 64 * wave < H (H is a
+  // multiple of 128, so a wave's 64 features are all in range or all out)
+  const int nch = (H - wave * 64 + NCH - 1) / NCH;
+  const int nst = nch * KB;
+  // w2 instruction i covers rows 8i .. 8i+7 of the wave's 64; chunk c adds c * NCH rows
+  uint32_t woff[8];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[tt][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int nkb = I / 128;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int kofs = kb * 128 + kq * 32;
-    i32x8 a[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) a[tt] = ok[tt] ? ld32(arow[tt] + kofs) : zero8();
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int n = n_base + f * 16;
-      const i32x8 b = ld32(wb + (size_t)(n + r16) * I + kofs);
-      const float s = load_scale(w2.scales, w2.scale_bf16, sb + (int64_t)(n / kScaleBlock) * w2.srow + kb);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 p = mfma_fp8(a[tt], b);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][f][q] = __builtin_fmaf(s, p[q], acc[tt][f][q]);
-      }
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int b = i * 8 + lr;
+    woff[i] = (uint32_t)(wave * 64 + b) * (uint32_t)I + (uint32_t)((lc ^ sw(b)) << 4);
   }
-  // epilogue: pair rows 4*kq + q of each 16-tile
+  uint8_t* myring = ring + wave * kStages * WB;
+  auto issue = [&](int st) {
+    const int c = st / KB, kb = st - c * KB;
+    const uint8_t* src = wb + (size_t)c * NCH * I + kb * 128;
+    uint8_t* slot = myring + (st % kStages) * WB;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + i * 1024);
+  };
+  if (nst > 0) issue(0);
+  if (nst > 1) issue(1);
+  stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
+  float hsc[4][4];
+  int prow[4][4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int pos = pos0 + tt * 16 + kq * 4 + q;
-      if (pos >= pos_end) continue;
-      const int p = plan.sorted[pos];
-      const int t = p / k;
-      const float mult = hs[pos] * plan.w[p];
-      float* orow = acc_out + (size_t)t * H;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) unsafeAtomicAdd(orow + n_base + f * 16 + r16, acc[tt][f][q] * mult);
+      const int pos = pos0 + pt * 16 + kq * 4 + q;
+      const bool ok = pos < pos_end;
+      hsc[pt][q] = ok ? hs[pos] : 0.0f;
+      prow[pt][q] = ok ? plan.sorted[pos] : -1;
     }
+  // everyone's h rows (and the scales) are in
+  wait_vm<0>();
+  __syncthreads();
+
+  f32x4 acc[FT][4];
+  for (int st = 0; st < nst; ++st) {
+    const int c = st / KB, kb = st - c * KB;
+    // the previous chunk's y stores are outstanding at a chunk start, and stores and
+    // loads may complete out of order: drain everything there
+    if (st + 1 < nst && kb != 0) wait_vm<8>();
+    else wait_vm<0>();
+    if (st + 2 < nst) issue(st + 2);
+    if (kb == 0) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const uint8_t* slot = myring + (st % kStages) * WB;
+    const uint8_t* hs_ = sH + kb * HB;
+    i32x8 a[4], bw[FT];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) a[pt] = lds_operand(hs_, pt * 16 + r16, kq);
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
+    const int n0 = c * NCH + wave * 64;
+    // features n0 .. n0 + 63 share one 128-row scale block
+    const float sc = s_sc[(n0 / kScaleBlock) * KB + kb];
+    f32x4 pp = mfma_fp8(a[0], bw[0]);
+#pragma unroll
+    for (int j = 0; j < FT * 4; ++j) {
+      const int ft = j / 4, pt = j % 4;
+      f32x4 nx;
+      if (j + 1 < FT * 4) nx = mfma_fp8(a[(j + 1) % 4], bw[(j + 1) / 4]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
+      if (j + 1 < FT * 4) pp = nx;
+    }
+    if (kb == KB - 1) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (prow[pt][q] < 0) continue;
+          float* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = acc[ft][pt][q] * hsc[pt][q];
+        }
+    }
+  }
 }
 
-__global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
-}
-
-__global__ void finalize_kernel(const float* __restrict__ acc, size_t n, void* __restrict__ out, int out_bf16) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  if (out_bf16) ((uint16_t*)out)[i] = f32_to_bf16(acc[i]);
-  else ((float*)out)[i] = acc[i];
-}
-
-template <int NT>
+template <int NP>
 hipError_t g1m(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int nblocks, int H,
                int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
-  hipLaunchKernelGGL((gemm1_mfma_kernel<NT>), dim3(nblocks), dim3(256), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
+  hipLaunchKernelGGL((gemm1_mfma_kernel<NP>), dim3(nblocks), dim3(256), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
                      hq, hs);
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
+               int I, int k, float* y, hipStream_t s) {
+  hipLaunchKernelGGL((gemm2_mfma_kernel<KB>), dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, k, nblocks,
+                     y);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Upper bound on the tiles of any routing (sum over experts of ceil(count/32) <= P/32 + E),
+// Upper bound on the tiles of any routing (sum over experts of ceil(count/64) <= P/64 + E),
 // rounded up to a multiple of 8 so that xcd_tile maps the grid onto [0, bound) one to one.
 size_t mfma_tiles_bound(int P, int E) {
   const size_t b = (size_t)(P + kTM - 1) / kTM + (size_t)E;
   return (b + 7) / 8 * 8;
+}
+
+bool mfma_shape_ok(int H, int I) {
+  return H % 128 == 0 && H > 0 && H <= kMaxH && I % 128 == 0 && I >= 128 && I <= kMaxI;
 }
 
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
@@ -338,42 +489,26 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t
 
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int P,
                              int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
+  if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E);
-  switch (I / 64) {
+  switch (I / 128) {
+    case 1: return g1m<1>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
     case 2: return g1m<2>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    case 4: return g1m<4>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    case 6: return g1m<6>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    case 8: return g1m<8>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    default: return hipErrorInvalidValue;
+    case 3: return g1m<3>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
+    default: return g1m<4>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
   }
 }
 
-template <int NF>
-static hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks,
-                      int H, int I, int k, float* acc, hipStream_t s) {
-  dim3 grid(nblocks, H / (64 * NF));
-  hipLaunchKernelGGL((gemm2_mfma_kernel<NF>), grid, dim3(256), 0, s, hq, hs, w2, plan, E, H, I, k, nblocks, acc);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
-                             int H, int I, int k, float* acc, hipStream_t s) {
+                             int H, int I, int k, float* y, hipStream_t s) {
+  if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E);
-  if (H % 512 == 0) return g2m<8>(hq, hs, w2, plan, E, nblocks, H, I, k, acc, s);
-  if (H % 256 == 0) return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, k, acc, s);
-  return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, k, acc, s);
-}
-
-hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(const float* acc, size_t n, void* out, int out_bf16, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, acc, n, out, out_bf16);
-  return hipGetLastError();
+  switch (I / 128) {
+    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
+    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
+    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
+    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
+  }
 }
 
 }  // namespace moe

@@ -338,16 +338,27 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
   }
 }
 
+// Four consecutive outputs per thread (H is a multiple of 128), slots summed in order.
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                            int T, int H, int k, void* __restrict__ out,
                                                            int out_bf16) {
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t idx = ((size_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (idx >= (size_t)T * H) return;
   const size_t t = idx / H, n = idx % H;
-  float s = 0.0f;
-  for (int j = 0; j < k; ++j) s = __builtin_fmaf(w[t * k + j], y[(t * k + j) * H + n], s);
-  if (out_bf16) ((uint16_t*)out)[idx] = f32_to_bf16(s);
-  else ((float*)out)[idx] = s;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const f32x4 v = *(const f32x4*)(y + (t * k + j) * H + n);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = __builtin_fmaf(wj, v[q], s[q]);
+  }
+  if (out_bf16) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
+    *(uint2*)((uint16_t*)out + idx) = make_uint2(lo, hi);
+  } else {
+    *(f32x4*)((float*)out + idx) = s;
+  }
 }
 
 template <int LPR, int MCH, int RP, int PER>
@@ -458,7 +469,7 @@ hipError_t launch_gemm2_gather(const float* h, const BankArg& w2, const int32_t*
 
 hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, void* out, int out_bf16,
                           hipStream_t s) {
-  const size_t n = (size_t)T * H;
+  const size_t n = (size_t)T * H / 4;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, y, w,
                      T, H, k, out, out_bf16);
   return hipGetLastError();

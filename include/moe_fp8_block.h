@@ -151,15 +151,17 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  *   logits  [T, E] float.
  *   w13     bank with N = 2I, K = H (gate rows 0..I-1, up rows I..2I-1).
  *   w2      bank with N = H, K = I.
- *   out     [T, H], out_dtype float or bf16 (round to nearest even from float).
+ *   out     [T, H], out_dtype float or bf16 (round to nearest even from float), 16-byte
+ *           aligned.
  *   ids_out [T, top_k] int32 and weights_out [T, top_k] float: the routing, or NULL.
  *   opts    host, NULL = defaults; info host, NULL = not reported.
  * H and I must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise). Every pointer the
  * chosen path reads must be non-NULL. T = 0 is a no-op (info still filled).
- * The W8A16 paths (GATHER, STREAM) decode weights exactly and accumulate in float; they
- * are deterministic. MFMA quantises x per token and h per (token, slot) row to e4m3 with
- * scale amax/448 (float division, 1 for a zero row; codes round to nearest even and
- * saturate at 448) and accumulates with float atomics, so its last bits may vary.
+ * The W8A16 paths (GATHER, STREAM) decode weights exactly and accumulate in float. MFMA
+ * quantises x per token and h per (token, slot) row to e4m3 with scale amax/448 (float
+ * division, 1 for a zero row; codes round to nearest even and saturate at 448) and
+ * multiplies on the fp8 matrix cores. Every path writes each (token, slot) result once
+ * and sums a token's slots in slot order, so all of them are deterministic.
  */
 int moe_fp8_block_forward(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
                           const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
@@ -171,11 +173,9 @@ typedef enum {
   MOE_K_ROUTE = 1,    /* top-k and weights */
   MOE_K_SORT = 2,     /* token-to-expert sort (one or three kernels) */
   MOE_K_QUANT = 3,    /* per-token e4m3 activation quantisation (MFMA path) */
-  MOE_K_ZERO = 4,     /* clears the float accumulator (MFMA path) */
   MOE_K_GEMM1 = 5,    /* gate/up GEMM with silu(gate)*up */
-  MOE_K_GEMM2 = 6,    /* down GEMM (with the combine on GATHER and MFMA) */
-  MOE_K_COMBINE = 7,  /* router-weighted sum of the slots (STREAM path) */
-  MOE_K_FINALIZE = 8  /* float accumulator -> bf16 output (MFMA path) */
+  MOE_K_GEMM2 = 6,    /* down GEMM (with the combine on GATHER) */
+  MOE_K_COMBINE = 7   /* router-weighted sum of the slots (STREAM and MFMA paths) */
 } moe_kernel;
 
 /*

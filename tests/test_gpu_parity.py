@@ -245,7 +245,7 @@ def test_mfma_small_sizes_forced(decode_banks):
 
 # ------------------------------------------------------------------- properties
 
-@pytest.mark.parametrize("path", ["gather", "stream"])
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
 def test_bf16_is_rounded_fp32_and_deterministic(decode_banks, path):
     c = W.make_case("sweep", T=8, seed=12, device=DEV, banks=decode_banks)
     say("bf16 vs fp32", path)
