@@ -14,11 +14,22 @@ serve a routed expert from an earlier step. The steps are captured into one HIP 
 
 Also reported on the same JSON line:
   roofline      the dominant kernel's algorithmic bytes per launch over its mean duration,
-                timed with HIP events recorded around it on its own stream
-                (moe_fp8_block_forward_timed), against the 8 TB/s HBM peak;
+                timed with HIP events the library attaches to that kernel's dispatch on
+                its own stream (moe_fp8_block_forward_timed), against the 8 TB/s HBM peak;
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--workload decode|sweep|large|prefill] [--T T]
+
+Two helpers turn rocprofv3 counters into the HBM traffic the roofline reports:
+  python bench.py --copy-calibration
+      copies 1 GiB device to device three times: run it under rocprofv3 --pmc FETCH_SIZE
+      (then WRITE_SIZE) to learn how those counters scale for a transfer of known size;
+  python bench.py --traffic-record --kernel K --workload W --fetch-dir D1 --write-dir D2
+                  --copy-fetch-dir D3 --copy-write-dir D4
+      reads the four rocprofv3 output folders and writes profiles/traffic_K_W.json: the
+      dominant kernel's FETCH_SIZE + WRITE_SIZE per launch, each scaled by what the counter
+      read for the known copy, stamped with a digest of the kernel sources (the bench only
+      reports it while the sources are unchanged).
 """
 
 from __future__ import annotations
@@ -60,7 +71,80 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=64, help="steps timed per kernel with events")
+    ap.add_argument("--copy-calibration", action="store_true", help="copy 1 GiB three times and exit")
+    ap.add_argument("--traffic-record", action="store_true", help="write profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--kernel", default="gemm1")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
     return ap.parse_args()
+
+
+# kernel kinds of the library -> a substring of their symbol names
+KERNEL_SYMBOLS = {"route": "route_", "sort": "sort_", "quant": "quant_rows", "gemm1": "gemm1_", "gemm2": "gemm2_",
+                  "combine": "combine_kernel"}
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+
+
+def _counter_per_dispatch(folder: str, counter: str, name_has: str):
+    """Mean value of one rocprofv3 counter per dispatch of the kernels whose name contains
+    name_has, from the counter_collection CSVs under folder."""
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter and name_has in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} records for kernels matching {name_has!r} under {folder}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_record(args):
+    """HBM bytes per launch of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by the same counter's reading for a device copy of known size."""
+    copy_sym = "copyBuffer"
+    cf, _ = _counter_per_dispatch(args.copy_fetch_dir, "FETCH_SIZE", copy_sym)
+    cw, _ = _counter_per_dispatch(args.copy_write_dir, "WRITE_SIZE", copy_sym)
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    sym = KERNEL_SYMBOLS[args.kernel]
+    kf, nf = _counter_per_dispatch(args.fetch_dir, "FETCH_SIZE", sym)
+    kw, nw = _counter_per_dispatch(args.write_dir, "WRITE_SIZE", sym)
+    rec = {
+        "kernel": args.kernel,
+        "workload": args.workload,
+        "fetch_kib_per_launch": round(kf, 1),
+        "write_kib_per_launch": round(kw, 1),
+        "dispatches": [nf, nw],
+        "copy_fetch_kib": round(cf, 1),
+        "copy_write_kib": round(cw, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "bytes_per_launch": round(kf * 1024.0 * f_scale + kw * 1024.0 * w_scale),
+        "source_digest": source_digest(),
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.kernel}_{args.workload}.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
 
 
 class Hip:
@@ -116,6 +200,10 @@ def committed_traffic(kernel: str, workload: str):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.traffic_record:
+        return traffic_record(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the single-GPU hot path; runs on more than one GPU are not part of this "
@@ -204,9 +292,9 @@ def main():
     gbs = total_bytes / (ms * 1e-3) / 1e9
     tok_s = K * T / (ms * 1e-3)
 
-    # per-kernel durations: HIP events around every kernel, recorded by the library on the
-    # stream the kernels run on; a spin kernel first lets the host enqueue everything before
-    # the GPU reaches it, so no host gap falls inside a bracket
+    # per-kernel durations: HIP events the library attaches to each kernel's dispatch on the
+    # stream the kernels run on (start and end of that kernel's execution); a spin kernel
+    # first lets the host enqueue everything before the GPU reaches it
     hip = Hip()
     nk = info["kernels"]
     KS = min(args.kernel_steps, S)

@@ -185,8 +185,8 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-// Enqueues the kernels of one call in order, optionally bracketing kernel i with the
-// caller's events 2i and 2i+1 and naming it in kinds[i].
+// Enqueues the kernels of one call in order, optionally timing kernel i with the caller's
+// events 2i (start) and 2i+1 (end), attached to its dispatch, and naming it in kinds[i].
 struct Runner {
   hipStream_t s;
   void* const* ev;
@@ -197,12 +197,14 @@ struct Runner {
   template <class F>
   hipError_t run(int kind, F&& launch) {
     const bool timed = ev != nullptr && 2 * n + 1 < nev;
-    if (timed) {
-      hipError_t e = hipEventRecord((hipEvent_t)ev[2 * n], s);
-      if (e != hipSuccess) return e;
-    }
+    if (timed) moe::kernel_events() = moe::KernelEvents{(hipEvent_t)ev[2 * n], (hipEvent_t)ev[2 * n + 1]};
     hipError_t e = launch();
-    if (e == hipSuccess && timed) e = hipEventRecord((hipEvent_t)ev[2 * n + 1], s);
+    if (timed && moe::kernel_events().start != nullptr) {
+      // nothing was launched (an error path): leave the events at a zero-length interval
+      moe::kernel_events() = moe::KernelEvents{};
+      if (e == hipSuccess) e = hipEventRecord((hipEvent_t)ev[2 * n], s);
+      if (e == hipSuccess) e = hipEventRecord((hipEvent_t)ev[2 * n + 1], s);
+    }
     if (kinds != nullptr && n < nev / 2) kinds[n] = kind;
     ++n;
     return e;
@@ -299,6 +301,13 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
 }
 
 }  // extern "C"
+
+namespace moe {
+KernelEvents& kernel_events() {
+  thread_local KernelEvents ev;
+  return ev;
+}
+}  // namespace moe
 
 namespace {
 

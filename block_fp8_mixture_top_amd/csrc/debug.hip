@@ -23,13 +23,13 @@ __global__ void encode_e4m3_kernel(const float* __restrict__ x, uint8_t* __restr
 
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, out, n);
+  launch_kernel(decode_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, out, n);
   return hipGetLastError();
 }
 
 hipError_t launch_encode_e4m3(const float* x, uint8_t* codes, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(encode_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, codes, n);
+  launch_kernel(encode_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, codes, n);
   return hipGetLastError();
 }
 

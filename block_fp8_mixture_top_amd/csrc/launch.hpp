@@ -1,6 +1,7 @@
 // Host-side launchers of the kernels (internal to the library; not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,30 @@
 #define MAX_EXPERTS 1024
 
 namespace moe {
+
+// Events a timed forward attaches to the next kernel it enqueues: the runtime ties them to
+// that kernel's dispatch, so their elapsed time is the kernel's own execution time (no
+// queue or dispatch gap). Per host thread; cleared by the launch that uses them.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+KernelEvents& kernel_events();
+
+// Every kernel of the library is enqueued through here.
+template <typename... Params, typename... Args>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+  KernelEvents& ev = kernel_events();
+  if (ev.start != nullptr) {
+    const KernelEvents use = ev;
+    ev = KernelEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, use.start, use.stop, 0, static_cast<Params>(args)...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<Params>(args)...);
+  }
+}
 
 // Pair counts up to this sort in one workgroup; larger ones use the three-pass sort.
 constexpr int kSmallSortPairs = 4096;

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
 template <int NP>
 hipError_t g1m(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int nblocks, int H,
                int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
-  hipLaunchKernelGGL((gemm1_mfma_kernel<NP>), dim3(nblocks), dim3(256), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
+  launch_kernel((gemm1_mfma_kernel<NP>), dim3(nblocks), dim3(256), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
                      hq, hs);
   return hipGetLastError();
 }
@@ -462,7 +462,7 @@ hipError_t g1m(const uint8_t* xq, const float* xs, const BankArg& w13, const Pla
 template <int KB>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
                int I, int k, float* y, hipStream_t s) {
-  hipLaunchKernelGGL((gemm2_mfma_kernel<KB>), dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, k, nblocks,
+  launch_kernel((gemm2_mfma_kernel<KB>), dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, k, nblocks,
                      y);
   return hipGetLastError();
 }
@@ -483,7 +483,7 @@ bool mfma_shape_ok(int H, int I) {
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                   hipStream_t s) {
   const int blocks = (rows + 3) / 4;
-  hipLaunchKernelGGL(quant_rows_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, rows, cols, codes, scales);
+  launch_kernel(quant_rows_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, rows, cols, codes, scales);
   return hipGetLastError();
 }
 

@@ -252,7 +252,7 @@ size_t sort_scratch_bytes(int P, int E) {
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   const int waves_per_block = 4;
   const int blocks = (T + waves_per_block - 1) / waves_per_block;
-  MOE_TOPK_DISPATCH(E, hipLaunchKernelGGL((route_topk_kernel<PER>), dim3(blocks), dim3(waves_per_block * kWave), 0,
+  MOE_TOPK_DISPATCH(E, launch_kernel((route_topk_kernel<PER>), dim3(blocks), dim3(waves_per_block * kWave), 0,
                                           s, logits, T, E, k, ids, w));
   return hipGetLastError();
 }
@@ -264,7 +264,7 @@ hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int 
                               int slots, int tile_m, int32_t* tile_off, void* scratch, hipStream_t s) {
   const int P = T * k;
   if (P <= kSmallSortPairs) {
-    MOE_TOPK_DISPATCH(E, hipLaunchKernelGGL((route_plan_kernel<PER>), dim3(1), dim3(1024), 0, s, logits, T, E, k,
+    MOE_TOPK_DISPATCH(E, launch_kernel((route_plan_kernel<PER>), dim3(1), dim3(1024), 0, s, logits, T, E, k,
                                             ids, w, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off));
     return hipGetLastError();
   }
@@ -274,13 +274,13 @@ hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int 
     case 0:
       return launch_route_topk(logits, T, E, k, ids, w, s);
     case 1:
-      hipLaunchKernelGGL(sort_hist_kernel, dim3(nchunks), dim3(kWave), 0, s, ids, P, E, chunk);
+      launch_kernel(sort_hist_kernel, dim3(nchunks), dim3(kWave), 0, s, ids, P, E, chunk);
       break;
     case 2:
-      hipLaunchKernelGGL(sort_chunk_scan_kernel, dim3(E), dim3(256), 0, s, chunk, nchunks, E, counts);
+      launch_kernel(sort_chunk_scan_kernel, dim3(E), dim3(256), 0, s, chunk, nchunks, E, counts);
       break;
     default:
-      hipLaunchKernelGGL(sort_scatter_kernel, dim3(nchunks), dim3(kWave), 0, s, ids, P, E, chunk, counts, offsets,
+      launch_kernel(sort_scatter_kernel, dim3(nchunks), dim3(kWave), 0, s, ids, P, E, chunk, counts, offsets,
                          sorted, act, n_act, slots, tile_m, tile_off);
       break;
   }

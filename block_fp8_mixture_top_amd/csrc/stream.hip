@@ -365,7 +365,7 @@ template <int LPR, int MCH, int RP, int PER>
 hipError_t g1(const Gemm1Args& a, hipStream_t s) {
   const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
   dim3 grid((a.I + rows - 1) / rows, a.slots);
-  hipLaunchKernelGGL((gemm1_w8a16_kernel<LPR, MCH, RP, PER>), grid, dim3(kThreads), 0, s, a.hidden, a.logits, a.T,
+  launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER>), grid, dim3(kThreads), 0, s, a.hidden, a.logits, a.T,
                      a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
   return hipGetLastError();
 }
@@ -383,7 +383,7 @@ hipError_t g2e(const float* h, const BankArg& w, const Plan& p, int slots, int H
                hipStream_t s) {
   const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
   dim3 grid((H + rows - 1) / rows, slots);
-  hipLaunchKernelGGL((gemm2_expert_kernel<LPR, MCH, RP>), grid, dim3(kThreads), 0, s, h, w, p, H, I, y);
+  launch_kernel((gemm2_expert_kernel<LPR, MCH, RP>), grid, dim3(kThreads), 0, s, h, w, p, H, I, y);
   return hipGetLastError();
 }
 
@@ -444,7 +444,7 @@ template <int MC, int ROWS>
 static hipError_t g2g(const float* h, const BankArg& w2, const int32_t* ids, const float* w, int T, int H, int I,
                       int k, void* out, int out_bf16, hipStream_t s) {
   dim3 grid((H + ROWS - 1) / ROWS, T);
-  hipLaunchKernelGGL((gemm2_gather_kernel<MC, ROWS>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
+  launch_kernel((gemm2_gather_kernel<MC, ROWS>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
                      out_bf16);
   return hipGetLastError();
 }
@@ -470,7 +470,7 @@ hipError_t launch_gemm2_gather(const float* h, const BankArg& w2, const int32_t*
 hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, void* out, int out_bf16,
                           hipStream_t s) {
   const size_t n = (size_t)T * H / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, y, w,
+  launch_kernel(combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, y, w,
                      T, H, k, out, out_bf16);
   return hipGetLastError();
 }

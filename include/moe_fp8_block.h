@@ -179,14 +179,15 @@ typedef enum {
 } moe_kernel;
 
 /*
- * moe_fp8_block_forward with HIP events recorded around its kernels, so a caller can time
- * each kernel on the stream it runs on. events: n_events hipEvent_t (as void*) created by
- * the caller with timing enabled; events[2i] is recorded on `stream` just before kernel i
- * is enqueued and events[2i+1] just after, for every i < n_events/2 (later kernels run
- * unbracketed). kinds: host array of n_events/2 int32 or NULL; receives the moe_kernel of
- * each bracketed kernel and 0 past the last. info->kernels counts all kernels. Everything
- * else, errors included, is as moe_fp8_block_forward; MOE_ERR_ARG if n_events < 0 or
- * events is NULL with n_events > 0.
+ * moe_fp8_block_forward with each kernel timed by the caller's HIP events. events: n_events
+ * hipEvent_t (as void*) created by the caller with timing enabled. For every i <
+ * n_events/2, kernel i is enqueued with events[2i] and events[2i+1] attached to its own
+ * dispatch (hipExtLaunchKernel), so hipEventElapsedTime(events[2i], events[2i+1]) is that
+ * kernel's execution time on `stream`, without queue or dispatch gaps; later kernels run
+ * untimed. kinds: host array of n_events/2 int32 or NULL; receives the moe_kernel of each
+ * timed kernel and 0 past the last. info->kernels counts all kernels. Everything else,
+ * errors included, is as moe_fp8_block_forward; MOE_ERR_ARG if n_events < 0 or events is
+ * NULL with n_events > 0.
  */
 int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
                                 const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
