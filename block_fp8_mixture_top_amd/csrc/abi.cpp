@@ -114,7 +114,7 @@ struct Carve {
 // Workspace layout; offsets into the caller's buffer.
 struct Layout {
   size_t ids, w, counts, offsets, sorted, act, n_act, tile_off, scratch;
-  size_t h, y, xq, xs, hq, hs;
+  size_t h, y, xq, xs;
   size_t total;
 };
 
@@ -132,13 +132,11 @@ Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
   L.n_act = c.take(4);
   L.tile_off = c.take((size_t)(E + 1) * 4);
   L.scratch = c.take(moe::sort_scratch_bytes((int)P, E));
-  if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) L.h = c.take(P * (size_t)I * 4);
+  L.h = c.take(P * (size_t)I * 4);  // h in float, [pair or sorted position, I]
   if (path == MOE_PATH_STREAM || path == MOE_PATH_MFMA) L.y = c.take(P * (size_t)H * 4);
   if (path == MOE_PATH_MFMA) {
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
-    L.hq = c.take(P * (size_t)I);
-    L.hs = c.take(P * 4);
   }
   L.total = c.off;
   return L;
@@ -384,13 +382,12 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   } else {
     uint8_t* xq = at<uint8_t>(workspace, L.xq);
     float* xs = at<float>(workspace, L.xs);
-    uint8_t* hq = at<uint8_t>(workspace, L.hq);
-    float* hs = at<float>(workspace, L.hs);
+    float* hf = at<float>(workspace, L.h);
     float* y = at<float>(workspace, L.y);
     RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
-    RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hq, hs, s),
+    RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s),
         "gemm1 mfma launch");
-    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, top_k, y, s), "gemm2 mfma launch");
+    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hf, b2, plan, E, (int)P, H, I, y, s), "gemm2 mfma launch");
     RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
   }
   if (info) info->kernels = R.n;

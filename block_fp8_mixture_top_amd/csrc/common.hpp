@@ -13,6 +13,7 @@ constexpr float kE4M3Max = 448.0f;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two e4m3 codes (bytes 0,1 when HI is false, bytes 2,3 when true) of a 32-bit word to
 // float with gfx950's conversion instruction, which reads OCP e4m3fn (bias 7). The decode
@@ -64,11 +65,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// A block scale as float.
-__device__ __forceinline__ float load_scale(const void* base, int is_bf16, int64_t idx) {
-  if (is_bf16) return bf16_to_f32(((const uint16_t*)base)[idx]);
-  return ((const float*)base)[idx];
+// A block scale as float, from a bf16 or a float table. Written without a branch (two 16-bit
+// reads: a float's high and low halves, or the bf16 value twice) so that the wait for the
+// value can stay at its first use; a load inside a branch is waited for at once, together
+// with every load issued before it.
+struct ScaleBits {
+  uint32_t hi, lo;
+};
+
+__device__ __forceinline__ ScaleBits load_scale_bits(const void* base, int is_bf16, int64_t idx) {
+  const uint16_t* p = (const uint16_t*)base + (is_bf16 ? idx : 2 * idx);
+  return ScaleBits{p[is_bf16 ? 0 : 1], p[0]};
 }
+
+__device__ __forceinline__ float scale_value(const ScaleBits& b, int is_bf16) {
+  return __uint_as_float((b.hi << 16) | (is_bf16 ? 0u : b.lo));
+}
+
+__device__ __forceinline__ float load_scale(const void* base, int is_bf16, int64_t idx) {
+  return scale_value(load_scale_bits(base, is_bf16, idx), is_bf16);
+}
+
+// Waits for a value loaded earlier at this point of the program, not sooner.
+__device__ __forceinline__ void settle(ScaleBits& b) { asm volatile("" : "+v"(b.hi), "+v"(b.lo)); }
 
 // ---- wave64 reductions on DPP (row shifts within 16-lane rows, then row broadcasts 15 and
 // 31), which stay in the VALU instead of going through LDS like a shuffle. The result is

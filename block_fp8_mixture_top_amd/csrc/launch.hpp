@@ -104,16 +104,17 @@ hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, v
 // W8A8 path.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                   hipStream_t s);
-constexpr int kMfmaTileM = 64;  // sorted pairs per MFMA tile
+constexpr int kMfmaTileM = 128;  // sorted pairs per MFMA tile
 size_t mfma_tiles_bound(int P, int E);
-// Shapes the MFMA kernels are built for: H a multiple of 128, I in {128, 256, 384, 512}.
+// Shapes the MFMA kernels are built for: H a multiple of 128 up to 8192, I in {128, 256, 384, 512}.
 bool mfma_shape_ok(int H, int I);
-// hq[p, I] e4m3 codes and hs[p] scales of h for every sorted pair position p.
+// hf[p, I] = silu(gate) * up in float for every sorted pair position p.
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
-                             int P, int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s);
-// y[pair, H] = s_h * W2 h for every pair (float, no atomics; the combine applies the weights).
-hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E,
-                             int P, int H, int I, int k, float* y, hipStream_t s);
+                             int P, int H, int I, int k, float* hf, hipStream_t s);
+// y[pair, H] = s_h * W2 h for every pair, h quantised per pair row (float, no atomics; the
+// combine applies the weights).
+hipError_t launch_gemm2_mfma(const float* hf, const BankArg& w2, const Plan& plan, int E, int P, int H, int I,
+                             float* y, hipStream_t s);
 
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);

@@ -13,12 +13,12 @@
 // block for lanes of K quarter kq), so whatever order the unit walks K in, matching A and
 // B bytes meet.
 //
-// Both GEMMs work on tiles of 64 sorted (token, slot) pairs of one expert. Every operand
+// Both GEMMs work on tiles of 128 sorted (token, slot) pairs of one expert. Every operand
 // goes global -> LDS with direct loads of 8 rows x 128 contiguous bytes per instruction,
-// through LDS rings a few K blocks ahead of the multiply. GEMM1 covers all 2I features of its
-// tile, so its epilogue has whole h rows: silu(gate)*up, row amax, scale and e4m3 codes are
-// produced without writing h in float. GEMM2 writes each pair's y row in float once; the
-// combine kernel sums the slots of a token in slot order with the router weights.
+// through LDS rings a few K blocks ahead of the multiply. GEMM1 writes h = silu(gate)*up in
+// float; GEMM2 reads each h row once, takes its amax, quantises it into LDS and multiplies.
+// GEMM2 writes each pair's y row in float once; the combine kernel sums the slots of a
+// token in slot order with the router weights.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,9 +30,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNeutralScale = 127;  // E8M0 2^0
 
-__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
-  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, kNeutralScale, 0, kNeutralScale);
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kNeutralScale, 0, kNeutralScale);
 }
 
 // ---------------------------------------------------------------- per-row quantisation
@@ -103,16 +102,17 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
 // the matrix cores, which is orders of magnitude larger.
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-constexpr int kTM = kMfmaTileM;  // pairs per tile: four 16-row MFMA tiles
+constexpr int kTM = kMfmaTileM;  // pairs per tile
 constexpr int kMaxH = 8192;      // bounds the block-scale slabs staged in LDS
-constexpr int kMaxI = 512;       // GEMM1 keeps 64 x I h values in registers
+constexpr int kMaxI = 512;       // GEMM2 keeps a half tile of h codes (64 x I) in LDS
 constexpr int kStages = 3;       // depth of the LDS rings
 constexpr int kRowB = 128;       // bytes of one row in one 128-wide K block
 
 // LDS rows hold one 128-byte K block; 16-byte chunk c of row r sits at chunk position
-// c ^ sw(r), so the 16 consecutive rows one operand read touches (same chunk) fall on
-// distinct banks whether the LDS serves 128 or 256 bytes a clock.
-__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 3)) & 7; }
+// c ^ (r & 7). Measured on gfx950 (SQ_LDS_BANK_CONFLICT), operand reads of 16 consecutive
+// rows at one chunk are conflict-free with this swizzle, while c ^ ((r ^ (r >> 3)) & 7)
+// costs four conflict cycles per read and no swizzle twelve.
+__device__ __forceinline__ int sw(int r) { return r & 7; }
 
 // One direct global->LDS load: lane j copies 16 bytes from its own address g to
 // lds + 16 j (lds wave-uniform). Issued as 8 rows x 128 contiguous bytes per instruction
@@ -161,216 +161,257 @@ __device__ __forceinline__ void stage_scales(float* s, const BankArg& b, int64_t
     s[q] = load_scale(b.scales, b.scale_bf16, sb + (int64_t)(q / cols) * b.srow + q % cols);
 }
 
+// Block scales as accumulator rescalings. A sum over K blocks sum_kb s_kb * P_kb is kept in
+// units of the latest block's scale: before block kb's products are accumulated in place by
+// the MFMA, the accumulator is multiplied by s_prev / s_kb, and the final sum is the
+// accumulator times the last scale. Real arithmetic gives the same value; float adds one
+// rounding of the ratio per block (2^-24 relative), far below the MFMA's own accumulation
+// error, and the MFMA results never wait for a VALU multiply. ratio[kb] is 0 for a zero scale
+// (that block contributes nothing and is skipped), 1 where the scale does not change.
+// One thread per block kb of a sequence: s_prev is the latest nonzero scale before kb, found
+// by looking back (one step unless scales are zero); the thread of the final block also
+// writes the last nonzero scale (0 if there is none).
+__device__ __forceinline__ void scale_ratio(const float* sc, int n, int kb, float* ratio, float* last) {
+  const float v = sc[kb];
+  float prev = 0.0f;
+  for (int j = kb - 1; j >= 0 && prev == 0.0f; --j) prev = sc[j];
+  ratio[kb] = v == 0.0f ? 0.0f : (prev == 0.0f ? 1.0f : prev / v);
+  if (kb == n - 1) *last = v != 0.0f ? v : prev;
+}
+
 // ---------------------------------------------------------------- GEMM1
 
-// One workgroup per (expert, 64-pair tile), 4 waves. NP = I/128 passes; in pass ps wave w
-// owns gate features ps*128 + 32w .. +32 (two 16-row MFMA tiles) and the matching up
-// features, for all 64 pairs. Every K block of every pass is a stage of a 3-deep LDS ring:
-// each wave copies in the 64 weight rows it multiplies, and the four waves together copy
-// the tile's 64 token rows of x. One barrier per stage. A = weight rows (features),
-// B = token rows, so lane (r16, kq) of a 16x16 result holds features 4kq..4kq+3 of token r16.
-template <int NP>
-__global__ __launch_bounds__(256, 1) void gemm1_mfma_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+// One workgroup per (expert, 128-pair tile, 128-feature block fb of h), 8 waves: two per
+// SIMD, so that one wave's LDS reads and copies proceed under the other's MFMAs (a single
+// wave serialises them). Wave w multiplies gate features fb*128 + 32(w%4) .. +32 (two 16-row
+// MFMA tiles) and the matching up features by tokens 64(w/4) .. +64 of the tile. Every
+// 128-wide K block is a stage of a 3-deep LDS ring, filled by direct loads shared out over
+// the waves (weight rows of a feature quarter by the two waves that multiply them, the tile's
+// 128 token rows by all eight); one barrier per stage. The operands of the next stage are
+// read into registers while the current one is multiplied. A = weight rows (features),
+// B = token rows, so lane (r16, kq) of a 16x16 result holds features 4kq..4kq+3 of token
+// r16. h = silu(g)*u is written in float, [sorted pair, I]; GEMM2 quantises it per row.
+__global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                                                             BankArg w13, Plan plan, int E, int H, int I, int k,
-                                                            int nblocks, uint8_t* __restrict__ hq,
-                                                            float* __restrict__ hs) {
-  constexpr int G = 2;                   // gate tiles per wave per pass (and as many up tiles)
-  constexpr int NF = 2 * G;              // weight tiles per wave per pass
-  constexpr int WB = 64 * kRowB;         // one wave's weight rows of a stage
-  constexpr int XB = kTM * kRowB;        // the tile's x rows of a stage
-  constexpr int SB = 4 * WB + XB;        // one stage
-  constexpr int LPW = 8 + 2;             // direct loads per wave per stage
+                                                            int nblocks, float* __restrict__ hf) {
+  constexpr int TM = kTM;                 // pairs per tile
+  constexpr int NTT = 4;                  // token tiles per wave (64 tokens)
+  constexpr int NF = 4;                   // weight tiles per wave: 2 gate + 2 up
+  constexpr int QB = 64 * kRowB;          // one feature quarter's weight rows of a stage
+  constexpr int XB = TM * kRowB;          // the tile's x rows of a stage
+  constexpr int SB = 4 * QB + XB;         // one stage
+  constexpr int LPW = 4 + 2;              // direct loads per wave per stage
   __shared__ __align__(16) uint8_t ring[kStages * SB];
-  __shared__ float s_sc[(2 * kMaxI / 128) * (kMaxH / 128)];
-  __shared__ float s_amax[4][kTM];
-  __shared__ int s_tok[kTM];
+  __shared__ float s_sc[2 * (kMaxH / 128)];
+  __shared__ float s_rt[2 * (kMaxH / 128)];
+  __shared__ float s_last[2];
+  __shared__ int s_tok[TM];
 
-  const int tile = xcd_tile(blockIdx.x, nblocks);
+  const int nfb = I / 128;
+  const int L = xcd_tile(blockIdx.x, nblocks);  // consecutive L share an expert's rows and a tile's x
+  const int tile = L / nfb, fb = L - tile * nfb;
   if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
-  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM;
+  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * TM;
   const int pos_end = plan.offsets[e + 1];
-  const int nvalid = pos_end - pos0 < kTM ? pos_end - pos0 : kTM;
+  const int nvalid = pos_end - pos0 < TM ? pos_end - pos0 : TM;
+  const int tid = (int)threadIdx.x;
   const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int fq = wave & 3, th = wave >> 2;  // feature quarter, token half
   const int r16 = lane & 15, kq = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
   const int nkb = H / 128;
 
   // token of each tile row (rows past the expert's pairs repeat the first token; their
-  // results are never stored)
-  if ((int)threadIdx.x < kTM)
-    s_tok[threadIdx.x] = plan.sorted[pos0 + ((int)threadIdx.x < nvalid ? (int)threadIdx.x : 0)] / k;
-  stage_scales(s_sc, w13, (int64_t)e * w13.sexp, 2 * I / 128, nkb);
-  __syncthreads();
-  float xsc[4];  // x scale of token tt*16 + r16
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) xsc[tt] = xs[s_tok[tt * 16 + r16]];
-
-  // direct-load sources. Weight instruction i covers rows 8i .. 8i+7 of the wave's 64
-  // (rows 0..31 gate, 32..63 up); pass ps adds 128 rows and K block kb adds kb*128 bytes.
-  const int lr = lane >> 3, lc = lane & 7;
-  uint32_t woff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = i * 8 + lr;
-    const int row = (b < 32 ? 0 : I - 32) + wave * 32 + b;
-    woff[i] = (uint32_t)row * (uint32_t)H + (uint32_t)((lc ^ sw(b)) << 4);
+  // results are never stored) and the gate / up block scales of this feature block
+  if (tid < TM) s_tok[tid] = plan.sorted[pos0 + (tid < nvalid ? tid : 0)] / k;
+  if (tid < 2 * nkb) {
+    const int up = tid >= nkb;
+    const int kb = tid - up * nkb;
+    s_sc[tid] = load_scale(w13.scales, w13.scale_bf16, (int64_t)e * w13.sexp + (int64_t)(fb + up * nfb) * w13.srow + kb);
   }
-  // x instruction i covers tile rows 16w + 8i .. +7
+  __syncthreads();
+  if (tid < 2 * nkb) {
+    const int up = tid >= nkb;
+    scale_ratio(s_sc + up * nkb, nkb, tid - up * nkb, s_rt + up * nkb, s_last + up);
+  }
+  __syncthreads();
+
+  // direct-load sources. Quarter fq's 64 weight rows (0..31 gate, 32..63 up) are copied 8 rows
+  // at a time: this wave takes copies 4th .. 4th+3. x copies: this wave takes tile rows
+  // 16w .. 16w+15. K block kb adds kb*128 bytes.
+  uint32_t woff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = (th * 4 + j) * 8 + lr;
+    const int row = (b < 32 ? 0 : I - 32) + fb * 128 + fq * 32 + b;
+    woff[j] = (uint32_t)row * (uint32_t)H + (uint32_t)((lc ^ sw(b)) << 4);
+  }
   const uint8_t* xsrc[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wave * 16 + i * 8 + lr;
-    xsrc[i] = xq + (size_t)s_tok[r] * H + ((lc ^ sw(r)) << 4);
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * 16 + j * 8 + lr;
+    xsrc[j] = xq + (size_t)s_tok[r] * H + ((lc ^ sw(r)) << 4);
   }
-  const int total = NP * nkb;
-  auto issue = [&](int st) {
-    const int ps = st / nkb, kb = st - ps * nkb;
-    uint8_t* slot = ring + (st % kStages) * SB;
-    const uint8_t* src = wb + (size_t)ps * 128 * H + kb * 128;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + wave * WB + i * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) g2lds(xsrc[i] + kb * 128, slot + 4 * WB + (wave * 16 + i * 8) * kRowB);
+  auto copy = [&](int kb, int j) {  // this wave's copy j (0..5) of stage kb
+    uint8_t* slot = ring + (kb % kStages) * SB;
+    if (j < 4) g2lds(wb + kb * 128 + woff[j], slot + fq * QB + (th * 4 + j) * 1024);
+    else g2lds(xsrc[j - 4] + kb * 128, slot + 4 * QB + (wave * 16 + (j - 4) * 8) * kRowB);
   };
-  issue(0);
-  if (total > 1) issue(1);
+  float xsc[NTT];  // x scale of token 64th + tt*16 + r16
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) xsc[tt] = xs[s_tok[th * 64 + tt * 16 + r16]];
 
-  float hkeep[NP][G][4][4];
-  float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Operands of one K block in registers: this wave's token rows (B) and weight rows (A).
+  struct Ops {
+    i32x8 bx[NTT];
+    i32x8 wa[NF];
+  };
+  f32x4 acc[NF][NTT];
 #pragma unroll
-  for (int ps = 0; ps < NP; ++ps) {
-    f32x4 acc[NF][4];
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[f][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int st = ps * nkb + kb;
-      // this wave's loads of stage st are in; after the barrier everyone's are, and every
-      // wave is done with stage st - 1, whose slot the next issue refills
-      if (st + 1 < total) wait_vm<LPW>();
+    for (int tt = 0; tt < NTT; ++tt) acc[f][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Stage kb + 1 is read into registers while stage kb is multiplied. At step kb: this wave's
+  // copies of stage kb + 1 are in, the barrier makes everyone's visible and shows every wave
+  // has read stage kb into registers (its LDS reads waited for), so stage kb's slot is
+  // refilled with stage kb + 3. Copies, reads and MFMAs go in two interleaved groups.
+  auto step = [&](int kb, const Ops& cur, Ops& nxt) {
+    // the scale ratios first, so that the explicit LDS wait below covers them too
+    const float rg = s_rt[kb], ru = s_rt[nkb + kb];
+    if (kb + 1 < nkb) {
+      if (kb + 2 < nkb) wait_vm<LPW>();
       else wait_vm<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb are done
       bar();
-      if (st + 2 < total) issue(st + 2);
-      const uint8_t* slot = ring + (st % kStages) * SB;
-      const uint8_t* sw_ = slot + wave * WB;
-      const uint8_t* sx_ = slot + 4 * WB;
-      i32x8 bx[4], wa[NF];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) bx[tt] = lds_operand(sx_, tt * 16 + r16, kq);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) wa[f] = lds_operand(sw_, f * 16 + r16, kq);
-      // one scale per K block for the gate rows of this pass, one for the up rows
-      const float sg = s_sc[ps * nkb + kb];
-      const float su = s_sc[(ps + NP) * nkb + kb];
-      // software pipelined: MFMA j + 1 is issued before the scale FMAs of MFMA j
-      f32x4 pp = mfma_fp8(wa[0], bx[0]);
-#pragma unroll
-      for (int j = 0; j < NF * 4; ++j) {
-        const int f = j / 4, tt = j % 4;
-        f32x4 nx;
-        if (j + 1 < NF * 4) nx = mfma_fp8(wa[(j + 1) / 4], bx[(j + 1) % 4]);
-        const float sc = f < G ? sg : su;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[f][tt][q] = __builtin_fmaf(sc, pp[q], acc[f][tt][q]);
-        if (j + 1 < NF * 4) pp = nx;
-      }
     }
+    const bool refill = kb + 3 < nkb;
+    // the next stage's operands; on the last step this rereads a settled slot (unused), which
+    // keeps LDS reads out of branches so the compiler's waits stay exact
+    const uint8_t* rslot = ring + ((kb + 1) % kStages) * SB;
 #pragma unroll
-    for (int f = 0; f < G; ++f)
+    for (int g = 0; g < 2; ++g) {
+      if (refill) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = acc[f][tt][q] * xsc[tt];
-          const float u = acc[f + G][tt][q] * xsc[tt];
-          const float v = silu_fast(g) * u;
-          hkeep[ps][f][tt][q] = v;
-          am[tt] = __builtin_fmaxf(am[tt], __builtin_fabsf(v));
-        }
-  }
-  // row amax over the four K-quarter lane groups, then over the waves
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    am[tt] = __builtin_fmaxf(am[tt], __shfl_xor(am[tt], 16, kWave));
-    am[tt] = __builtin_fmaxf(am[tt], __shfl_xor(am[tt], 32, kWave));
-    if (kq == 0) s_amax[wave][tt * 16 + r16] = am[tt];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int r = tt * 16 + r16;
-    const int pos = pos0 + r;
-    if (pos >= pos_end) continue;
-    const float a = __builtin_fmaxf(__builtin_fmaxf(s_amax[0][r], s_amax[1][r]),
-                                    __builtin_fmaxf(s_amax[2][r], s_amax[3][r]));
-    const float s = a > 0.0f ? a / kE4M3Max : 1.0f;
-    const float rs = 1.0f / s;  // codes of v * (1/s): within 1 ulp of v / s
-#pragma unroll
-    for (int ps = 0; ps < NP; ++ps)
-#pragma unroll
-      for (int f = 0; f < G; ++f) {
-        const int i = ps * 128 + wave * (16 * G) + f * 16 + kq * 4;
-        const float* v = hkeep[ps][f][tt];
-        const uint32_t lo = enc2(v[0] * rs, v[1] * rs);
-        const uint32_t hi = enc2(v[2] * rs, v[3] * rs);
-        *(uint32_t*)(hq + (size_t)pos * I + i) = lo | (hi << 16);
+        for (int j = 3 * g; j < 3 * g + 3; ++j) copy(kb + 3, j);
       }
-    if (wave == 0 && kq == 0) hs[pos] = s;
+#pragma unroll
+      for (int t = 2 * g; t < 2 * g + 2; ++t) {
+        nxt.bx[t] = lds_operand(rslot + 4 * QB, th * 64 + t * 16 + r16, kq);
+        nxt.wa[t] = lds_operand(rslot + fq * QB, t * 16 + r16, kq);
+      }
+      // gate tiles in group 0, up tiles in group 1
+      const float r = g == 0 ? rg : ru;  // uniform
+      if (r != 0.0f) {                   // a zero block scale adds nothing
+#pragma unroll
+        for (int f = 2 * g; f < 2 * g + 2; ++f) {
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[f][tt][q] *= r;
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) acc[f][tt] = mfma_fp8(cur.wa[f], cur.bx[tt], acc[f][tt]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) copy(0, j);
+  if (nkb > 1) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) copy(1, j);
+  }
+  if (nkb > 2) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) copy(2, j);
+  }
+  if (nkb > 2) wait_vm<2 * LPW>();
+  else if (nkb > 1) wait_vm<LPW>();
+  else wait_vm<0>();
+  bar();
+  Ops o0, o1;
+  {
+    const uint8_t* rslot = ring;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o0.bx[t] = lds_operand(rslot + 4 * QB, th * 64 + t * 16 + r16, kq);
+      o0.wa[t] = lds_operand(rslot + fq * QB, t * 16 + r16, kq);
+    }
+  }
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, o0, o1);
+    if (kb + 1 < nkb) step(kb + 1, o1, o0);
+  }
+  // h of gate tile f (features fb*128 + 32fq + 16f + 4kq .. +3) for token 64th + 16tt + r16
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int pos = pos0 + th * 64 + tt * 16 + r16;
+    if (pos >= pos_end) continue;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      f32x4 h;
+      const float gs = s_last[0] * xsc[tt], us = s_last[1] * xsc[tt];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float g = acc[f][tt][q] * gs;
+        const float u = acc[f + 2][tt][q] * us;
+        h[q] = silu_fast(g) * u;
+      }
+      *(f32x4*)(hf + (size_t)pos * I + fb * 128 + fq * 32 + f * 16 + kq * 4) = h;
+    }
   }
 }
 
 // ---------------------------------------------------------------- GEMM2
 
-// One workgroup per (expert, 64-pair tile), 4 waves. The tile's h codes (64 x I) are copied
-// to LDS once: A = h (pairs as rows). B = w2 rows (features). The H outputs go in chunks of
-// 256; wave w owns features 64w .. 64w+64 of each chunk (FT = 4 MFMA tiles; a last chunk
-// of 128 has work for waves 0 and 1 only), so lane (r16, kq) of a result holds pairs
-// 4kq..4kq+3 of feature r16. Each wave streams its own w2 rows, (chunk, K block) after
-// (chunk, K block), through a private 3-deep LDS ring and so never waits for the others.
+// One workgroup per (expert, 128-pair tile, half of 64 pairs), 4 waves; the two halves of a
+// tile are consecutive workgroups of one XCD, so the second reads the expert's w2 from L2.
+// The half's float h rows are read once, quantised per (token, slot) row to e4m3 with
+// scale amax/448 (1 for a zero row) and placed in LDS: A = h codes (pairs as rows). B = w2
+// rows (features). The H outputs go in chunks of 256; wave w owns features 64w .. 64w+64 of
+// each chunk (FT = 4 MFMA tiles; a last chunk of 128 has work for waves 0 and 1 only), so
+// lane (r16, kq) of a result holds pairs 4kq..4kq+3 of feature r16. Each wave streams its
+// own w2 rows, (chunk, K block) after (chunk, K block), through a private 3-deep LDS ring.
 // Each pair's y row = s_h * W2 h is written once, in float; the combine kernel applies the
 // router weights.
 template <int KB>  // I / 128
-__global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
-                                                            BankArg w2, Plan plan, int E, int H, int I, int k,
-                                                            int nblocks, float* __restrict__ y) {
+__global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restrict__ hf, BankArg w2, Plan plan, int E,
+                                                            int H, int I, int nblocks, float* __restrict__ y) {
+  constexpr int HM = 64;           // pairs per half tile
   constexpr int FT = 4;
   constexpr int NCH = 4 * FT * 16;
-  constexpr int WB = 64 * kRowB;  // one wave's w2 rows of a stage
-  constexpr int HB = kTM * kRowB; // the h tile's rows of one K block
+  constexpr int WB = 64 * kRowB;   // one wave's w2 rows of a stage
+  constexpr int HB = HM * kRowB;   // the h codes of one K block
+  constexpr int HPT = KB * 128 / 4;  // h values per thread (4 threads per row)
   __shared__ __align__(16) uint8_t sH[KB * HB];
   __shared__ __align__(16) uint8_t ring[4 * kStages * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
-  (void)k;
+  __shared__ float s_rt[(kMaxH / 128) * (kMaxI / 128)];
+  __shared__ float s_last[kMaxH / 128];
+  __shared__ float s_hs[HM];
 
-  const int tile = xcd_tile(blockIdx.x, nblocks);
+  const int L = xcd_tile(blockIdx.x, nblocks);
+  const int tile = L >> 1, half = L & 1;
   if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
-  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM;
+  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM + half * HM;
   const int pos_end = plan.offsets[e + 1];
-  const int nvalid = pos_end - pos0 < kTM ? pos_end - pos0 : kTM;
+  if (pos0 >= pos_end) return;
+  const int tid = (int)threadIdx.x;
   const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r16 = lane & 15, kq = lane >> 4;
-  const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
   const int lr = lane >> 3, lc = lane & 7;
+  const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
 
-  // h tile: 8 * KB instructions of 8 rows x 128 bytes, 2 * KB per wave (rows past the
-  // expert's pairs copy the tile's first row; their results are never stored)
-#pragma unroll
-  for (int i = 0; i < 2 * KB; ++i) {
-    const int q = wave * 2 * KB + i;
-    const int kb = q >> 3, r = (q & 7) * 8 + lr;
-    const int rr = r < nvalid ? r : 0;
-    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), sH + kb * HB + (q & 7) * 1024);
-  }
   // chunks holding features of this wave: those with c * NCH + 64 * wave < H (H is a
   // multiple of 128, so a wave's 64 features are all in range or all out)
   const int nch = (H - wave * 64 + NCH - 1) / NCH;
   const int nst = nch * KB;
-  // w2 instruction i covers rows 8i .. 8i+7 of the wave's 64; chunk c adds c * NCH rows
+  // w2 copy i covers rows 8i .. 8i+7 of the wave's 64; chunk c adds c * NCH rows
   uint32_t woff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -385,85 +426,127 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + i * 1024);
   };
-  if (nst > 0) issue(0);
-  if (nst > 1) issue(1);
   stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
-  float hsc[4][4];
-  int prow[4][4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int pos = pos0 + pt * 16 + kq * 4 + q;
-      const bool ok = pos < pos_end;
-      hsc[pt][q] = ok ? hs[pos] : 0.0f;
-      prow[pt][q] = ok ? plan.sorted[pos] : -1;
-    }
-  // everyone's h rows (and the scales) are in
-  wait_vm<0>();
   __syncthreads();
-
-  f32x4 acc[FT][4];
-  for (int st = 0; st < nst; ++st) {
-    const int c = st / KB, kb = st - c * KB;
-    // the previous chunk's y stores are outstanding at a chunk start, and stores and
-    // loads may complete out of order: drain everything there
-    if (st + 1 < nst && kb != 0) wait_vm<8>();
-    else wait_vm<0>();
-    if (st + 2 < nst) issue(st + 2);
-    if (kb == 0) {
+  if (tid < (H / 128) * KB) {
+    const int nb = tid / KB;
+    scale_ratio(s_sc + nb * KB, KB, tid - nb * KB, s_rt + nb * KB, s_last + nb);
+  }
+  // (visible after the barrier that follows the h codes)
+  {
+    const int nvalid = pos_end - pos0 < HM ? pos_end - pos0 : HM;
+    if (nst > 0) issue(0);
+    if (nst > 1) issue(1);
+    // h rows: thread t takes row t/4, quarter t%4 (HPT contiguous values); the four
+    // threads of a row are adjacent lanes
+    {
+      const int r = tid >> 2, qd = tid & 3;
+      const bool ok = r < nvalid;
+      // every read unconditional (rows past the expert's pairs read its first row), so that
+      // they are all in flight before the first wait; those rows are then zeroed
+      const float* src = hf + (size_t)(pos0 + (ok ? r : 0)) * I + qd * HPT;
+      f32x4 v[HPT / 4];
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+      for (int j = 0; j < HPT / 4; ++j) v[j] = *(const f32x4*)(src + 4 * j);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const uint8_t* slot = myring + (st % kStages) * WB;
-    const uint8_t* hs_ = sH + kb * HB;
-    i32x8 a[4], bw[FT];
+      for (int j = 0; j < HPT / 4; ++j)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) a[pt] = lds_operand(hs_, pt * 16 + r16, kq);
+        for (int q = 0; q < 4; ++q) v[j][q] = ok ? v[j][q] : 0.0f;
+      float am = 0.0f;
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
-    const int n0 = c * NCH + wave * 64;
-    // features n0 .. n0 + 63 share one 128-row scale block
-    const float sc = s_sc[(n0 / kScaleBlock) * KB + kb];
-    f32x4 pp = mfma_fp8(a[0], bw[0]);
+      for (int j = 0; j < HPT / 4; ++j)
 #pragma unroll
-    for (int j = 0; j < FT * 4; ++j) {
-      const int ft = j / 4, pt = j % 4;
-      f32x4 nx;
-      if (j + 1 < FT * 4) nx = mfma_fp8(a[(j + 1) % 4], bw[(j + 1) / 4]);
+        for (int q = 0; q < 4; ++q) am = __builtin_fmaxf(am, __builtin_fabsf(v[j][q]));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 1, kWave));
+      am = __builtin_fmaxf(am, __shfl_xor(am, 2, kWave));
+      const float s = am > 0.0f ? am / kE4M3Max : 1.0f;
+      const float rs = 1.0f / s;  // codes of v * (1/s): within 1 ulp of v / s
+      if (qd == 0) s_hs[r] = s;
+      // 16 codes (one 16-byte chunk) at a time, placed by the swizzle of their K block
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
-      if (j + 1 < FT * 4) pp = nx;
-    }
-    if (kb == KB - 1) {
+      for (int j = 0; j < HPT / 16; ++j) {
+        uint32_t wd[4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (prow[pt][q] < 0) continue;
-          float* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = acc[ft][pt][q] * hsc[pt][q];
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 a = v[4 * j + m];
+          wd[m] = enc2(a[0] * rs, a[1] * rs) | (enc2(a[2] * rs, a[3] * rs) << 16);
         }
+        const int c = (qd * HPT) / 16 + j;  // chunk of the row
+        *(u32x4*)(sH + (c >> 3) * HB + r * kRowB + (((c & 7) ^ sw(r)) << 4)) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      }
+    }
+    __syncthreads();
+    float hsc[4][4];
+    int prow[4][4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = pt * 16 + kq * 4 + q;
+        const bool ok = r < nvalid;
+        hsc[pt][q] = s_hs[r];
+        prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
+      }
+
+    f32x4 acc[FT][4];
+    for (int st = 0; st < nst; ++st) {
+      const int c = st / KB, kb = st - c * KB;
+      // the previous chunk's y stores are outstanding at a chunk start, and stores and
+      // loads may complete out of order: drain everything there
+      if (st + 1 < nst && kb != 0) wait_vm<8>();
+      else wait_vm<0>();
+      if (st + 2 < nst) issue(st + 2);
+      if (kb == 0) {
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      const uint8_t* slot = myring + (st % kStages) * WB;
+      const uint8_t* hs_ = sH + kb * HB;
+      i32x8 a[4], bw[FT];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) a[pt] = lds_operand(hs_, pt * 16 + r16, kq);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
+      const int n0 = c * NCH + wave * 64;
+      // features n0 .. n0 + 63 share one 128-row scale block
+      const int nb = n0 / kScaleBlock;
+      const float r = s_rt[nb * KB + kb];  // uniform
+      if (r != 0.0f) {
+        if (r != 1.0f) {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[ft][pt][q] *= r;
+        }
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = mfma_fp8(a[pt], bw[ft], acc[ft][pt]);
+      }
+      if (kb == KB - 1) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (prow[pt][q] < 0) continue;
+            float* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
+            const float ys = s_last[nb] * hsc[pt][q];
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = acc[ft][pt][q] * ys;
+          }
+      }
     }
   }
 }
 
-template <int NP>
-hipError_t g1m(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int nblocks, int H,
-               int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
-  launch_kernel((gemm1_mfma_kernel<NP>), dim3(nblocks), dim3(256), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
-                     hq, hs);
-  return hipGetLastError();
-}
-
 template <int KB>
-hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
-               int I, int k, float* y, hipStream_t s) {
-  launch_kernel((gemm2_mfma_kernel<KB>), dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, k, nblocks,
-                     y);
+hipError_t g2m(const float* hf, const BankArg& w2, const Plan& plan, int E, int nblocks, int H, int I, float* y,
+               hipStream_t s) {
+  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hf, w2, plan, E, H, I, nblocks, y);
   return hipGetLastError();
 }
 
@@ -488,26 +571,22 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t
 }
 
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int P,
-                             int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
+                             int H, int I, int k, float* hf, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
-  const int nblocks = (int)mfma_tiles_bound(P, E);
-  switch (I / 128) {
-    case 1: return g1m<1>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    case 2: return g1m<2>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    case 3: return g1m<3>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-    default: return g1m<4>(xq, xs, w13, plan, E, nblocks, H, I, k, hq, hs, s);
-  }
+  const int nblocks = (int)mfma_tiles_bound(P, E) * (I / 128);
+  launch_kernel(gemm1_mfma_kernel, dim3(nblocks), dim3(512), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks, hf);
+  return hipGetLastError();
 }
 
-hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
-                             int H, int I, int k, float* y, hipStream_t s) {
+hipError_t launch_gemm2_mfma(const float* hf, const BankArg& w2, const Plan& plan, int E, int P, int H, int I,
+                             float* y, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
-  const int nblocks = (int)mfma_tiles_bound(P, E);
+  const int nblocks = (int)mfma_tiles_bound(P, E) * 2;
   switch (I / 128) {
-    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
-    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
-    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
-    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, k, y, s);
+    case 1: return g2m<1>(hf, w2, plan, E, nblocks, H, I, y, s);
+    case 2: return g2m<2>(hf, w2, plan, E, nblocks, H, I, y, s);
+    case 3: return g2m<3>(hf, w2, plan, E, nblocks, H, I, y, s);
+    default: return g2m<4>(hf, w2, plan, E, nblocks, H, I, y, s);
   }
 }
 

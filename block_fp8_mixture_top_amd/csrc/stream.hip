@@ -65,14 +65,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     if (T == 1) {
 #pragma unroll
       for (int m = 0; m < MCH; ++m) {
-        const int c = gl + LPR * m;
-        if (c < NC) {
-          x0[m] = ld16((const uint8_t*)hidden + (size_t)c * 32);
-          x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
-        } else {
-          x0[m] = u32x4{0, 0, 0, 0};
-          x1[m] = u32x4{0, 0, 0, 0};
-        }
+        const int c = min(gl + LPR * m, NC - 1);  // chunks past NC read the last one, unused
+        x0[m] = ld16((const uint8_t*)hidden + (size_t)c * 32);
+        x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
       }
       wave_topk_ids<PER>(logits, E, k, my_id, my_l);
       route_wave = wave == 0;
@@ -138,26 +133,38 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
   const int64_t sb = (int64_t)e * w13.sexp;
 
+  // The RP rows of a lane group lie in one 128-row scale block (i0 is a multiple of RP, which
+  // divides 128), so a chunk's gate and up scales are shared by them. Scales are read first
+  // and waited for only after every code read is issued.
   u32x4 cg[RP][MCH], cu[RP][MCH];
-  float sg[RP][MCH], su[RP][MCH];
+  ScaleBits bg[MCH], bu[MCH];
+  const int ib = (i0 < I ? i0 : I - 1) / kScaleBlock;
+#pragma unroll
+  for (int m = 0; m < MCH; ++m) {
+    const int c = gl + LPR * m;
+    const int cb = (c < NC ? c : NC - 1) / 8;
+    bg[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)ib * w13.srow + cb);
+    bu[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)(I / kScaleBlock + ib) * w13.srow + cb);
+  }
+  // Every read is unconditional (rows past I and chunks past NC read in-bounds neighbours whose
+  // results are dropped), so the compiler can count them exactly and wait only at first use.
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    const int i = i0 + r;
+    const int i = min(i0 + r, I - 1);
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
-      const int c = gl + LPR * m;
-      if (i < I && c < NC) {
-        cg[r][m] = ld16_stream(wb + (size_t)i * H + (size_t)c * 16);
-        cu[r][m] = ld16_stream(wb + (size_t)(I + i) * H + (size_t)c * 16);
-        sg[r][m] = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)(i / kScaleBlock) * w13.srow + c / 8);
-        su[r][m] = load_scale(w13.scales, w13.scale_bf16, sb + (int64_t)((I + i) / kScaleBlock) * w13.srow + c / 8);
-      } else {
-        cg[r][m] = u32x4{0, 0, 0, 0};
-        cu[r][m] = u32x4{0, 0, 0, 0};
-        sg[r][m] = 0.0f;
-        su[r][m] = 0.0f;
-      }
+      const int c = min(gl + LPR * m, NC - 1);
+      cg[r][m] = ld16_stream(wb + (size_t)i * H + (size_t)c * 16);
+      cu[r][m] = ld16_stream(wb + (size_t)(I + i) * H + (size_t)c * 16);
     }
+  }
+  float sg[MCH], su[MCH];
+#pragma unroll
+  for (int m = 0; m < MCH; ++m) {
+    settle(bg[m]);
+    settle(bu[m]);
+    sg[m] = scale_value(bg[m], w13.scale_bf16);
+    su[m] = scale_value(bu[m], w13.scale_bf16);
   }
   if constexpr (PER > 0) {
     // the router weights, while the weight codes are in flight
@@ -175,14 +182,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
 #pragma unroll
       for (int m = 0; m < MCH; ++m) {
-        const int c = gl + LPR * m;
-        if (c < NC) {
-          x0[m] = ld16(xb + (size_t)c * 32);
-          x1[m] = ld16(xb + (size_t)c * 32 + 16);
-        } else {
-          x0[m] = u32x4{0, 0, 0, 0};
-          x1[m] = u32x4{0, 0, 0, 0};
-        }
+        const int c = min(gl + LPR * m, NC - 1);
+        x0[m] = ld16(xb + (size_t)c * 32);
+        x1[m] = ld16(xb + (size_t)c * 32 + 16);
       }
     }
 #pragma unroll
@@ -190,8 +192,10 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       float g = 0.0f, u = 0.0f;
 #pragma unroll
       for (int m = 0; m < MCH; ++m) {
-        g = __builtin_fmaf(sg[r][m], dot16_bf16(cg[r][m], x0[m], x1[m]), g);
-        u = __builtin_fmaf(su[r][m], dot16_bf16(cu[r][m], x0[m], x1[m]), u);
+        if (gl + LPR * m < NC) {
+          g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], x0[m], x1[m]), g);
+          u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], x0[m], x1[m]), u);
+        }
       }
       g = group_sum<LPR>(g);
       u = group_sum<LPR>(u);
@@ -216,49 +220,65 @@ __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __r
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int CPR = I / 16;
   const int F = k * CPR;
-  float hv[MC][16];
-  const uint8_t* wp[MC];
-  float ws[MC];
+  // Thread chunk m: slot j, 16 h values c*16 .. c*16+15. Reads in dependency order, each
+  // batch issued before anything waits: the slot's expert id and router weight with h (h's
+  // address does not depend on the id), then the scales, then the codes; the scales are
+  // waited for only after every code read is issued. Chunks past F read slot 0, chunk 0 (in
+  // bounds) and are given weight 0.
+  f32x4 hq[MC][4];
+  int ev[MC];
+  float wv[MC];
 #pragma unroll
   for (int m = 0; m < MC; ++m) {
-    const int f = tid + kThreads * m;
-    if (f < F) {
-      const int j = f / CPR, c = f % CPR;
-      const int e = ids[(size_t)t * k + j];
-      const float* hp = h + ((size_t)t * k + j) * I + (size_t)c * 16;
+    const int f = tid + kThreads * m < F ? tid + kThreads * m : 0;
+    const int j = f / CPR, c = f % CPR;
+    ev[m] = ids[(size_t)t * k + j];
+    wv[m] = wts[(size_t)t * k + j];
+    const float* hp = h + ((size_t)t * k + j) * I + (size_t)c * 16;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *(const f32x4*)(hp + 4 * q);
-        hv[m][4 * q + 0] = v.x;
-        hv[m][4 * q + 1] = v.y;
-        hv[m][4 * q + 2] = v.z;
-        hv[m][4 * q + 3] = v.w;
-      }
-      wp[m] = w2.codes + (size_t)e * w2.expert_stride + (size_t)c * 16;
-      ws[m] = wts[(size_t)t * k + j] *
-              load_scale(w2.scales, w2.scale_bf16, (int64_t)e * w2.sexp + (int64_t)(n0 / kScaleBlock) * w2.srow + c / 8);
-    } else {
+    for (int q = 0; q < 4; ++q) hq[m][q] = *(const f32x4*)(hp + 4 * q);
+  }
+  ScaleBits sbits[MC];
+  const uint8_t* wp[MC];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) hv[m][q] = 0.0f;
-      wp[m] = nullptr;
-      ws[m] = 0.0f;
-    }
+  for (int m = 0; m < MC; ++m) {
+    const int f = tid + kThreads * m < F ? tid + kThreads * m : 0;
+    const int c = f % CPR;
+    sbits[m] = load_scale_bits(w2.scales, w2.scale_bf16,
+                               (int64_t)ev[m] * w2.sexp + (int64_t)(n0 / kScaleBlock) * w2.srow + c / 8);
+    wp[m] = w2.codes + (size_t)ev[m] * w2.expert_stride + (size_t)c * 16;
   }
   u32x4 cw[ROWS][MC];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    const int n = n0 + r;
+    const int n = n0 + r < H ? n0 + r : H - 1;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      if (wp[m] != nullptr && n < H) cw[r][m] = ld16_stream(wp[m] + (size_t)n * I);
-      else cw[r][m] = u32x4{0, 0, 0, 0};
+    for (int m = 0; m < MC; ++m) cw[r][m] = ld16_stream(wp[m] + (size_t)n * I);
+  }
+  float hv[MC][16];
+  float ws[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    settle(sbits[m]);
+    const bool live = tid + kThreads * m < F;
+    ws[m] = live ? wv[m] * scale_value(sbits[m], w2.scale_bf16) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hv[m][4 * q + 0] = live ? hq[m][q].x : 0.0f;
+      hv[m][4 * q + 1] = live ? hq[m][q].y : 0.0f;
+      hv[m][4 * q + 2] = live ? hq[m][q].z : 0.0f;
+      hv[m][4 * q + 3] = live ? hq[m][q].w : 0.0f;
     }
   }
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     float acc = 0.0f;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) acc = __builtin_fmaf(ws[m], dot16_f32(cw[r][m], hv[m]), acc);
+    for (int m = 0; m < MC; ++m) {
+      // a chunk past F multiplies zero codes (a NaN code times a zero weight would not vanish)
+      const u32x4 code = tid + kThreads * m < F ? cw[r][m] : u32x4{0, 0, 0, 0};
+      acc = __builtin_fmaf(ws[m], dot16_f32(code, hv[m]), acc);
+    }
     acc = wave_sum_dpp(acc);
     if (lane == 0) red[wave][r] = acc;
   }

@@ -20,12 +20,21 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
   const int lane = lane_id();
   uint32_t key[PER];
   int idx[PER];
+  float f[PER];
+  // All loads first, in bounds and outside any branch, so that they are in flight together
+  // (the empty asm keeps each one unconditional).
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + kWave * i;
-    float f = e < E ? row[e] : 0.0f;
-    f = f != f ? -__builtin_inff() : f;
-    key[i] = e < E ? order_key(f) : 0u;  // every real logit has a key > 0
+    f[i] = row[e < E ? e : E - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(f[i]));
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    const float v = f[i] != f[i] ? -__builtin_inff() : f[i];
+    key[i] = e < E ? order_key(v) : 0u;  // every real logit has a key > 0
     idx[i] = e;
   }
   // insertion sort, best first: larger key, then lower id (ids rise with i, so a strict
