@@ -310,22 +310,28 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
   const int NC = I / 16;
   const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
   const int64_t sb = (int64_t)e * w2.sexp;
+  // The RP rows share one 128-row scale block (n0 is a multiple of RP, which divides 128).
+  // Scales first, then every code read, all unconditional (out-of-range rows and chunks read
+  // in-bounds neighbours whose results are dropped), so no read waits inside a branch.
+  ScaleBits sbits[MCH];
+  const int nb = (n0 < H ? n0 : H - 1) / kScaleBlock;
+#pragma unroll
+  for (int m = 0; m < MCH; ++m) {
+    const int c = min(gl + LPR * m, NC - 1);
+    sbits[m] = load_scale_bits(w2.scales, w2.scale_bf16, sb + (int64_t)nb * w2.srow + c / 8);
+  }
   u32x4 cw[RP][MCH];
-  float sw[RP][MCH];
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    const int n = n0 + r;
+    const int n = min(n0 + r, H - 1);
 #pragma unroll
-    for (int m = 0; m < MCH; ++m) {
-      const int c = gl + LPR * m;
-      if (n < H && c < NC) {
-        cw[r][m] = ld16_stream(wb + (size_t)n * I + (size_t)c * 16);
-        sw[r][m] = load_scale(w2.scales, w2.scale_bf16, sb + (int64_t)(n / kScaleBlock) * w2.srow + c / 8);
-      } else {
-        cw[r][m] = u32x4{0, 0, 0, 0};
-        sw[r][m] = 0.0f;
-      }
-    }
+    for (int m = 0; m < MCH; ++m) cw[r][m] = ld16_stream(wb + (size_t)n * I + (size_t)min(gl + LPR * m, NC - 1) * 16);
+  }
+  float sw[MCH];
+#pragma unroll
+  for (int m = 0; m < MCH; ++m) {
+    settle(sbits[m]);
+    sw[m] = scale_value(sbits[m], w2.scale_bf16);
   }
   const int beg = plan.offsets[e];
   const int cnt = plan.counts[e];
@@ -335,11 +341,10 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
     float hv[MCH][16];
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
-      const int c = gl + LPR * m;
+      const int c = min(gl + LPR * m, NC - 1);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (c < NC) v = *(const f32x4*)(hp + (size_t)c * 16 + 4 * qq);
+        const f32x4 v = *(const f32x4*)(hp + (size_t)c * 16 + 4 * qq);
         hv[m][4 * qq + 0] = v.x;
         hv[m][4 * qq + 1] = v.y;
         hv[m][4 * qq + 2] = v.z;
@@ -350,7 +355,8 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
     for (int r = 0; r < RP; ++r) {
       float acc = 0.0f;
 #pragma unroll
-      for (int m = 0; m < MCH; ++m) acc = __builtin_fmaf(sw[r][m], dot16_f32(cw[r][m], hv[m]), acc);
+      for (int m = 0; m < MCH; ++m)
+        if (gl + LPR * m < NC) acc = __builtin_fmaf(sw[m], dot16_f32(cw[r][m], hv[m]), acc);
       acc = group_sum<LPR>(acc);
       const int n = n0 + r;
       if (gl == 0 && n < H) y[(size_t)p * H + n] = acc;
