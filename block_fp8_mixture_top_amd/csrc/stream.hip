@@ -422,7 +422,7 @@ hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s) {
   if (L.lpr == 64) {
     switch (L.mch) {
       case 1: return g1r<64, 1, 2>(a, s);
-      case 2: return g1r<64, 2, 2>(a, s);
+      case 2: return g1r<64, 2, 1>(a, s);
       case 3: return g1r<64, 3, 1>(a, s);
       case 4: return g1r<64, 4, 1>(a, s);
       case 5: return g1r<64, 5, 1>(a, s);
