@@ -39,7 +39,10 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // Workgroup (0, 0) writes the ids and weights for the down GEMM; the weights (double exp and
 // sum) are computed after the weight loads are issued, off the critical path.
 // PER == 0: the slot's expert and pairs come from the sorted plan in global memory.
-template <int LPR, int MCH, int RP, int PER>
+// XL (T == 1 with long rows only): the token's x is staged once per workgroup in LDS instead
+// of being held in every lane's registers, which leaves room for more waves per SIMD; one
+// barrier, after the weight reads are issued, publishes it.
+template <int LPR, int MCH, int RP, int PER, bool XL = false>
 __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden,
                                                                const float* __restrict__ logits, int T, int E,
                                                                BankArg w13, Plan plan, int H, int I, int k,
@@ -59,15 +62,25 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   __shared__ int s_pairs[PER > 0 ? kFuseMaxPairs : 1];
   __shared__ uint32_t s_bits[MAX_EXPERTS / 32];
   __shared__ int s_e, s_m;
-  // x of token 0, issued before routing when T == 1
-  u32x4 x0[MCH], x1[MCH];
+  // x of token 0, issued before routing when T == 1 (XL: 16-byte pieces q = tid + kThreads*j
+  // of the row, bound for LDS)
+  u32x4 x0[XL ? 1 : MCH], x1[XL ? 1 : MCH];
+  constexpr int XQ = XL ? (MCH * kWave * 2 + kThreads - 1) / kThreads : 1;
+  __shared__ __align__(16) uint8_t s_x[XL ? MCH * kWave * 32 : 16];
+  u32x4 xr[XQ];
   if constexpr (PER > 0) {
     if (T == 1) {
+      if constexpr (XL) {
 #pragma unroll
-      for (int m = 0; m < MCH; ++m) {
-        const int c = min(gl + LPR * m, NC - 1);  // chunks past NC read the last one, unused
-        x0[m] = ld16((const uint8_t*)hidden + (size_t)c * 32);
-        x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
+        for (int j = 0; j < XQ; ++j)
+          xr[j] = ld16((const uint8_t*)hidden + (size_t)min((int)threadIdx.x + kThreads * j, 2 * NC - 1) * 16);
+      } else {
+#pragma unroll
+        for (int m = 0; m < MCH; ++m) {
+          const int c = min(gl + LPR * m, NC - 1);  // chunks past NC read the last one, unused
+          x0[m] = ld16((const uint8_t*)hidden + (size_t)c * 32);
+          x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
+        }
       }
       wave_topk_ids<PER>(logits, E, k, my_id, my_l);
       route_wave = wave == 0;
@@ -78,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       single = __builtin_ctzll(hit);
       e = __builtin_amdgcn_readlane(my_id, single);
       cnt = 1;
-    } else {
+    } else if constexpr (!XL) {
       const int P = T * k;
       if (threadIdx.x < MAX_EXPERTS / 32) s_bits[threadIdx.x] = 0u;
       if (wave < T) {
@@ -128,6 +141,14 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     cnt = plan.counts[e];
     pairs = plan.sorted + plan.offsets[e];
   }
+  if constexpr (XL) {
+    // routing waited for the logits, read after x, so x is here: to LDS, freeing registers
+#pragma unroll
+    for (int j = 0; j < XQ; ++j) {
+      const int q = (int)threadIdx.x + kThreads * j;
+      if (q < 2 * NC) *(u32x4*)(s_x + q * 16) = xr[j];
+    }
+  }
   const int rows_per_block = (kThreads / kWave) * GPW * RP;
   const int i0 = blockIdx.x * rows_per_block + (wave * GPW + grp) * RP;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
@@ -166,6 +187,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     sg[m] = scale_value(bg[m], w13.scale_bf16);
     su[m] = scale_value(bu[m], w13.scale_bf16);
   }
+  if constexpr (XL) __syncthreads();  // x in LDS (written before the weight reads were issued)
   if constexpr (PER > 0) {
     // the router weights, while the weight codes are in flight
     if (route_wave && blockIdx.x == 0 && blockIdx.y == 0) {
@@ -178,13 +200,15 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   }
   for (int q = 0; q < cnt; ++q) {
     const int p = single >= 0 ? single : pairs[q];
-    if (single < 0) {
+    if (!XL && single < 0) {
       const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
+      if constexpr (!XL) {
 #pragma unroll
-      for (int m = 0; m < MCH; ++m) {
-        const int c = min(gl + LPR * m, NC - 1);
-        x0[m] = ld16(xb + (size_t)c * 32);
-        x1[m] = ld16(xb + (size_t)c * 32 + 16);
+        for (int m = 0; m < MCH; ++m) {
+          const int c = min(gl + LPR * m, NC - 1);
+          x0[m] = ld16(xb + (size_t)c * 32);
+          x1[m] = ld16(xb + (size_t)c * 32 + 16);
+        }
       }
     }
 #pragma unroll
@@ -193,8 +217,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
 #pragma unroll
       for (int m = 0; m < MCH; ++m) {
         if (gl + LPR * m < NC) {
-          g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], x0[m], x1[m]), g);
-          u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], x0[m], x1[m]), u);
+          u32x4 xa, xb;
+          if constexpr (XL) {
+            xa = *(const u32x4*)(s_x + (gl + LPR * m) * 32);
+            xb = *(const u32x4*)(s_x + (gl + LPR * m) * 32 + 16);
+          } else {
+            xa = x0[m];
+            xb = x1[m];
+          }
+          g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], xa, xb), g);
+          u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], xa, xb), u);
         }
       }
       g = group_sum<LPR>(g);
@@ -391,6 +423,13 @@ template <int LPR, int MCH, int RP, int PER>
 hipError_t g1(const Gemm1Args& a, hipStream_t s) {
   const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
   dim3 grid((a.I + rows - 1) / rows, a.slots);
+  if constexpr (PER > 0 && LPR == kWave && MCH >= 4) {
+    if (a.T == 1) {
+      launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER, true>), grid, dim3(kThreads), 0, s, a.hidden, a.logits,
+                    a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
+      return hipGetLastError();
+    }
+  }
   launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER>), grid, dim3(kThreads), 0, s, a.hidden, a.logits, a.T,
                      a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
   return hipGetLastError();
