@@ -82,7 +82,8 @@ def parse():
 
 
 # kernel kinds of the library -> a substring of their symbol names
-KERNEL_SYMBOLS = {"route": "route_", "sort": "sort_", "quant": "quant_rows", "gemm1": "gemm1_", "gemm2": "gemm2_",
+KERNEL_SYMBOLS = {"route": "route_", "sort": "sort_", "quant": "quant_rows_bf16", "hquant": "quant_rows_f32",
+                  "gemm1": "gemm1_", "gemm2": "gemm2_",
                   "combine": "combine_kernel"}
 COPY_BYTES = 1 << 30
 

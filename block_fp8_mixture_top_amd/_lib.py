@@ -23,7 +23,7 @@ STATUS_NAMES = {
 MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_STREAM, PATH_MFMA = 0, 1, 2, 3
 PATH_NAMES = {PATH_AUTO: "auto", PATH_GATHER: "gather", PATH_STREAM: "stream", PATH_MFMA: "mfma"}
-KERNEL_NAMES = {1: "route", 2: "sort", 3: "quant", 5: "gemm1", 6: "gemm2", 7: "combine"}
+KERNEL_NAMES = {1: "route", 2: "sort", 3: "quant", 4: "hquant", 5: "gemm1", 6: "gemm2", 7: "combine"}
 EXPORTS = [
     "moe_fp8_block_abi_version",
     "moe_fp8_block_last_error",

@@ -114,7 +114,7 @@ struct Carve {
 // Workspace layout; offsets into the caller's buffer.
 struct Layout {
   size_t ids, w, counts, offsets, sorted, act, n_act, tile_off, scratch;
-  size_t h, y, xq, xs;
+  size_t h, y, xq, xs, hq, hs;
   size_t total;
 };
 
@@ -137,6 +137,8 @@ Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
   if (path == MOE_PATH_MFMA) {
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
+    L.hq = c.take(P * (size_t)I);
+    L.hs = c.take(P * 4);
   }
   L.total = c.off;
   return L;
@@ -387,7 +389,10 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
     RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s),
         "gemm1 mfma launch");
-    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hf, b2, plan, E, (int)P, H, I, y, s), "gemm2 mfma launch");
+    uint8_t* hq = at<uint8_t>(workspace, L.hq);
+    float* hs = at<float>(workspace, L.hs);
+    RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, hq, hs, s), "h quant launch");
+    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y, s), "gemm2 mfma launch");
     RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
   }
   if (info) info->kernels = R.n;

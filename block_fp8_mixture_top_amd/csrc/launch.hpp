@@ -111,10 +111,12 @@ bool mfma_shape_ok(int H, int I);
 // hf[p, I] = silu(gate) * up in float for every sorted pair position p.
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
                              int P, int H, int I, int k, float* hf, hipStream_t s);
-// y[pair, H] = s_h * W2 h for every pair, h quantised per pair row (float, no atomics; the
-// combine applies the weights).
-hipError_t launch_gemm2_mfma(const float* hf, const BankArg& w2, const Plan& plan, int E, int P, int H, int I,
-                             float* y, hipStream_t s);
+// Per-row e4m3 codes and scales (amax/448) of hf, rows in sorted-position order.
+hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s);
+// y[pair, H] = s_h * W2 h for every pair from the h codes hq and row scales hs (float, no
+// atomics; the combine applies the weights).
+hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
+                             int H, int I, float* y, hipStream_t s);
 
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);

@@ -71,6 +71,31 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
   if (lane == 0) scales[row] = s;
 }
 
+// The same for rows of float (h before the down GEMM, in sorted-position order).
+__global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __restrict__ x, int rows, int cols,
+                                                             uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  const int row = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+  if (row >= rows) return;
+  const int lane = lane_id();
+  const float* xr = x + (size_t)row * cols;
+  float amax = 0.0f;
+  for (int c = lane * 8; c < cols; c += kWave * 8) {
+    const f32x4 a = *(const f32x4*)(xr + c), b = *(const f32x4*)(xr + c + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(a[q]), __builtin_fabsf(b[q])));
+  }
+  amax = wave_max(amax);
+  const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+  for (int c = lane * 8; c < cols; c += kWave * 8) {
+    const f32x4 a = *(const f32x4*)(xr + c), b = *(const f32x4*)(xr + c + 4);
+    const uint32_t lo = enc2(a[0] / s, a[1] / s) | (enc2(a[2] / s, a[3] / s) << 16);
+    const uint32_t hi = enc2(b[0] / s, b[1] / s) | (enc2(b[2] / s, b[3] / s) << 16);
+    *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(lo, hi);
+  }
+  if (lane == 0) scales[row] = s;
+}
+
 // ---------------------------------------------------------------- tile lookup
 
 // Tile `tile` of the grouped problem -> expert and first sorted position. Tiles of one
@@ -378,20 +403,17 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 // Each pair's y row = s_h * W2 h is written once, in float; the combine kernel applies the
 // router weights.
 template <int KB>  // I / 128
-__global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restrict__ hf, BankArg w2, Plan plan, int E,
+__global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
+                                                            BankArg w2, Plan plan, int E,
                                                             int H, int I, int nblocks, float* __restrict__ y) {
   constexpr int HM = 64;           // pairs per half tile
   constexpr int FT = 4;
   constexpr int NCH = 4 * FT * 16;
   constexpr int WB = 64 * kRowB;   // one wave's w2 rows of a stage
   constexpr int HB = HM * kRowB;   // the h codes of one K block
-  constexpr int HPT = KB * 128 / 4;  // h values per thread (4 threads per row)
   __shared__ __align__(16) uint8_t sH[KB * HB];
   __shared__ __align__(16) uint8_t ring[4 * kStages * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
-  __shared__ float s_rt[(kMaxH / 128) * (kMaxI / 128)];
-  __shared__ float s_last[kMaxH / 128];
-  __shared__ float s_hs[HM];
 
   const int L = xcd_tile(blockIdx.x, nblocks);
   const int tile = L >> 1, half = L & 1;
@@ -427,55 +449,20 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restr
     for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + i * 1024);
   };
   stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
-  __syncthreads();
-  if (tid < (H / 128) * KB) {
-    const int nb = tid / KB;
-    scale_ratio(s_sc + nb * KB, KB, tid - nb * KB, s_rt + nb * KB, s_last + nb);
-  }
   // (visible after the barrier that follows the h codes)
   {
     const int nvalid = pos_end - pos0 < HM ? pos_end - pos0 : HM;
+    // the half's h codes: 8 * KB copies of 8 rows x 128 bytes, 2 * KB per wave (rows past the
+    // expert's pairs copy the first row; their results are never stored)
+#pragma unroll
+    for (int i = 0; i < 2 * KB; ++i) {
+      const int q = wave * 2 * KB + i;
+      const int kb = q >> 3, r = (q & 7) * 8 + lr;
+      const int rr = r < nvalid ? r : 0;
+      g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), sH + kb * HB + (q & 7) * 1024);
+    }
     if (nst > 0) issue(0);
     if (nst > 1) issue(1);
-    // h rows: thread t takes row t/4, quarter t%4 (HPT contiguous values); the four
-    // threads of a row are adjacent lanes
-    {
-      const int r = tid >> 2, qd = tid & 3;
-      const bool ok = r < nvalid;
-      // every read unconditional (rows past the expert's pairs read its first row), so that
-      // they are all in flight before the first wait; those rows are then zeroed
-      const float* src = hf + (size_t)(pos0 + (ok ? r : 0)) * I + qd * HPT;
-      f32x4 v[HPT / 4];
-#pragma unroll
-      for (int j = 0; j < HPT / 4; ++j) v[j] = *(const f32x4*)(src + 4 * j);
-#pragma unroll
-      for (int j = 0; j < HPT / 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[j][q] = ok ? v[j][q] : 0.0f;
-      float am = 0.0f;
-#pragma unroll
-      for (int j = 0; j < HPT / 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) am = __builtin_fmaxf(am, __builtin_fabsf(v[j][q]));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 1, kWave));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 2, kWave));
-      const float s = am > 0.0f ? am / kE4M3Max : 1.0f;
-      const float rs = 1.0f / s;  // codes of v * (1/s): within 1 ulp of v / s
-      if (qd == 0) s_hs[r] = s;
-      // 16 codes (one 16-byte chunk) at a time, placed by the swizzle of their K block
-#pragma unroll
-      for (int j = 0; j < HPT / 16; ++j) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 a = v[4 * j + m];
-          wd[m] = enc2(a[0] * rs, a[1] * rs) | (enc2(a[2] * rs, a[3] * rs) << 16);
-        }
-        const int c = (qd * HPT) / 16 + j;  // chunk of the row
-        *(u32x4*)(sH + (c >> 3) * HB + r * kRowB + (((c & 7) ^ sw(r)) << 4)) = u32x4{wd[0], wd[1], wd[2], wd[3]};
-      }
-    }
-    __syncthreads();
     float hsc[4][4];
     int prow[4][4];
 #pragma unroll
@@ -484,9 +471,11 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restr
       for (int q = 0; q < 4; ++q) {
         const int r = pt * 16 + kq * 4 + q;
         const bool ok = r < nvalid;
-        hsc[pt][q] = s_hs[r];
+        hsc[pt][q] = hs[pos0 + (ok ? r : 0)];
         prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
       }
+    wait_vm<0>();  // everyone's h codes are in after the barrier
+    __syncthreads();
 
     f32x4 acc[FT][4];
     for (int st = 0; st < nst; ++st) {
@@ -512,20 +501,21 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restr
       const int n0 = c * NCH + wave * 64;
       // features n0 .. n0 + 63 share one 128-row scale block
       const int nb = n0 / kScaleBlock;
-      const float r = s_rt[nb * KB + kb];  // uniform
-      if (r != 0.0f) {
-        if (r != 1.0f) {
+      // each MFMA starts from zero and its block product is scaled into the accumulator on
+      // the VALU while the next MFMA runs
+      const float sc = s_sc[nb * KB + kb];  // uniform
+      {
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 pp = mfma_fp8(a[0], bw[0], z);
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft)
+        for (int j = 0; j < FT * 4; ++j) {
+          const int ft = j / 4, pt = j % 4;
+          f32x4 nx;
+          if (j + 1 < FT * 4) nx = mfma_fp8(a[(j + 1) % 4], bw[(j + 1) / 4], z);
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[ft][pt][q] *= r;
+          for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
+          if (j + 1 < FT * 4) pp = nx;
         }
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = mfma_fp8(a[pt], bw[ft], acc[ft][pt]);
       }
       if (kb == KB - 1) {
 #pragma unroll
@@ -534,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restr
           for (int q = 0; q < 4; ++q) {
             if (prow[pt][q] < 0) continue;
             float* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
-            const float ys = s_last[nb] * hsc[pt][q];
+            const float ys = hsc[pt][q];
 #pragma unroll
             for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = acc[ft][pt][q] * ys;
           }
@@ -544,9 +534,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const float* __restr
 }
 
 template <int KB>
-hipError_t g2m(const float* hf, const BankArg& w2, const Plan& plan, int E, int nblocks, int H, int I, float* y,
-               hipStream_t s) {
-  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hf, w2, plan, E, H, I, nblocks, y);
+hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
+               int I, float* y, hipStream_t s) {
+  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y);
   return hipGetLastError();
 }
 
@@ -570,6 +560,12 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t
   return hipGetLastError();
 }
 
+hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s) {
+  const int blocks = (rows + 3) / 4;
+  launch_kernel(quant_rows_f32_kernel, dim3(blocks), dim3(256), 0, s, x, rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int P,
                              int H, int I, int k, float* hf, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
@@ -578,15 +574,15 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_mfma(const float* hf, const BankArg& w2, const Plan& plan, int E, int P, int H, int I,
-                             float* y, hipStream_t s) {
+hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
+                             int H, int I, float* y, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E) * 2;
   switch (I / 128) {
-    case 1: return g2m<1>(hf, w2, plan, E, nblocks, H, I, y, s);
-    case 2: return g2m<2>(hf, w2, plan, E, nblocks, H, I, y, s);
-    case 3: return g2m<3>(hf, w2, plan, E, nblocks, H, I, y, s);
-    default: return g2m<4>(hf, w2, plan, E, nblocks, H, I, y, s);
+    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
+    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
+    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
+    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
   }
 }
 

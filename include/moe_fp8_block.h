@@ -173,6 +173,7 @@ typedef enum {
   MOE_K_ROUTE = 1,    /* top-k and weights */
   MOE_K_SORT = 2,     /* token-to-expert sort (one or three kernels) */
   MOE_K_QUANT = 3,    /* per-token e4m3 activation quantisation (MFMA path) */
+  MOE_K_HQUANT = 4,   /* per-(token, slot) e4m3 quantisation of h before the down GEMM (MFMA path) */
   MOE_K_GEMM1 = 5,    /* gate/up GEMM with silu(gate)*up */
   MOE_K_GEMM2 = 6,    /* down GEMM (with the combine on GATHER) */
   MOE_K_COMBINE = 7   /* router-weighted sum of the slots (STREAM and MFMA paths) */
