@@ -110,13 +110,16 @@ __device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int t
   return lo;
 }
 
-// Workgroup -> tile with the tiles of one expert kept on one XCD (workgroups are dealt to
-// the 8 XCDs round-robin), so the expert's weights are fetched into one L2. nblocks is a
-// multiple of 8, which makes the map a permutation of [0, nblocks).
-__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
-  const int per = nblocks / 8;
+// Workgroup -> work item in [0, n), n the number of items of this routing (the grid is an
+// upper bound on it). Workgroups are dealt to the 8 XCDs round-robin; XCD x gets items
+// x*per .. x*per + per - 1 with per = ceil(n/8), so every XCD gets an equal share and
+// consecutive items (the tiles of one expert, the blocks of one tile) stay on one XCD and
+// share its L2. Returns n for a workgroup with no item; the grid must hold 8*per of them.
+__device__ __forceinline__ int xcd_item(int bid, int n) {
+  const int per = (n + 7) / 8;
   const int x = bid & 7, i = bid >> 3;
-  return x * per + i;
+  const int L = x * per + i;
+  return i < per && L < n ? L : n;
 }
 
 
@@ -233,9 +236,10 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
   __shared__ int s_tok[TM];
 
   const int nfb = I / 128;
-  const int L = xcd_tile(blockIdx.x, nblocks);  // consecutive L share an expert's rows and a tile's x
+  const int nitems = plan.tile_off[E] * nfb;
+  const int L = xcd_item(blockIdx.x, nitems);  // consecutive L share an expert's rows and a tile's x
+  if (L >= nitems) return;
   const int tile = L / nfb, fb = L - tile * nfb;
-  if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
   const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * TM;
   const int pos_end = plan.offsets[e + 1];
@@ -415,9 +419,10 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   __shared__ __align__(16) uint8_t ring[4 * kStages * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
 
-  const int L = xcd_tile(blockIdx.x, nblocks);
+  const int nitems = plan.tile_off[E] * 2;
+  const int L = xcd_item(blockIdx.x, nitems);
+  if (L >= nitems) return;
   const int tile = L >> 1, half = L & 1;
-  if (tile >= plan.tile_off[E]) return;
   const int e = find_expert(plan.tile_off, E, tile);
   const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM + half * HM;
   const int pos_end = plan.offsets[e + 1];
@@ -542,8 +547,9 @@ hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan
 
 }  // namespace
 
-// Upper bound on the tiles of any routing (sum over experts of ceil(count/64) <= P/64 + E),
-// rounded up to a multiple of 8 so that xcd_tile maps the grid onto [0, bound) one to one.
+// Upper bound on the tiles of any routing (sum over experts of ceil(count/128) <=
+// P/128 + E), rounded up to a multiple of 8; a grid of bound * (items per tile) workgroups
+// covers 8 * ceil(n/8) for any n items of a routing.
 size_t mfma_tiles_bound(int P, int E) {
   const size_t b = (size_t)(P + kTM - 1) / kTM + (size_t)E;
   return (b + 7) / 8 * 8;
