@@ -114,7 +114,7 @@ struct Carve {
 // Workspace layout; offsets into the caller's buffer.
 struct Layout {
   size_t ids, w, counts, offsets, sorted, act, n_act, tile_off, scratch;
-  size_t h, y, xq, xs, hq, hs;
+  size_t h, y, yexp, xq, xs, hq, hs;
   size_t total;
 };
 
@@ -133,8 +133,10 @@ Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
   L.tile_off = c.take((size_t)(E + 1) * 4);
   L.scratch = c.take(moe::sort_scratch_bytes((int)P, E));
   L.h = c.take(P * (size_t)I * 4);  // h in float, [pair or sorted position, I]
-  if (path == MOE_PATH_STREAM || path == MOE_PATH_MFMA) L.y = c.take(P * (size_t)H * 4);
+  if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);  // y in float
   if (path == MOE_PATH_MFMA) {
+    L.y = c.take(P * (size_t)H * 2);  // y in fp16, one exponent per (pair, 64 outputs)
+    L.yexp = c.take(P * (size_t)(H / 64));
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
     L.hq = c.take(P * (size_t)I);
@@ -385,15 +387,16 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     uint8_t* xq = at<uint8_t>(workspace, L.xq);
     float* xs = at<float>(workspace, L.xs);
     float* hf = at<float>(workspace, L.h);
-    float* y = at<float>(workspace, L.y);
     RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
     RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s),
         "gemm1 mfma launch");
     uint8_t* hq = at<uint8_t>(workspace, L.hq);
     float* hs = at<float>(workspace, L.hs);
     RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, hq, hs, s), "h quant launch");
-    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y, s), "gemm2 mfma launch");
-    RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
+    _Float16* y16 = at<_Float16>(workspace, L.y);
+    int8_t* yexp = at<int8_t>(workspace, L.yexp);
+    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
+    RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, w, T, H, top_k, out, out_bf16, s), "combine launch");
   }
   if (info) info->kernels = R.n;
   return ok();

@@ -113,10 +113,14 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
                              int P, int H, int I, int k, float* hf, hipStream_t s);
 // Per-row e4m3 codes and scales (amax/448) of hf, rows in sorted-position order.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s);
-// y[pair, H] = s_h * W2 h for every pair from the h codes hq and row scales hs (float, no
+// y[pair, H] = s_h * W2 h for every pair from the h codes hq and row scales hs, stored as
+// fp16 of y * 2^-e with one exponent e per (pair, 64 outputs) in yexp[pair, H/64] (no
 // atomics; the combine applies the weights).
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
-                             int H, int I, float* y, hipStream_t s);
+                             int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
+// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^yexp[t*k + j, n/64], slots summed in order.
+hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, int T, int H, int k, void* out,
+                              int out_bf16, hipStream_t s);
 
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);

@@ -96,6 +96,46 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
   if (lane == 0) scales[row] = s;
 }
 
+// ---------------------------------------------------------------- y in fp16
+
+// Exponent ey for a group of y values whose largest magnitude has float bits m: the values
+// are stored as fp16 of v * 2^-ey, which puts the largest in [2^14, 2^15) (below the fp16
+// maximum) and keeps the 11-bit significand for all values within 2^24 of it. ey is kept in
+// [-60, 100], so 2^-ey and 2^ey are normal floats; a group that is all zero gets 0.
+__device__ __forceinline__ int y_exponent(uint32_t m) {
+  if (m == 0u) return 0;
+  const int eb = (int)(m >> 23) - 127;  // floor(log2) for normal m; -127 for subnormal m
+  const int ey = eb - 14;
+  return ey < -60 ? -60 : (ey > 100 ? 100 : ey);
+}
+
+// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/64], slots in order; four
+// consecutive outputs (one exponent group) per thread.
+__global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __restrict__ y,
+                                                          const int8_t* __restrict__ yexp,
+                                                          const float* __restrict__ w, int T, int H, int k,
+                                                          void* __restrict__ out, int out_bf16) {
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (idx >= (size_t)T * H) return;
+  const size_t t = idx / H, n = idx % H;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < k; ++j) {
+    const size_t p = t * k + j;
+    const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / 64) + n / 64]) << 23);  // 2^e
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 v = *(const h4*)(y + p * H + n);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = __builtin_fmaf(w[p], (float)v[q] * up, s[q]);
+  }
+  if (out_bf16) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
+    *(uint2*)((uint16_t*)out + idx) = make_uint2(lo, hi);
+  } else {
+    *(f32x4*)((float*)out + idx) = s;
+  }
+}
+
 // ---------------------------------------------------------------- tile lookup
 
 // Tile `tile` of the grouped problem -> expert and first sorted position. Tiles of one
@@ -409,7 +449,8 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 template <int KB>  // I / 128
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
-                                                            int H, int I, int nblocks, float* __restrict__ y) {
+                                                            int H, int I, int nblocks, _Float16* __restrict__ y,
+                                                            int8_t* __restrict__ yexp) {
   constexpr int HM = 64;           // pairs per half tile
   constexpr int FT = 4;
   constexpr int NCH = 4 * FT * 16;
@@ -523,15 +564,30 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
         }
       }
       if (kb == KB - 1) {
+        // y of pair (pt, 4kq+q), features n0 .. n0+63, held by the 16 lanes of row kq (r16)
+        // times FT: stored in fp16 with one power-of-two exponent per (pair, 64 features)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (prow[pt][q] < 0) continue;
-            float* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
-            const float ys = hsc[pt][q];
+            float v[FT];
+            uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = acc[ft][pt][q] * ys;
+            for (int ft = 0; ft < FT; ++ft) {
+              v[ft] = acc[ft][pt][q] * hsc[pt][q];
+              m = max(m, __float_as_uint(__builtin_fabsf(v[ft])));
+            }
+            m = max(m, dpp_u32<0xB1, 0xF, 0xF>(0u, m));   // quad_perm [1,0,3,2]
+            m = max(m, dpp_u32<0x4E, 0xF, 0xF>(0u, m));   // quad_perm [2,3,0,1]
+            m = max(m, dpp_u32<0x124, 0xF, 0xF>(0u, m));  // row_ror:4
+            m = max(m, dpp_u32<0x128, 0xF, 0xF>(0u, m));  // row_ror:8
+            const int ey = y_exponent(m);
+            const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
+            if (prow[pt][q] < 0) continue;
+            _Float16* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = (_Float16)(v[ft] * down);
+            if (r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
           }
       }
     }
@@ -540,8 +596,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
 
 template <int KB>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
-               int I, float* y, hipStream_t s) {
-  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y);
+               int I, _Float16* y, int8_t* yexp, hipStream_t s) {
+  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y, yexp);
   return hipGetLastError();
 }
 
@@ -572,6 +628,14 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* co
   return hipGetLastError();
 }
 
+hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, int T, int H, int k, void* out,
+                              int out_bf16, hipStream_t s) {
+  const size_t n = (size_t)T * H / 4;
+  launch_kernel(combine_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, T, H, k, out,
+                out_bf16);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int P,
                              int H, int I, int k, float* hf, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
@@ -581,14 +645,14 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
 }
 
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
-                             int H, int I, float* y, hipStream_t s) {
+                             int H, int I, _Float16* y, int8_t* yexp, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E) * 2;
   switch (I / 128) {
-    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
-    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
-    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
-    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, y, s);
+    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
   }
 }
 
