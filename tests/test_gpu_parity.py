@@ -196,6 +196,23 @@ def test_sweep_forced(decode_banks, path):
     check_out(out, oracle_out(c), 0, f"sweep forced {path}")
 
 
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("H,I", [(384, 256), (640, 384), (8192, 128)])
+def test_odd_shapes_forced(path, H, I):
+    """Every path at shapes the decode banks do not reach. H=384: 24 chunks of 16 codes per
+    row, so lane groups of 16 with a second chunk that only some lanes have, and a last MFMA
+    output chunk of 128 worked by two waves only. I = 256, 384: the down GEMM's other K-block
+    counts. H=8192: the largest H the MFMA kernels take."""
+    T = 2 if path == "gather" else 48
+    c = W.make_case("decode", T=T, seed=21, device=DEV, E=16, H=H, I=I, top_k=4)
+    say("odd shape", path, H, I)
+    act = 1 if path == "mfma" else 0
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    assert info["path"] == path
+    check_out(out, oracle_out(c, act_mode=act), act, f"{path} H={H} I={I}")
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_large_expert_workload(T):
     """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest
