@@ -109,30 +109,35 @@ __device__ __forceinline__ int y_exponent(uint32_t m) {
   return ey < -60 ? -60 : (ey > 100 ? 100 : ey);
 }
 
-// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/64], slots in order; four
-// consecutive outputs (one exponent group) per thread.
+// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/64], slots in order; eight
+// consecutive outputs (within one exponent group) per thread, read as one 16-byte load per
+// slot, the slots' reads unrolled so several are in flight.
 __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __restrict__ y,
                                                           const int8_t* __restrict__ yexp,
                                                           const float* __restrict__ w, int T, int H, int k,
                                                           void* __restrict__ out, int out_bf16) {
-  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (idx >= (size_t)T * H) return;
   const size_t t = idx / H, n = idx % H;
-  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const size_t p = t * k + j;
     const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / 64) + n / 64]) << 23);  // 2^e
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 v = *(const h4*)(y + p * H + n);
+    const float wj = w[p];
+    const h8 v = *(const h8*)(y + p * H + n);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = __builtin_fmaf(w[p], (float)v[q] * up, s[q]);
+    for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, (float)v[q] * up, s[q]);
   }
   if (out_bf16) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
-    *(uint2*)((uint16_t*)out + idx) = make_uint2(lo, hi);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (uint32_t)f32_to_bf16(s[2 * q]) | ((uint32_t)f32_to_bf16(s[2 * q + 1]) << 16);
+    *(u32x4*)((uint16_t*)out + idx) = u32x4{o[0], o[1], o[2], o[3]};
   } else {
-    *(f32x4*)((float*)out + idx) = s;
+    *(f32x4*)((float*)out + idx) = f32x4{s[0], s[1], s[2], s[3]};
+    *(f32x4*)((float*)out + idx + 4) = f32x4{s[4], s[5], s[6], s[7]};
   }
 }
 
@@ -630,7 +635,7 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* co
 
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, int T, int H, int k, void* out,
                               int out_bf16, hipStream_t s) {
-  const size_t n = (size_t)T * H / 4;
+  const size_t n = (size_t)T * H / 8;
   launch_kernel(combine_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, T, H, k, out,
                 out_bf16);
   return hipGetLastError();
