@@ -7,18 +7,20 @@
 // rows being tokens for GEMM1 and (token, slot) pairs for GEMM2.
 //
 // One v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 scales) covers exactly one 128-wide
-// K block, so every MFMA result is one block's partial sum and is multiplied by that block's
-// bank scale before it is accumulated (FreeToken PR #662, PR body: one scale per 128x128
-// block). A and B are read with the same per-lane K pattern (chunks kq and kq + 4 of the
-// block for lanes of K quarter kq), so whatever order the unit walks K in, matching A and
-// B bytes meet.
+// K block, so every MFMA result is one block's partial sum and takes that block's bank
+// scale (FreeToken PR #662, PR body: one scale per 128x128 block): GEMM1 rescales its
+// accumulator to the block's scale before the MFMA accumulates in place, GEMM2 scales each
+// zero-start product into its accumulator. A and B are read with the same per-lane K
+// pattern (chunks kq and kq + 4 of the block for lanes of K quarter kq), so whatever order
+// the unit walks K in, matching A and B bytes meet.
 //
 // Both GEMMs work on tiles of 128 sorted (token, slot) pairs of one expert. Every operand
 // goes global -> LDS with direct loads of 8 rows x 128 contiguous bytes per instruction,
-// through LDS rings a few K blocks ahead of the multiply. GEMM1 writes h = silu(gate)*up in
-// float; GEMM2 reads each h row once, takes its amax, quantises it into LDS and multiplies.
-// GEMM2 writes each pair's y row in float once; the combine kernel sums the slots of a
-// token in slot order with the router weights.
+// through LDS rings a few K blocks ahead of the multiply. GEMM1 (a 128-feature block of h
+// per workgroup) writes h = silu(gate)*up in float; a row quantiser turns it into e4m3
+// codes and one scale per (token, slot); GEMM2 copies the codes to LDS, multiplies, and
+// writes each pair's y row once, in fp16 with a power-of-two exponent per 64 outputs; the
+// combine kernel sums the slots of a token in slot order with the router weights.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -443,14 +445,14 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 
 // One workgroup per (expert, 128-pair tile, half of 64 pairs), 4 waves; the two halves of a
 // tile are consecutive workgroups of one XCD, so the second reads the expert's w2 from L2.
-// The half's float h rows are read once, quantised per (token, slot) row to e4m3 with
-// scale amax/448 (1 for a zero row) and placed in LDS: A = h codes (pairs as rows). B = w2
-// rows (features). The H outputs go in chunks of 256; wave w owns features 64w .. 64w+64 of
-// each chunk (FT = 4 MFMA tiles; a last chunk of 128 has work for waves 0 and 1 only), so
-// lane (r16, kq) of a result holds pairs 4kq..4kq+3 of feature r16. Each wave streams its
-// own w2 rows, (chunk, K block) after (chunk, K block), through a private 3-deep LDS ring.
-// Each pair's y row = s_h * W2 h is written once, in float; the combine kernel applies the
-// router weights.
+// The half's h codes (e4m3 per (token, slot) row, scale amax/448, from the row quantiser)
+// are copied to LDS once: A = h codes (pairs as rows), B = w2 rows (features). The H
+// outputs go in chunks of 256; wave w owns features 64w .. 64w+64 of each chunk (FT = 4
+// MFMA tiles; a last chunk of 128 has work for waves 0 and 1 only), so lane (r16, kq) of a
+// result holds pairs 4kq..4kq+3 of feature r16. Each wave streams its own w2 rows, (chunk,
+// K block) after (chunk, K block), through a private 3-deep LDS ring. Each pair's y row =
+// s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
+// applies the router weights.
 template <int KB>  // I / 128
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
