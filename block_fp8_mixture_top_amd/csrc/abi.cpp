@@ -49,9 +49,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 moe_opts defaults() {
   moe_opts o;
-  o.gate_ratio = 0.4f;
+  // measured crossovers on MI355X at E=256, H=2048, I=512, top_k=8 (tune_gate.py): GATHER
+  // is fastest up to 2 pairs per expert, MFMA from 3; STREAM never wins there but takes the
+  // grouped work of shapes the MFMA kernels do not cover
+  o.gate_ratio = 2.0f;
   o.force_path = MOE_PATH_AUTO;
-  o.mfma_min_tokens_per_expert = 32;
+  o.mfma_min_tokens_per_expert = 2;
   o.reserved = 0;
   return o;
 }
@@ -91,7 +94,7 @@ int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* 
   int p = gate(T, E, top_k, o);
   const bool forced = o.force_path != MOE_PATH_AUTO;
   if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
-    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 2048 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
     p = MOE_PATH_STREAM;
   }
   if (p == MOE_PATH_GATHER && !moe::gemm2_gather_supported(top_k, I)) {

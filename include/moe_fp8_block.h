@@ -89,9 +89,9 @@ typedef struct {
 
 /* Host-side options; NULL means the defaults below. */
 typedef struct {
-  float gate_ratio;                  /* gather iff T*top_k <= gate_ratio*E (default 0.4) */
+  float gate_ratio;                  /* gather iff T*top_k <= gate_ratio*E (default 2.0, measured) */
   int32_t force_path;                /* moe_path; anything but AUTO is taken as asked or fails */
-  int32_t mfma_min_tokens_per_expert;/* grouped work uses MFMA iff T*top_k >= this*E (default 32) */
+  int32_t mfma_min_tokens_per_expert;/* grouped work uses MFMA iff T*top_k >= this*E (default 2, measured) */
   int32_t reserved;                  /* must be 0 */
 } moe_opts;
 
@@ -117,8 +117,11 @@ int moe_fp8_block_default_opts(moe_opts* opts);
 /*
  * The gather/grouped gate, host only (gaudi-cookbook "fp8-moe-gather", The fix and the
  * VLLM_HPU_MOE_GATHER_RATIO row of its table): GATHER iff T*top_k <= gate_ratio*E,
- * else MFMA iff T*top_k >= mfma_min_tokens_per_expert*E, else STREAM. A forced path is
- * reported unchanged. Writes path, act_mode and slots into *info; no HIP call.
+ * else MFMA iff T*top_k >= mfma_min_tokens_per_expert*E, else STREAM. The defaults are the
+ * crossovers measured on MI355X by block_fp8_mixture_top_amd/tune_gate.py (the page's
+ * ratio 0.4 was chosen for another device). A forced path is reported unchanged; forward
+ * runs STREAM where the gate says MFMA for a shape the MFMA kernels do not take. Writes
+ * path, act_mode and slots into *info; no HIP call.
  */
 int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe_run_info* info);
 

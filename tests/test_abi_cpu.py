@@ -42,8 +42,8 @@ def test_abi_version_matches_header(lib):
 def test_default_opts(lib):
     o = L.Opts()
     assert lib.moe_fp8_block_default_opts(ctypes.byref(o)) == 0
-    assert o.gate_ratio == pytest.approx(0.4)
-    assert (o.force_path, o.mfma_min_tokens_per_expert, o.reserved) == (0, 32, 0)
+    assert o.gate_ratio == pytest.approx(2.0)
+    assert (o.force_path, o.mfma_min_tokens_per_expert, o.reserved) == (0, 2, 0)
     assert lib.moe_fp8_block_default_opts(None) == -1
     assert b"NULL" in lib.moe_fp8_block_last_error()
 
@@ -58,9 +58,9 @@ def _path(lib, T, E, k, **kw):
     return st, info
 
 
-@pytest.mark.parametrize("T,path", [(1, 1), (4, 1), (12, 1), (13, 2), (16, 2), (64, 2), (1023, 2), (1024, 3), (4096, 3)])
+@pytest.mark.parametrize("T,path", [(1, 1), (4, 1), (12, 1), (64, 1), (65, 3), (96, 3), (1024, 3), (4096, 3)])
 def test_gate_on_the_decode_shape(lib, T, path):
-    """gather iff T*k <= 0.4*E (E=256, k=8: T <= 12); MFMA from 32 pairs per expert."""
+    """Defaults: gather iff T*k <= 2*E (E=256, k=8: T <= 64); MFMA from 2 pairs per expert."""
     st, info = _path(lib, T, 256, 8)
     assert st == 0
     assert info.path == path
@@ -71,6 +71,9 @@ def test_gate_on_the_decode_shape(lib, T, path):
 def test_gate_ratio_and_forced_paths(lib):
     assert _path(lib, 16, 256, 8, gate_ratio=1.0)[1].path == 1
     assert _path(lib, 1, 256, 8, gate_ratio=0.0)[1].path == 2
+    # the page's ratio and a high MFMA threshold leave STREAM in between
+    assert _path(lib, 13, 256, 8, gate_ratio=0.4, mfma_min_tokens_per_expert=32)[1].path == 2
+    assert _path(lib, 1024, 256, 8, gate_ratio=0.4, mfma_min_tokens_per_expert=32)[1].path == 3
     for forced in (1, 2, 3):
         assert _path(lib, 4096, 256, 8, force_path=forced)[1].path == forced
     assert _path(lib, 1, 256, 8, force_path=7)[0] == -1

@@ -179,11 +179,11 @@ def decode_banks():
 
 @pytest.mark.parametrize("T", [1, 4, 12, 16, 32, 64])
 def test_sweep_auto(decode_banks, T):
-    """Zipf(1.1) popularity over the decode banks; T<=12 gathers, T>=16 streams."""
+    """Zipf(1.1) popularity over the decode banks; with the default gate every T here gathers."""
     c = W.make_case("sweep", T=T, seed=2, device=DEV, banks=decode_banks)
     say("sweep", T)
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
-    assert info["path"] == ("gather" if T <= 12 else "stream")
+    assert info["path"] == "gather"
     check_out(out, oracle_out(c), 0, f"sweep T={T} {info['path']}")
 
 
@@ -213,8 +213,8 @@ def test_odd_shapes_forced(path, H, I):
     check_out(out, oracle_out(c, act_mode=act), act, f"{path} H={H} I={I}")
 
 
-@pytest.mark.parametrize("T", [1, 16])
-def test_large_expert_workload(T):
+@pytest.mark.parametrize("T,path", [(1, None), (16, None), (16, "stream")])
+def test_large_expert_workload(T, path):
     """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest
     hold NaN codes and NaN scales, so reading an unrouted expert would poison the output."""
     shp = W.SHAPES["large"]
@@ -225,9 +225,10 @@ def test_large_expert_workload(T):
     banks = W.make_banks("large", seed=4, device=DEV, experts=used)
     c = W.make_case("large", T=T, seed=4, device=DEV, banks=banks)
     c.logits = logits.to(DEV)
-    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
+    kw = {} if path is None else {"force_path": PATHS[path]}
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
-    assert info["path"] == ("gather" if T == 1 else "stream")
+    assert info["path"] == (path or "gather")  # the default gate gathers up to 2 pairs per expert
     assert torch.isfinite(out.float()).all()
     rows = np.array([0]) if T == 1 else np.array([0, 7, T - 1])
     need = O.routed_experts(ids[rows])
@@ -250,14 +251,16 @@ def test_prefill_sampled(decode_banks, T):
     check_out(sub, res, 1, f"prefill T={T} sampled")
 
 
-def test_mfma_small_sizes_forced(decode_banks):
-    """Forced MFMA with ragged tiles (few tokens per expert) against all rows."""
-    c = W.make_case("decode", T=40, seed=8, device=DEV, banks=decode_banks)
-    say("mfma forced T=40")
+@pytest.mark.parametrize("T", [40, 100])
+def test_mfma_small_sizes_forced(decode_banks, T):
+    """Forced MFMA with ragged tiles (few tokens per expert) against all rows; T=40 sorts
+    its 320 pairs in one workgroup, T=100 (800 pairs) takes the three-pass sort."""
+    c = W.make_case("decode", T=T, seed=8, device=DEV, banks=decode_banks)
+    say("mfma forced", T)
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
                           force_path=M.PATH_MFMA)
     res = oracle_out(c, act_mode=1)
-    check_out(out, res, 1, "mfma T=40")
+    check_out(out, res, 1, f"mfma T={T}")
 
 
 # ------------------------------------------------------------------- properties
