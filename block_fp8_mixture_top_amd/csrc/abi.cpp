@@ -323,8 +323,10 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "H and I must be positive (got H=%d, I=%d)", H, I);
-  if (H % 128 != 0 || I % 128 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (got H=%d, I=%d)", H, I);
+  // rows of 16-byte code chunks; a last 128-wide scale block may be partial (the MFMA path
+  // needs whole blocks and is never chosen otherwise)
+  if (H % 16 != 0 || I % 16 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 16 (got H=%d, I=%d)", H, I);
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
   const moe_opts o = opts ? *opts : defaults();
   if ((st = check_opts(&o))) return st;

@@ -158,14 +158,18 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   // divides 128), so a chunk's gate and up scales are shared by them. Scales are read first
   // and waited for only after every code read is issued.
   u32x4 cg[RP][MCH], cu[RP][MCH];
+  // Scale blocks tile the stored [2I, H] rows, so up row I+i is in block (I+i)/128 (the same
+  // as the gate blocks shifted by I/128 when 128 divides I). I is even, so the up rows of a
+  // lane group, like its gate rows, share one block.
   ScaleBits bg[MCH], bu[MCH];
-  const int ib = (i0 < I ? i0 : I - 1) / kScaleBlock;
+  const int i0c = i0 < I ? i0 : I - 1;
+  const int ib = i0c / kScaleBlock, iu = (I + i0c) / kScaleBlock;
 #pragma unroll
   for (int m = 0; m < MCH; ++m) {
     const int c = gl + LPR * m;
     const int cb = (c < NC ? c : NC - 1) / 8;
     bg[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)ib * w13.srow + cb);
-    bu[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)(I / kScaleBlock + ib) * w13.srow + cb);
+    bu[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)iu * w13.srow + cb);
   }
   // Every read is unconditional (rows past I and chunks past NC read in-bounds neighbours whose
   // results are dropped), so the compiler can count them exactly and wait only at first use.

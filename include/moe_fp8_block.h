@@ -158,7 +158,9 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  *           aligned.
  *   ids_out [T, top_k] int32 and weights_out [T, top_k] float: the routing, or NULL.
  *   opts    host, NULL = defaults; info host, NULL = not reported.
- * H and I must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise). Every pointer the
+ * H and I must be multiples of 16 (MOE_ERR_UNSUPPORTED otherwise); a last 128-wide scale
+ * block may be partial. Scale blocks tile the stored rows, so w13's up row I+i takes block
+ * (I+i)/128. The MFMA path needs multiples of 128 and is not chosen otherwise. Every pointer the
  * chosen path reads must be non-NULL. T = 0 is a no-op (info still filled).
  * The W8A16 paths (GATHER, STREAM) decode weights exactly and accumulate in float. MFMA
  * quantises x per token and h per (token, slot) row to e4m3 with scale amax/448 (float

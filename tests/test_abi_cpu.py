@@ -130,7 +130,7 @@ def test_forward_rejects_bad_arguments(lib):
     assert _forward(lib, k=9)[0] == -1
     assert _forward(lib, E=2000)[0] == -1
     assert _forward(lib, H=200)[0] == -2
-    assert _forward(lib, I=192)[0] == -2
+    assert _forward(lib, I=200)[0] == -2
     assert _forward(lib, out_dtype=5)[0] == -1
     assert _forward(lib, hidden=None)[0] == -1
     assert _forward(lib, w13=_bank(256, 256, codes=None))[0] == -1
@@ -156,6 +156,18 @@ def test_forward_rejects_misalignment(lib):
     assert _forward(lib, w13=_bank(256, 256, expert_stride_bytes=256 * 256 + 8))[0] == -4
     assert _forward(lib, hidden=ctypes.c_void_p(0x10002))[0] == -4
     assert _forward(lib, workspace=ctypes.c_void_p(0x10010))[0] == -4
+
+
+def test_partial_scale_blocks_are_accepted(lib):
+    """H and I need only be multiples of 16 (a last 128-wide scale block may be partial); the
+    call then gets as far as the workspace check."""
+    st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), ws_bytes=16)
+    assert st == -5 and "workspace" in msg
+    o = L.Opts()
+    lib.moe_fp8_block_default_opts(ctypes.byref(o))
+    o.force_path = 3  # MFMA needs whole 128-wide blocks
+    st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), opts=o)
+    assert st == -2 and "MFMA" in msg
 
 
 def test_forward_rejects_small_workspace(lib):

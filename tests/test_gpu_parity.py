@@ -213,6 +213,20 @@ def test_odd_shapes_forced(path, H, I):
     check_out(out, oracle_out(c, act_mode=act), act, f"{path} H={H} I={I}")
 
 
+@pytest.mark.parametrize("path", [None, "gather", "stream"])
+@pytest.mark.parametrize("H,I,T", [(144, 80, 1), (144, 80, 3), (2064, 528, 1), (2064, 528, 40)])
+def test_partial_scale_blocks(path, H, I, T):
+    """H and I that are multiples of 16 but not of 128: every row ends in a partial scale
+    block, and w13's up rows start inside a block (blocks tile the stored rows). The gate
+    never picks MFMA for them."""
+    c = W.make_case("decode", T=T, seed=31, device=DEV, E=16, H=H, I=I, top_k=4)
+    say("partial blocks", path, H, I, T)
+    kw = {} if path is None else {"force_path": PATHS[path]}
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, **kw)
+    assert info["path"] == (path or info["path"]) and info["path"] != "mfma"
+    check_out(out, oracle_out(c), 0, f"{info['path']} H={H} I={I} T={T}")
+
+
 @pytest.mark.parametrize("T,path", [(1, None), (16, None), (16, "stream")])
 def test_large_expert_workload(T, path):
     """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest

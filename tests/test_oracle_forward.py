@@ -131,6 +131,17 @@ def test_forward_matches_scalar_loops(scale_dtype):
     assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("scale_dtype", [torch.float32, torch.bfloat16])
+def test_forward_matches_scalar_loops_partial_blocks(scale_dtype):
+    """H=144 and I=80 leave the last 128-wide scale block of every row and column partial,
+    and put w13's up rows 80..159 across its two row blocks (blocks tile the stored rows)."""
+    c = W.make_case("tiny", T=2, seed=5, E=4, H=144, I=80, top_k=2, scale_dtype=scale_dtype, pad="slab16")
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    ref = brute_forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 @pytest.mark.parametrize("act_mode", [0, 1])
 def test_dense_equals_gathered(act_mode):
     c = W.make_case("tiny", T=5, seed=7)
