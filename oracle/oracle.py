@@ -11,7 +11,9 @@ pairs, and a second, dense all-experts loop. Nothing is blocked, fused or reorde
 Sources (the three pages; each function names the passage it follows):
   [gather] gaudi-cookbook, fixes page "fp8-moe-gather": sections Problem, The fix.
   [tpu]    tpu-inference PR #3040 "Add another fused EP MoE kernels": review of the w1
-           weight/scale DMA (gate half first, up half second).
+           weight/scale DMA (gate half first, up half second) and of the w1 bias DMA (the
+           gate and up halves of the MLP bias come from their own offsets; the w2 bias is
+           added after the down projection).
   [cpu]    FreeToken PR #662 "serve block-fp8 experts on the cpu and hybrid backends": the
            PR body (bank format, e4m3 exactness), commit "honor padded fp8 scale strides",
            commit "add float64 parity reference", the final description (Kernels).
@@ -26,9 +28,10 @@ Pins (tests/test_oracle_*.py, run without a GPU):
                     with unit scales give exact small integers; a pure-Python scalar loop.
   route             brute-force sort by (-logit, id); k=E gives the full softmax.
   sort_pairs        brute-force stable counting sort.
-  forward           pure-Python scalar loops on tiny shapes; dense == gathered;
-                    unrouted experts contribute exactly zero; E=1,k=1 is a textbook SwiGLU
-                    FFN (torch); expert permutation and token independence invariants.
+  forward           pure-Python scalar loops on tiny shapes (also with partial scale blocks
+                    and with MLP biases); dense == gathered; unrouted experts contribute
+                    exactly zero; E=1,k=1 is a textbook SwiGLU FFN (torch), with and
+                    without biases; expert permutation and token independence invariants.
   w8a8 flags        parity unpinned beyond the self-consistency checks: the ambiguity
                     window is an analysis bound (documented), not a value the pages give.
 """
@@ -229,12 +232,22 @@ def _silu_grad(g):
 
 # ----------------------------------------------------------------------------- forward
 
+def expert_bias(bank: dict, e: int) -> np.ndarray:
+    """Bias row of expert e as float64 [N], zeros if the bank has none. Rows follow the
+    codes' rows, so w13's bias holds the gate half 0..I-1 then the up half I..2I-1
+    ([tpu] review of the w1 bias DMA: each half must come from its own offset)."""
+    b = bank.get("bias")
+    if b is None:
+        return np.zeros(bank["N"], dtype=np.float64)
+    return np.asarray(b, dtype=np.float64).reshape(bank["E"], bank["N"])[e]
+
+
 def _expert_cache(w13: dict, w2: dict):
     cache = {}
 
     def get(e):
         if e not in cache:
-            cache[e] = (dequant_expert(w13, e), dequant_expert(w2, e))
+            cache[e] = (dequant_expert(w13, e), dequant_expert(w2, e), expert_bias(w13, e), expert_bias(w2, e))
         return cache[e]
     return get
 
@@ -261,21 +274,25 @@ def h_drift(W13, xrow, g, u, h):
     return SAFETY * U32 * (math.sqrt(K) * (dg + du) + 16.0 * np.abs(h))
 
 
-def _expert_mlp(W13, W2, xrow, act_mode: int):
-    """One (token, expert) pair: a = W13 x, h = silu(a[:I]) * a[I:], y = W2 h.
+def _expert_mlp(W13, W2, xrow, act_mode: int, b13=None, b2=None):
+    """One (token, expert) pair: a = W13 x + b13, h = silu(a[:I]) * a[I:], y = W2 h + b2.
 
     Gate rows are 0..I-1 and up rows I..2I-1 ([tpu] review of the w1 DMA: gate half
-    first, up half second). act_mode 1 re-quantises h per pair before the down GEMM and
+    first, up half second); the optional MLP biases follow the same rows ([tpu] review of
+    the w1 bias DMA). act_mode 1 re-quantises h per pair before the down GEMM and
     flags the elements of h whose rounding an fp32 evaluation could decide either way:
     |v - midpoint| <= drift(h_i)/s + |v| * drift(h_r)/amax, where r is the row's argmax
     (the second term is the scale moving with amax).
     """
     I = W13.shape[0] // 2
     a = W13 @ xrow
+    if b13 is not None:
+        a = a + b13
     g, u = a[:I], a[I:]
     h = silu(g) * u
+    zb = 0.0 if b2 is None else b2
     if act_mode == 0:
-        return W2 @ h, None
+        return W2 @ h + zb, None
     h32 = h.astype(np.float32)
     q, s = quantize_rows(h32[None, :])
     q, s = q[0], s[0]
@@ -288,7 +305,7 @@ def _expert_mlp(W13, W2, xrow, act_mode: int):
     rho = d / float(s) + (np.abs(v) * d[r] / amax if amax > 0 else 0.0)
     flags = dist <= rho
     extra = dict(h_codes=q, h_scale=s, flags=flags, step=step)
-    return W2 @ h_deq, extra
+    return W2 @ h_deq + zb, extra
 
 
 def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
@@ -322,8 +339,8 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     for t in range(T):
         for j in range(top_k):
             e = int(ids[t, j])
-            W13, W2 = get(e)
-            y, extra = _expert_mlp(W13, W2, x_used[t], act_mode)
+            W13, W2, b13, b2 = get(e)
+            y, extra = _expert_mlp(W13, W2, x_used[t], act_mode, b13, b2)
             out[t] += w[t, j] * y
             if extra is not None:
                 f = extra["flags"]
@@ -363,8 +380,9 @@ def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode
     out = np.zeros((T, H), dtype=np.float64)
     for e in range(E):
         W13, W2 = dequant_expert(w13, e), dequant_expert(w2, e)
+        b13, b2 = expert_bias(w13, e), expert_bias(w2, e)
         for t in range(T):
-            y, _ = _expert_mlp(W13, W2, x_used[t], act_mode)
+            y, _ = _expert_mlp(W13, W2, x_used[t], act_mode, b13, b2)
             out[t] += C[t, e] * y
     return out
 

@@ -47,6 +47,10 @@ def brute_forward(hidden_bits, logits, w13, w2, k):
         c = int(bank["codes"][e * bank["expert_stride_bytes"] + n * bank["K"] + kk])
         return tab[c] * scale_of(bank, e, n, kk)
 
+    def bias(bank, e, n):  # MLP bias, flat [E*N] in the codes' row order, or none
+        b = bank.get("bias")
+        return 0.0 if b is None else float(np.asarray(b).reshape(-1)[e * bank["N"] + n])
+
     I = w13["N"] // 2
     out = [[0.0] * H for _ in range(T)]
     for t in range(T):
@@ -57,19 +61,19 @@ def brute_forward(hidden_bits, logits, w13, w2, k):
                 acc = 0.0
                 for kk in range(H):
                     acc += weight(w13, e, n, kk) * x[t][kk]
-                a.append(acc)
+                a.append(acc + bias(w13, e, n))
             h = [a[i] / (1.0 + math.exp(-a[i])) * a[I + i] for i in range(I)]
             for n in range(H):
                 acc = 0.0
                 for i in range(I):
                     acc += weight(w2, e, n, i) * h[i]
-                out[t][n] += wt * acc
+                out[t][n] += wt * (acc + bias(w2, e, n))
     return np.array(out)
 
 
-def _tiny_case(T=2, E=4, top_k=2, scale_dtype=torch.float32, seed=1, pad="none"):
+def _tiny_case(T=2, E=4, top_k=2, scale_dtype=torch.float32, seed=1, pad="none", bias_std=None):
     return W.make_case("tiny", T=T, seed=seed, E=E, H=256, I=128, top_k=top_k,
-                       scale_dtype=scale_dtype, pad=pad)
+                       scale_dtype=scale_dtype, pad=pad, bias_std=bias_std)
 
 
 def test_route_matches_bruteforce_with_ties():
@@ -131,6 +135,14 @@ def test_forward_matches_scalar_loops(scale_dtype):
     assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+def test_forward_matches_scalar_loops_with_biases():
+    c = _tiny_case(scale_dtype=torch.bfloat16, bias_std=0.5)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    ref = brute_forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 @pytest.mark.parametrize("scale_dtype", [torch.float32, torch.bfloat16])
 def test_forward_matches_scalar_loops_partial_blocks(scale_dtype):
     """H=144 and I=80 leave the last 128-wide scale block of every row and column partial,
@@ -169,9 +181,11 @@ def test_unrouted_experts_contribute_nothing():
     assert np.array_equal(base["out"], again["out"])
 
 
-def test_single_expert_is_swiglu():
-    """E=1, k=1: out = W2 (silu(Wg x) * (Wu x)), with torch doing dequant and products."""
-    c = _tiny_case(T=3, E=1, top_k=1, scale_dtype=torch.bfloat16)
+@pytest.mark.parametrize("bias_std", [None, 0.5])
+def test_single_expert_is_swiglu(bias_std):
+    """E=1, k=1: out = W2 (silu(Wg x + bg) * (Wu x + bu)) + b2, with torch doing dequant
+    and products (biases zero when absent)."""
+    c = _tiny_case(T=3, E=1, top_k=1, scale_dtype=torch.bfloat16, bias_std=bias_std)
     n = case_numpy(c)
     res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], 1)
 
@@ -185,9 +199,11 @@ def test_single_expert_is_swiglu():
     W13, W2 = deq(c.w13), deq(c.w2)
     x = c.hidden.to(torch.float64)
     I = c.I
-    g = x @ W13[:I].T
-    u = x @ W13[I:].T
-    y = (torch.nn.functional.silu(g) * u) @ W2.T
+    b13 = torch.zeros(2 * I, dtype=torch.float64) if c.w13.bias is None else c.w13.bias[0].to(torch.float64)
+    b2 = torch.zeros(c.H, dtype=torch.float64) if c.w2.bias is None else c.w2.bias[0].to(torch.float64)
+    g = x @ W13[:I].T + b13[:I]
+    u = x @ W13[I:].T + b13[I:]
+    y = (torch.nn.functional.silu(g) * u) @ W2.T + b2
     assert np.max(np.abs(res["out"] - y.numpy())) <= 1e-12 * float(y.abs().max())
     assert np.all(res["w"] == 1.0)
 

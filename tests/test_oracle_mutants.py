@@ -25,7 +25,9 @@ PINS = [
     PF.test_route_is_renormalised_full_softmax,
     PF.test_sort_pairs_bruteforce,
     lambda: PF.test_forward_matches_scalar_loops(torch.float32),
-    PF.test_single_expert_is_swiglu,
+    PF.test_forward_matches_scalar_loops_with_biases,
+    lambda: PF.test_single_expert_is_swiglu(None),
+    lambda: PF.test_single_expert_is_swiglu(0.5),
     PF.test_w8a8_matches_torch_quantised_reference,
 ]
 
@@ -40,17 +42,28 @@ def _failures():
     return n
 
 
-def _mlp_swapped(W13, W2, xrow, act_mode):
+def _mlp_swapped(W13, W2, xrow, act_mode, b13=None, b2=None):
     I = W13.shape[0] // 2
-    a = W13 @ xrow
+    a = W13 @ xrow + (0.0 if b13 is None else b13)
     g, u = a[I:], a[:I]
-    return W2 @ (OO.silu(g) * u), None
+    return W2 @ (OO.silu(g) * u) + (0.0 if b2 is None else b2), None
 
 
-def _mlp_no_silu(W13, W2, xrow, act_mode):
+def _mlp_no_silu(W13, W2, xrow, act_mode, b13=None, b2=None):
     I = W13.shape[0] // 2
-    a = W13 @ xrow
-    return W2 @ (a[:I] * a[I:]), None
+    a = W13 @ xrow + (0.0 if b13 is None else b13)
+    return W2 @ (a[:I] * a[I:]) + (0.0 if b2 is None else b2), None
+
+
+def _bias_halves_swapped(bank, e):
+    """The bias analogue of loading the next gate slice where the up bias belongs."""
+    b = OO.__dict__["_orig_expert_bias"](bank, e)
+    n = b.shape[0] // 2
+    return np.concatenate([b[n:], b[:n]])
+
+
+def _bias_dropped(bank, e):
+    return np.zeros(bank["N"], dtype=np.float64)
 
 
 def _scales_transposed(bank, e):
@@ -117,6 +130,8 @@ MUTANTS = {
     "weights_not_renormalised": ("route", _route_not_renormalised),
     "encode_ties_away": ("e4m3_encode", _encode_ties_away),
     "bf16_decode_shift": ("bf16_to_f64", _bf16_wrong_shift),
+    "bias_halves_swapped": ("expert_bias", _bias_halves_swapped),
+    "bias_dropped": ("expert_bias", _bias_dropped),
 }
 
 
@@ -128,6 +143,7 @@ def test_unmutated_oracle_passes_every_pin():
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(OO, "_orig_route", OO.route, raising=False)
+    monkeypatch.setattr(OO, "_orig_expert_bias", OO.expert_bias, raising=False)
     monkeypatch.setattr(OO, attr, fn)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, fn)

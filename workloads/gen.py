@@ -49,6 +49,7 @@ _BANK_FAMILY = {"tiny": 1, "decode": 2, "sweep": 2, "prefill": 2, "large": 3}
 
 # tensor ids mixed into the seeds
 _TID_W13, _TID_W2, _TID_HIDDEN, _TID_LOGITS, _TID_PERM = 1, 2, 3, 4, 5
+_TID_BIAS = 6  # added to a bank's tensor id for its MLP bias
 
 
 def _seed(*parts: int) -> int:
@@ -109,6 +110,7 @@ class FP8Bank:
     expert_stride_bytes: int
     scale_row_stride: int
     scale_expert_stride: int
+    bias: Optional[torch.Tensor] = None  # float32 [E, N] MLP bias (rows as the codes' rows), or None
 
     @property
     def scale_dtype(self) -> str:
@@ -129,7 +131,8 @@ class FP8Bank:
         return self.N * self.K + self.scale_rows * self.scale_cols * esz
 
     def to(self, device) -> "FP8Bank":
-        return dataclasses.replace(self, codes=self.codes.to(device), scales=self.scales.to(device))
+        return dataclasses.replace(self, codes=self.codes.to(device), scales=self.scales.to(device),
+                                   bias=None if self.bias is None else self.bias.to(device))
 
     def numpy(self) -> dict:
         """Host arrays for the oracle: codes uint8, scales as uint16 bf16 bits or float32."""
@@ -148,6 +151,7 @@ class FP8Bank:
             expert_stride_bytes=self.expert_stride_bytes,
             scale_row_stride=self.scale_row_stride,
             scale_expert_stride=self.scale_expert_stride,
+            bias=None if self.bias is None else self.bias.cpu().numpy(),
         )
 
 
@@ -166,6 +170,7 @@ def make_bank(
     pad_fill: float = float("nan"),
     std: float = 0.02,
     experts=None,
+    bias_std: Optional[float] = None,
 ) -> FP8Bank:
     """Draw an fp8 block bank expert by expert.
 
@@ -175,7 +180,8 @@ def make_bank(
     Scale padding holds ``pad_fill`` (NaN by default, so a reader of padding sees it);
     ``code_pad_bytes`` of 0x7F (NaN codes) follow each expert's codes. With ``experts``
     only those experts are drawn; the others keep NaN codes and NaN scales, so any read
-    of an expert that should not be read poisons the result.
+    of an expert that should not be read poisons the result. With ``bias_std`` each expert
+    also gets a float32 MLP bias row drawn from N(0, bias_std) (NaN for undrawn experts).
     """
     esz = 2 if scale_dtype == torch.bfloat16 else 4
     rows, cols = -(-N // BLOCK), -(-K // BLOCK)
@@ -208,6 +214,12 @@ def make_bank(
             scales[e, :, :cols] = s
         else:
             raise ValueError(f"unknown bank kind {kind!r}")
+    bias = None
+    if bias_std is not None:
+        bias = torch.full((E, N), float("nan"), dtype=torch.float32, device=device)
+        for e in range(E) if experts is None else sorted(set(int(x) for x in experts)):
+            g = _gen(device, seed, tensor_id + _TID_BIAS, e)
+            bias[e] = torch.randn((N,), generator=g, device=device, dtype=torch.float32) * bias_std
     return FP8Bank(
         codes=codes.reshape(-1),
         scales=scales.reshape(-1),
@@ -217,6 +229,7 @@ def make_bank(
         expert_stride_bytes=estride,
         scale_row_stride=rstride,
         scale_expert_stride=sstride,
+        bias=bias,
     )
 
 
@@ -277,7 +290,7 @@ class MoECase:
 
 def make_banks(name: str, seed: int, device="cpu", *, E: Optional[int] = None, H: Optional[int] = None,
                I: Optional[int] = None, pad: Optional[str] = None, code_pad_bytes: int = 0,
-               scale_dtype: Optional[torch.dtype] = None, experts=None) -> tuple:
+               scale_dtype: Optional[torch.dtype] = None, experts=None, bias_std: Optional[float] = None) -> tuple:
     """The (w13, w2) banks of a workload; shapes may be overridden for tests."""
     shp = dict(SHAPES[name])
     E = E or shp["E"]
@@ -296,9 +309,11 @@ def make_banks(name: str, seed: int, device="cpu", *, E: Optional[int] = None, H
     # the decode, sweep and prefill workloads share one set of banks
     bank_seed = _seed(seed, _BANK_FAMILY[name])
     w13 = make_bank(E, 2 * I, H, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
-                    tensor_id=_TID_W13, device=device, code_pad_bytes=code_pad_bytes, experts=experts)
+                    tensor_id=_TID_W13, device=device, code_pad_bytes=code_pad_bytes, experts=experts,
+                    bias_std=bias_std)
     w2 = make_bank(E, H, I, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
-                   tensor_id=_TID_W2, device=device, code_pad_bytes=code_pad_bytes, experts=experts)
+                   tensor_id=_TID_W2, device=device, code_pad_bytes=code_pad_bytes, experts=experts,
+                   bias_std=bias_std)
     return w13, w2
 
 
