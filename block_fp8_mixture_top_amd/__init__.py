@@ -88,7 +88,8 @@ def select_path(T: int, E: int, top_k: int, **opts) -> dict:
 
 
 def bank_struct(bank) -> L.Bank:
-    """A moe_fp8_bank from an object with codes/scales tensors and the stride fields."""
+    """A moe_fp8_bank from an object with codes/scales tensors, the stride fields and an
+    optional float32 [E, N] MLP bias (``bias``, None for none)."""
     _need(bank.codes, "bank.codes", torch.uint8)
     if bank.scales.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("bank.scales must be bfloat16 or float32")
@@ -102,6 +103,10 @@ def bank_struct(bank) -> L.Bank:
     b.reserved = 0
     b.scale_row_stride = int(bank.scale_row_stride)
     b.scale_expert_stride = int(bank.scale_expert_stride)
+    bias = getattr(bank, "bias", None)
+    if bias is not None:
+        _need(bias, "bank.bias", torch.float32, bank.codes.device)
+        b.bias = bias.data_ptr()
     return b
 
 

@@ -8,7 +8,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8_block.so")
 
-ABI_VERSION = 1  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 2  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
 
 MOE_OK = 0
 STATUS_NAMES = {
@@ -49,6 +49,7 @@ class Bank(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("scale_row_stride", ctypes.c_int64),
         ("scale_expert_stride", ctypes.c_int64),
+        ("bias", ctypes.c_void_p),
     ]
 
 

@@ -156,6 +156,7 @@ int check_bank(const moe_fp8_bank* b, const char* name, int E, int64_t N, int64_
     return fail(MOE_ERR_ARG, "%s.scale_dtype %d is not MOE_F32/MOE_BF16", name, b->scale_dtype);
   if (b->reserved != 0) return fail(MOE_ERR_ARG, "%s.reserved must be 0", name);
   if (!aligned16(b->codes)) return fail(MOE_ERR_ALIGN, "%s.codes must be 16-byte aligned", name);
+  if (!aligned16(b->bias)) return fail(MOE_ERR_ALIGN, "%s.bias must be 16-byte aligned", name);
   if (b->expert_stride_bytes % 16 != 0)
     return fail(MOE_ERR_ALIGN, "%s.expert_stride_bytes must be a multiple of 16 (got %lld)", name,
                 (long long)b->expert_stride_bytes);
@@ -182,6 +183,7 @@ moe::BankArg bank_arg(const moe_fp8_bank* b) {
   a.scale_bf16 = b->scale_dtype == MOE_BF16;
   a.srow = b->scale_row_stride;
   a.sexp = b->scale_expert_stride;
+  a.bias = b->bias;
   return a;
 }
 
@@ -401,7 +403,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     _Float16* y16 = at<_Float16>(workspace, L.y);
     int8_t* yexp = at<int8_t>(workspace, L.yexp);
     RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
-    RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, w, T, H, top_k, out, out_bf16, s), "combine launch");
+    RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, w, ids, b2.bias, T, H, top_k, out, out_bf16, s), "combine launch");
   }
   if (info) info->kernels = R.n;
   return ok();

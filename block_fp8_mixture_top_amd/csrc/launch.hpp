@@ -46,6 +46,7 @@ struct BankArg {
   int scale_bf16;
   int64_t srow;  // scale row stride, elements
   int64_t sexp;  // scale expert stride, elements
+  const float* bias;  // [E, N] MLP bias in the codes' row order, or nullptr
 };
 
 // Sorted routing produced by the sort and read by the GEMMs.
@@ -119,9 +120,10 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* co
 // atomics; the combine applies the weights).
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
-// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^yexp[t*k + j, n/64], slots summed in order.
-hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, int T, int H, int k, void* out,
-                              int out_bf16, hipStream_t s);
+// out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/64] + bias[ids[t*k + j], n]),
+// slots summed in order; bias may be nullptr (no w2 bias).
+hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
+                              const float* bias, int T, int H, int k, void* out, int out_bf16, hipStream_t s);
 
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);

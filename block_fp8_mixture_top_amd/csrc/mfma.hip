@@ -114,9 +114,14 @@ __device__ __forceinline__ int y_exponent(uint32_t m) {
 // out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/64], slots in order; eight
 // consecutive outputs (within one exponent group) per thread, read as one 16-byte load per
 // slot, the slots' reads unrolled so several are in flight.
+// BIAS: each pair's y also gets its expert's w2 bias (ids give the expert) before the router
+// weight is applied.
+template <bool BIAS>
 __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __restrict__ y,
                                                           const int8_t* __restrict__ yexp,
-                                                          const float* __restrict__ w, int T, int H, int k,
+                                                          const float* __restrict__ w,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ bias, int T, int H, int k,
                                                           void* __restrict__ out, int out_bf16) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
@@ -129,8 +134,16 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __rest
     const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / 64) + n / 64]) << 23);  // 2^e
     const float wj = w[p];
     const h8 v = *(const h8*)(y + p * H + n);
+    if constexpr (BIAS) {
+      const float* b = bias + (size_t)ids[p] * H + n;
+      const f32x4 b0 = *(const f32x4*)b, b1 = *(const f32x4*)(b + 4);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, (float)v[q] * up, s[q]);
+      for (int q = 0; q < 8; ++q)
+        s[q] = __builtin_fmaf(wj, __builtin_fmaf((float)v[q], up, q < 4 ? b0[q] : b1[q - 4]), s[q]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, (float)v[q] * up, s[q]);
+    }
   }
   if (out_bf16) {
     uint32_t o[4];
@@ -421,6 +434,17 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     step(kb, o0, o1);
     if (kb + 1 < nkb) step(kb + 1, o1, o0);
   }
+  // the MLP bias of this lane's gate and up features (w13's bias: gate half, then up half);
+  // without a bias the reads go to an in-bounds address and are dropped
+  const bool hb = w13.bias != nullptr;
+  const float* bb = hb ? w13.bias + (size_t)e * 2 * I : (const float*)w13.codes;
+  f32x4 bgv[2], buv[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;
+    bgv[f] = *(const f32x4*)(bb + (hb ? i : 0));
+    buv[f] = *(const f32x4*)(bb + (hb ? I + i : 0));
+  }
   // h of gate tile f (features fb*128 + 32fq + 16f + 4kq .. +3) for token 64th + 16tt + r16
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
@@ -432,8 +456,12 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
       const float gs = s_last[0] * xsc[tt], us = s_last[1] * xsc[tt];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float g = acc[f][tt][q] * gs;
-        const float u = acc[f + 2][tt][q] * us;
+        float g = acc[f][tt][q] * gs;
+        float u = acc[f + 2][tt][q] * us;
+        if (hb) {
+          g += bgv[f][q];
+          u += buv[f][q];
+        }
         h[q] = silu_fast(g) * u;
       }
       *(f32x4*)(hf + (size_t)pos * I + fb * 128 + fq * 32 + f * 16 + kq * 4) = h;
@@ -635,11 +663,15 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* co
   return hipGetLastError();
 }
 
-hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, int T, int H, int k, void* out,
-                              int out_bf16, hipStream_t s) {
+hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
+                              const float* bias, int T, int H, int k, void* out, int out_bf16, hipStream_t s) {
   const size_t n = (size_t)T * H / 8;
-  launch_kernel(combine_f16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, T, H, k, out,
-                out_bf16);
+  if (bias != nullptr)
+    launch_kernel(combine_f16_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, ids,
+                  bias, T, H, k, out, out_bf16);
+  else
+    launch_kernel(combine_f16_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, ids,
+                  bias, T, H, k, out, out_bf16);
   return hipGetLastError();
 }
 

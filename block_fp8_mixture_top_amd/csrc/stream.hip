@@ -171,6 +171,18 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     bg[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)ib * w13.srow + cb);
     bu[m] = load_scale_bits(w13.scales, w13.scale_bf16, sb + (int64_t)iu * w13.srow + cb);
   }
+  // The MLP bias of the gate and up rows (w13's bias holds the gate half, then the up half).
+  // Without a bias the reads go to an in-bounds address and are dropped, so no read sits in a
+  // branch.
+  const bool hb = w13.bias != nullptr;
+  const float* bb = hb ? w13.bias + (size_t)e * 2 * I : (const float*)w13.codes;
+  float bgr[RP], bur[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const int i = min(i0 + r, I - 1);
+    bgr[r] = bb[hb ? i : 0];
+    bur[r] = bb[hb ? I + i : 0];
+  }
   // Every read is unconditional (rows past I and chunks past NC read in-bounds neighbours whose
   // results are dropped), so the compiler can count them exactly and wait only at first use.
 #pragma unroll
@@ -235,6 +247,10 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       }
       g = group_sum<LPR>(g);
       u = group_sum<LPR>(u);
+      if (hb) {
+        g += bgr[r];
+        u += bur[r];
+      }
       const int i = i0 + r;
       if (gl == 0 && i < I) h[(size_t)p * I + i] = silu(g) * u;
     }
@@ -244,8 +260,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
 // Token-major GEMM2 with the combine. grid.x: tiles of ROWS output rows, grid.y: tokens.
 // The k*I/16 chunks of a token's (slot, chunk) space are spread over the workgroup's
 // threads (MC per thread); each thread keeps its h values and its slot's router weight in
-// registers and streams the matching 16 bytes of every output row.
-template <int MC, int ROWS>
+// registers and streams the matching 16 bytes of every output row. BIAS: the thread holding
+// chunk 0 of a slot also adds the router weight times that expert's w2 bias to each row.
+template <int MC, int ROWS, bool BIAS>
 __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __restrict__ h, BankArg w2,
                                                                 const int32_t* __restrict__ ids,
                                                                 const float* __restrict__ wts, int H, int I,
@@ -284,6 +301,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __r
                                (int64_t)ev[m] * w2.sexp + (int64_t)(n0 / kScaleBlock) * w2.srow + c / 8);
     wp[m] = w2.codes + (size_t)ev[m] * w2.expert_stride + (size_t)c * 16;
   }
+  float bv[BIAS ? MC : 1][ROWS];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) bv[m][r] = w2.bias[(size_t)ev[m] * H + (n0 + r < H ? n0 + r : H - 1)];
+  }
   u32x4 cw[ROWS][MC];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -314,6 +338,14 @@ __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __r
       // a chunk past F multiplies zero codes (a NaN code times a zero weight would not vanish)
       const u32x4 code = tid + kThreads * m < F ? cw[r][m] : u32x4{0, 0, 0, 0};
       acc = __builtin_fmaf(ws[m], dot16_f32(code, hv[m]), acc);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        const int f = tid + kThreads * m;
+        const float wb = f < F && f % CPR == 0 ? wv[m] : 0.0f;
+        acc = __builtin_fmaf(wb, bv[m][r], acc);
+      }
     }
     acc = wave_sum_dpp(acc);
     if (lane == 0) red[wave][r] = acc;
@@ -363,6 +395,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
 #pragma unroll
     for (int m = 0; m < MCH; ++m) cw[r][m] = ld16_stream(wb + (size_t)n * I + (size_t)min(gl + LPR * m, NC - 1) * 16);
   }
+  // the w2 bias of the RP rows, read unconditionally (dropped without a bias)
+  const bool hb = w2.bias != nullptr;
+  const float* bb = hb ? w2.bias + (size_t)e * H : (const float*)w2.codes;
+  float brow[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) brow[r] = bb[hb ? min(n0 + r, H - 1) : 0];
   float sw[MCH];
 #pragma unroll
   for (int m = 0; m < MCH; ++m) {
@@ -394,6 +432,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_expert_kernel(const float* __r
       for (int m = 0; m < MCH; ++m)
         if (gl + LPR * m < NC) acc = __builtin_fmaf(sw[m], dot16_f32(cw[r][m], hv[m]), acc);
       acc = group_sum<LPR>(acc);
+      if (hb) acc += brow[r];
       const int n = n0 + r;
       if (gl == 0 && n < H) y[(size_t)p * H + n] = acc;
     }
@@ -513,8 +552,12 @@ template <int MC, int ROWS>
 static hipError_t g2g(const float* h, const BankArg& w2, const int32_t* ids, const float* w, int T, int H, int I,
                       int k, void* out, int out_bf16, hipStream_t s) {
   dim3 grid((H + ROWS - 1) / ROWS, T);
-  launch_kernel((gemm2_gather_kernel<MC, ROWS>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
-                     out_bf16);
+  if (w2.bias != nullptr)
+    launch_kernel((gemm2_gather_kernel<MC, ROWS, true>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
+                  out_bf16);
+  else
+    launch_kernel((gemm2_gather_kernel<MC, ROWS, false>), grid, dim3(kThreads), 0, s, h, w2, ids, w, H, I, k, out,
+                  out_bf16);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
  *   route    top-k experts per token by router logit, weights = softmax over the selected
  *            logits (the full softmax renormalised over the top-k);
  *   gather   only the routed experts' weight bytes are read;
- *   GEMM1    a = W13[e] x, gate rows 0..I-1 and up rows I..2I-1, h = silu(gate) * up;
- *   GEMM2    y = W2[e] h;
+ *   GEMM1    a = W13[e] x (+ b13[e]), gate rows 0..I-1 and up rows I..2I-1,
+ *            h = silu(gate) * up;
+ *   GEMM2    y = W2[e] h (+ b2[e]);
  *   combine  out[t] = sum_j w[t,j] * y[t,j].
  *
  * Sources: gaudi-cookbook fixes page "fp8-moe-gather" (The fix: gather g = min(local
@@ -44,7 +45,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a struct, an enum or an entry point's meaning. */
-#define MOE_FP8_BLOCK_ABI_VERSION 1
+#define MOE_FP8_BLOCK_ABI_VERSION 2
 
 /* Limits checked on every call. */
 #define MOE_FP8_BLOCK_MAX_EXPERTS 1024
@@ -76,6 +77,10 @@ typedef enum {
  * The scale of block (n / 128, k / 128) of expert e is
  *   scales[e * scale_expert_stride + (n / 128) * scale_row_stride + k / 128]
  * and multiplies the decoded code. Strides may include padding, which is never read.
+ * An optional MLP bias adds bias[e * N + n] to row n of expert e's product (tpu-inference
+ * PR #3040, review of the w1 bias DMA: the bias follows the weight rows, so w13's bias
+ * holds the gate half 0..I-1 and then the up half I..2I-1; w2's bias is added after the
+ * down projection, before the router weight is applied).
  */
 typedef struct {
   const uint8_t* codes;        /* device; 16-byte aligned */
@@ -85,6 +90,7 @@ typedef struct {
   int32_t reserved;            /* must be 0 */
   int64_t scale_row_stride;    /* elements, >= ceil(K/128) */
   int64_t scale_expert_stride; /* elements, >= (ceil(N/128)-1)*scale_row_stride + ceil(K/128) */
+  const float* bias;           /* device [E, N] float, 16-byte aligned, or NULL for no bias */
 } moe_fp8_bank;
 
 /* Host-side options; NULL means the defaults below. */
@@ -152,8 +158,10 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  * The whole expert computation.
  *   hidden  [T, H] bf16 (uint16 bits), 16-byte aligned.
  *   logits  [T, E] float.
- *   w13     bank with N = 2I, K = H (gate rows 0..I-1, up rows I..2I-1).
- *   w2      bank with N = H, K = I.
+ *   w13     bank with N = 2I, K = H (gate rows 0..I-1, up rows I..2I-1). With a bias,
+ *           gate = W_gate x + b13[e, 0..I-1] and up = W_up x + b13[e, I..2I-1].
+ *   w2      bank with N = H, K = I. With a bias, y = W2 h + b2[e] for each (token, slot)
+ *           pair before the router weight multiplies it.
  *   out     [T, H], out_dtype float or bf16 (round to nearest even from float), 16-byte
  *           aligned.
  *   ids_out [T, top_k] int32 and weights_out [T, top_k] float: the routing, or NULL.

@@ -90,5 +90,6 @@ def bank_numpy(bank, experts=None) -> dict:
         scales = bank.scales.cpu().numpy()
     d = dict(codes=codes, scales=scales, scale_dtype=bank.scale_dtype, E=bank.E, N=bank.N, K=bank.K,
              expert_stride_bytes=st, scale_row_stride=bank.scale_row_stride,
-             scale_expert_stride=bank.scale_expert_stride)
+             scale_expert_stride=bank.scale_expert_stride,
+             bias=None if getattr(bank, "bias", None) is None else bank.bias.cpu().numpy())
     return d

@@ -156,6 +156,10 @@ def test_forward_rejects_misalignment(lib):
     assert _forward(lib, w13=_bank(256, 256, expert_stride_bytes=256 * 256 + 8))[0] == -4
     assert _forward(lib, hidden=ctypes.c_void_p(0x10002))[0] == -4
     assert _forward(lib, workspace=ctypes.c_void_p(0x10010))[0] == -4
+    st, msg, _ = _forward(lib, w2=_bank(256, 128, bias=0x30004))
+    assert st == -4 and "bias" in msg
+    # an aligned bias gets as far as the workspace check
+    assert _forward(lib, w13=_bank(256, 256, bias=0x30000), w2=_bank(256, 128, bias=0x40000), ws_bytes=16)[0] == -5
 
 
 def test_partial_scale_blocks_are_accepted(lib):

@@ -227,6 +227,50 @@ def test_partial_scale_blocks(path, H, I, T):
     check_out(out, oracle_out(c), 0, f"{info['path']} H={H} I={I} T={T}")
 
 
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_mlp_bias(path, T):
+    """Per-expert MLP biases on both banks (gate half then up half for w13, added after the
+    down projection for w2), on every path. Undrawn experts hold NaN biases, so a bias read
+    from the wrong expert poisons the output."""
+    c = W.make_case("decode", T=T, seed=51 + T, device=DEV, E=16, H=640, I=384, top_k=4, bias_std=0.3)
+    say("bias", path, T)
+    act = 1 if path == "mfma" else 0
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    assert info["path"] == path
+    check_out(out, oracle_out(c, act_mode=act), act, f"bias {path} T={T}")
+
+
+@pytest.mark.parametrize("path", ["gather", "stream"])
+def test_mlp_bias_partial_blocks(path):
+    """Biases with partial last scale blocks (H, I multiples of 16 only)."""
+    c = W.make_case("decode", T=5, seed=57, device=DEV, E=16, H=144, I=80, top_k=4, bias_std=0.3)
+    say("bias partial", path)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    check_out(out, oracle_out(c), 0, f"bias partial {path}")
+
+
+def test_mlp_bias_decode_and_prefill_sampled():
+    """Biases at the decode workload (GATHER, bf16 out) and at T=4096 (MFMA, sampled rows)."""
+    banks = W.make_banks("decode", seed=1, device=DEV, bias_std=0.02)
+    c = W.make_case("decode", T=1, seed=1, device=DEV, banks=banks)
+    say("bias decode")
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
+    assert info["path"] == "gather"
+    check_out(out, oracle_out(c), 0, "bias decode T=1")
+    c = W.make_case("prefill", T=4096, seed=6, device=DEV, banks=banks)
+    say("bias prefill")
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16, return_routing=True)
+    torch.cuda.synchronize()
+    assert info["path"] == "mfma"
+    rows = np.array([0, 1, 777, 4095])
+    res = oracle_out(c, rows=rows, act_mode=1)
+    assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
+    check_out(out[torch.from_numpy(rows).to(DEV)], res, 1, "bias prefill T=4096 sampled")
+
+
 @pytest.mark.parametrize("T,path", [(1, None), (16, None), (16, "stream")])
 def test_large_expert_workload(T, path):
     """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest
