@@ -24,6 +24,8 @@ Pins (tests/test_oracle_*.py, run without a GPU):
   e4m3_encode       vs torch's float8_e4m3fn cast on every midpoint +-1 ulp and at random;
                     saturation and signed zero by definition.
   quantize_rows     hand-checked rows (power-of-two amax, zero row).
+  quantize_groups   scalar loops with a brute-force nearest-code search per 128-column
+                    group; one group per row reduces to quantize_rows.
   dequant_expert    padded-stride invariance with NaN in the padding; power-of-two codes
                     with unit scales give exact small integers; a pure-Python scalar loop.
   route             brute-force sort by (-logit, id); k=E gives the full softmax.
@@ -31,7 +33,8 @@ Pins (tests/test_oracle_*.py, run without a GPU):
   forward           pure-Python scalar loops on tiny shapes (also with partial scale blocks
                     and with MLP biases); dense == gathered; unrouted experts contribute
                     exactly zero; E=1,k=1 is a textbook SwiGLU FFN (torch), with and
-                    without biases; expert permutation and token independence invariants.
+                    without biases; expert permutation and token independence invariants;
+                    act_mode 2 against scalar loops over group-dequantised activations.
   w8a8 flags        parity unpinned beyond the self-consistency checks: the ambiguity
                     window is an analysis bound (documented), not a value the pages give.
 """
@@ -219,6 +222,29 @@ def quantize_rows(x32):
     return e4m3_encode(v), s
 
 
+def quantize_groups(x32, group: int = BLOCK):
+    """Dynamic e4m3 per (row, group of `group` consecutive columns), emulated exactly in fp32.
+
+    Each group is quantised as its own row by quantize_rows: scale amax/448 over the
+    group's columns, codes e4m3_encode(x / scale). With the default group of 128 the
+    activation groups line up with the 128-wide K blocks of the weight scales, so one
+    activation scale and one weight scale apply to each 128-long piece of a dot product
+    ([gather] Who is affected: block-quantized FP8 checkpoints with dynamic activation
+    scales; The fix: up/gate as one native FP8 GEMM). Returns codes [R, C] and scales
+    [R, C // group].
+    """
+    x = np.asarray(x32, dtype=np.float32)
+    R, C = x.shape
+    assert C % group == 0, "columns must be a whole number of groups"
+    q, s = quantize_rows(x.reshape(R * (C // group), group))
+    return q.reshape(R, C), s.reshape(R, C // group)
+
+
+def dequant_groups(q, s, group: int = BLOCK) -> np.ndarray:
+    """LUT[code] * the scale of the code's group, float64."""
+    return _LUT[np.asarray(q)] * np.repeat(np.asarray(s, dtype=np.float64), group, axis=1)
+
+
 def silu(g):
     with np.errstate(over="ignore"):
         return g / (1.0 + np.exp(-g))
@@ -308,6 +334,22 @@ def _expert_mlp(W13, W2, xrow, act_mode: int, b13=None, b2=None):
     return W2 @ h_deq + zb, extra
 
 
+def _x_used(x, act_mode: int, res: dict):
+    """The activations the up/gate GEMM multiplies: x itself (act_mode 0), x quantised per
+    token (1) or per (token, 128-column group) (2), dequantised in float64."""
+    if act_mode == 0:
+        return x
+    if act_mode == 1:
+        xq, xs = quantize_rows(x.astype(np.float32))
+        res.update(x_codes=xq, x_scales=xs)
+        return _LUT[xq] * xs.astype(np.float64)[:, None]
+    if act_mode == 2:
+        xq, xs = quantize_groups(x.astype(np.float32))
+        res.update(x_codes=xq, x_scales=xs)
+        return dequant_groups(xq, xs)
+    raise ValueError(f"act_mode {act_mode}")
+
+
 def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
     """Gathered formulation: out[t] = sum_j w_tj * expert_{ids[t,j]}(x_t).
 
@@ -315,9 +357,12 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     K = H; w2: bank with N = H, K = I (dicts as produced by the generators' numpy()).
     act_mode 0 is W8A16 (x exact, h float64); act_mode 1 is W8A8: x quantised per token
     and h per pair, both in fp32 emulation ([gather] The fix: the routed experts are
-    gathered, up/gate run as one GEMM and the down projection follows).
-    Returns a dict with out (float64 [T, H]), routing, and for act_mode 1 the x and h
-    quantisation and the per-output allowance for ambiguous h roundings.
+    gathered, up/gate run as one GEMM and the down projection follows); act_mode 2 is
+    the gather variant of [gather] The fix: the up/gate GEMM on e4m3 activations quantised
+    per (token, 128-column group) and the down projection on h in full precision.
+    Returns a dict with out (float64 [T, H]), routing, the x quantisation for act_modes 1
+    and 2, and for act_mode 1 the h quantisation and the per-output allowance for
+    ambiguous h roundings.
     """
     x = bf16_to_f64(hidden_bf16)
     T, H = x.shape
@@ -325,12 +370,8 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     ids, w, w32 = route(logits, top_k)
     counts, offsets, sorted_pairs = sort_pairs(ids, E)
     res = dict(ids=ids, w=w, w32=w32, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
-    if act_mode == 1:
-        xq, xs = quantize_rows(x.astype(np.float32))
-        x_used = _LUT[xq] * xs.astype(np.float64)[:, None]
-        res.update(x_codes=xq, x_scales=xs)
-    else:
-        x_used = x
+    x_used = _x_used(x, act_mode, res)
+    h_mode = 1 if act_mode == 1 else 0  # only act_mode 1 re-quantises h
     get = _expert_cache(w13, w2)
     out = np.zeros((T, H), dtype=np.float64)
     allowance = np.zeros((T, H), dtype=np.float64)
@@ -340,7 +381,7 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
         for j in range(top_k):
             e = int(ids[t, j])
             W13, W2, b13, b2 = get(e)
-            y, extra = _expert_mlp(W13, W2, x_used[t], act_mode, b13, b2)
+            y, extra = _expert_mlp(W13, W2, x_used[t], h_mode, b13, b2)
             out[t] += w[t, j] * y
             if extra is not None:
                 f = extra["flags"]
@@ -372,17 +413,13 @@ def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode
     for t in range(T):
         for j in range(top_k):
             C[t, ids[t, j]] = w[t, j]
-    if act_mode == 1:
-        xq, xs = quantize_rows(x.astype(np.float32))
-        x_used = _LUT[xq] * xs.astype(np.float64)[:, None]
-    else:
-        x_used = x
+    x_used = _x_used(x, act_mode, {})
     out = np.zeros((T, H), dtype=np.float64)
     for e in range(E):
         W13, W2 = dequant_expert(w13, e), dequant_expert(w2, e)
         b13, b2 = expert_bias(w13, e), expert_bias(w2, e)
         for t in range(T):
-            y, _ = _expert_mlp(W13, W2, x_used[t], act_mode, b13, b2)
+            y, _ = _expert_mlp(W13, W2, x_used[t], 1 if act_mode == 1 else 0, b13, b2)
             out[t] += C[t, e] * y
     return out
 

@@ -30,10 +30,33 @@ def brute_route(logits_row, k):
     return order, [v / tot for v in ex]
 
 
-def brute_forward(hidden_bits, logits, w13, w2, k):
-    """Scalar loops: per-element decode (torch's float8 table), per-element scale lookup."""
+def brute_group_quant(x, group=128):
+    """Dequantised e4m3 activations per (row, group of 128 columns), by scalar loops: the
+    group's amax over 448 as the scale (fp32 division; 1 for an all-zero group), each
+    element divided by it in fp32 and then the nearest finite code found by searching all
+    of torch's float8 table (ties to the even code, magnitudes past 448 saturate)."""
     tab = torch_e4m3_table()
-    x = _bf16_to_float_list(hidden_bits)
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    T, C = x.shape
+    out = np.zeros((T, C))
+    for t in range(T):
+        for g0 in range(0, C, group):
+            amax = max(abs(float(v)) for v in x[t, g0:g0 + group])
+            s = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+            for c in range(g0, g0 + group):
+                q = float(np.float32(np.float32(x[t, c]) / s))
+                q = min(448.0, max(-448.0, q))
+                code = min(finite, key=lambda cc: (abs(tab[cc] - q), cc & 1))
+                out[t, c] = tab[code] * float(s)
+    return out
+
+
+def brute_forward(hidden_bits, logits, w13, w2, k, x=None):
+    """Scalar loops: per-element decode (torch's float8 table), per-element scale lookup.
+    ``x`` replaces the bf16 activations (e.g. by group-quantised ones)."""
+    tab = torch_e4m3_table()
+    if x is None:
+        x = _bf16_to_float_list(hidden_bits)
     T, H = x.shape
 
     def scale_of(bank, e, n, kk):
@@ -279,3 +302,37 @@ def test_w8a8_ambiguity_flags_are_rare_on_gaussian_banks():
     res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=1)
     assert res["n_flagged"] <= 0.01 * res["n_h"]
     assert np.all(res["allowance"] >= 0)
+
+
+def test_group_quantisation_matches_scalar_search():
+    """quantize_groups against a brute-force nearest-code search per 128-column group, on
+    rows with very different group magnitudes, a zero group and exact midpoints."""
+    g = np.random.default_rng(21)
+    x = (g.normal(0, 1, (3, 512)) * np.repeat(g.uniform(0.001, 50, (3, 4)), 128, axis=1)).astype(np.float32)
+    x[1, 128:256] = 0.0
+    x[2, :8] = [448.0, 416.0, 432.0, 3.375, -3.125, 0.0, -0.0, 1.0]  # midpoints: 432, 3.375, -3.125
+    q, s = O.quantize_groups(x)
+    assert q.shape == x.shape and s.shape == (3, 4)
+    assert s[1, 1] == 1.0
+    assert np.array_equal(O.dequant_groups(q, s), brute_group_quant(x))
+    # one group per row is the per-row quantiser
+    q1, s1 = O.quantize_groups(x, group=512)
+    qr, sr = O.quantize_rows(x)
+    assert np.array_equal(q1, qr) and np.array_equal(s1[:, 0], sr)
+
+
+def test_group_w8a8_forward_matches_scalar_loops():
+    """act_mode 2: the up/gate GEMM on group-quantised activations and the down projection
+    on h in full precision, against scalar loops over brute-force quantised activations."""
+    c = _tiny_case(scale_dtype=torch.bfloat16, seed=4, bias_std=0.25)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=2)
+    xq = brute_group_quant(_bf16_to_float_list(n["hidden"]).astype(np.float32))
+    ref = brute_forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, x=xq)
+    assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    dense = O.forward_dense(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=2)
+    assert np.max(np.abs(res["out"] - dense)) <= 1e-12 * np.max(np.abs(ref))
+    # the quantisation moves the output, but only by the activation rounding
+    plain = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k)["out"]
+    d = np.max(np.abs(plain - res["out"])) / np.max(np.abs(plain))
+    assert 1e-4 < d < 0.1

@@ -29,6 +29,7 @@ PINS = [
     lambda: PF.test_single_expert_is_swiglu(None),
     lambda: PF.test_single_expert_is_swiglu(0.5),
     PF.test_w8a8_matches_torch_quantised_reference,
+    PF.test_group_quantisation_matches_scalar_search,
 ]
 
 
@@ -121,6 +122,18 @@ def _bf16_wrong_shift(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def _groups_tiled(q, s, group=128):
+    """Group scales laid out group-major instead of each one over its own columns."""
+    return OO._LUT[np.asarray(q)] * np.tile(np.asarray(s, dtype=np.float64), group)
+
+
+def _groups_of_64(x32, group=128):
+    """Activation groups half as wide as the weight blocks."""
+    q, s = OO.quantize_rows(np.asarray(x32, np.float32).reshape(-1, 64))
+    R, C = np.asarray(x32).shape
+    return q.reshape(R, C), np.repeat(s.reshape(R, C // 64)[:, ::2], 1, axis=1)
+
+
 MUTANTS = {
     "gate_up_swapped": ("_expert_mlp", _mlp_swapped),
     "silu_dropped": ("_expert_mlp", _mlp_no_silu),
@@ -132,6 +145,8 @@ MUTANTS = {
     "bf16_decode_shift": ("bf16_to_f64", _bf16_wrong_shift),
     "bias_halves_swapped": ("expert_bias", _bias_halves_swapped),
     "bias_dropped": ("expert_bias", _bias_dropped),
+    "group_scales_tiled": ("dequant_groups", _groups_tiled),
+    "groups_of_64": ("quantize_groups", _groups_of_64),
 }
 
 
