@@ -15,6 +15,9 @@ import torch
 
 from . import _lib as L
 from ._lib import (  # noqa: F401
+    ACT_GROUP_FP8,
+    ACT_PATH,
+    ACT_ROW_FP8,
     MOE_BF16,
     MOE_F32,
     PATH_AUTO,
@@ -28,7 +31,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "abi_version", "lib", "make_opts", "select_path", "route_workspace_size", "route", "workspace_size",
     "forward", "quantize_rows", "decode_e4m3", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
-    "PATH_STREAM", "PATH_MFMA", "PATH_NAMES",
+    "PATH_STREAM", "PATH_MFMA", "PATH_NAMES", "ACT_PATH", "ACT_ROW_FP8", "ACT_GROUP_FP8",
 ]
 
 
@@ -62,9 +65,11 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
 
 
 def make_opts(force_path: Optional[int] = None, gate_ratio: Optional[float] = None,
-              mfma_min_tokens_per_expert: Optional[int] = None) -> L.Opts:
+              mfma_min_tokens_per_expert: Optional[int] = None, act_mode: Optional[int] = None) -> L.Opts:
     o = L.Opts()
     L.check(lib().moe_fp8_block_default_opts(ctypes.byref(o)))
+    if act_mode is not None:
+        o.act_mode = int(act_mode)
     if force_path is not None:
         o.force_path = int(force_path)
     if gate_ratio is not None:
@@ -149,7 +154,8 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out
     """The expert computation for T tokens. Returns (out [T, H], info dict).
 
     w13 / w2 are banks (objects with codes, scales, expert_stride_bytes, scale_row_stride,
-    scale_expert_stride); opts are force_path, gate_ratio, mfma_min_tokens_per_expert.
+    scale_expert_stride, optional bias); opts are force_path, gate_ratio,
+    mfma_min_tokens_per_expert and act_mode (ACT_PATH or ACT_GROUP_FP8).
     With return_routing the info dict also holds the ids and weights tensors.
     """
     _need(hidden, "hidden", torch.bfloat16)

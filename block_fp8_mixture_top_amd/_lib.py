@@ -23,6 +23,7 @@ STATUS_NAMES = {
 MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_STREAM, PATH_MFMA = 0, 1, 2, 3
 PATH_NAMES = {PATH_AUTO: "auto", PATH_GATHER: "gather", PATH_STREAM: "stream", PATH_MFMA: "mfma"}
+ACT_PATH, ACT_ROW_FP8, ACT_GROUP_FP8 = 0, 1, 2
 KERNEL_NAMES = {1: "route", 2: "sort", 3: "quant", 4: "hquant", 5: "gemm1", 6: "gemm2", 7: "combine"}
 EXPORTS = [
     "moe_fp8_block_abi_version",
@@ -58,7 +59,7 @@ class Opts(ctypes.Structure):
         ("gate_ratio", ctypes.c_float),
         ("force_path", ctypes.c_int32),
         ("mfma_min_tokens_per_expert", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("act_mode", ctypes.c_int32),
     ]
 
 

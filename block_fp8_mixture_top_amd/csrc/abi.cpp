@@ -55,7 +55,7 @@ moe_opts defaults() {
   o.gate_ratio = 2.0f;
   o.force_path = MOE_PATH_AUTO;
   o.mfma_min_tokens_per_expert = 2;
-  o.reserved = 0;
+  o.act_mode = MOE_ACT_PATH;
   return o;
 }
 
@@ -75,17 +75,26 @@ int check_opts(const moe_opts* o) {
   if (o->force_path < MOE_PATH_AUTO || o->force_path > MOE_PATH_MFMA)
     return fail(MOE_ERR_ARG, "force_path %d is not a moe_path", o->force_path);
   if (o->mfma_min_tokens_per_expert < 1) return fail(MOE_ERR_ARG, "mfma_min_tokens_per_expert must be >= 1");
-  if (o->reserved != 0) return fail(MOE_ERR_ARG, "moe_opts.reserved must be 0");
+  if (o->act_mode != MOE_ACT_PATH && o->act_mode != MOE_ACT_GROUP_FP8)
+    return fail(MOE_ERR_ARG, "act_mode %d is not MOE_ACT_PATH or MOE_ACT_GROUP_FP8", o->act_mode);
   return MOE_OK;
 }
 
 // The gate (gaudi-cookbook "fp8-moe-gather", The fix): gather while T*top_k <= ratio*E.
+// Group-wise e4m3 activations run on GATHER and STREAM only, so the gate never picks MFMA
+// for them.
 int gate(int T, int E, int top_k, const moe_opts& o) {
   if (o.force_path != MOE_PATH_AUTO) return o.force_path;
   const double P = (double)T * top_k;
   if (P <= (double)o.gate_ratio * E) return MOE_PATH_GATHER;
-  if (P >= (double)o.mfma_min_tokens_per_expert * E) return MOE_PATH_MFMA;
+  if (P >= (double)o.mfma_min_tokens_per_expert * E && o.act_mode != MOE_ACT_GROUP_FP8) return MOE_PATH_MFMA;
   return MOE_PATH_STREAM;
+}
+
+// Activation precision a path runs with (moe_run_info.act_mode).
+int act_of(int path, const moe_opts& o) {
+  if (path == MOE_PATH_MFMA) return MOE_ACT_ROW_FP8;
+  return o.act_mode == MOE_ACT_GROUP_FP8 ? MOE_ACT_GROUP_FP8 : MOE_ACT_PATH;
 }
 
 // Path actually run: the gate's choice, moved off a path the shapes do not fit only when
@@ -93,6 +102,12 @@ int gate(int T, int E, int top_k, const moe_opts& o) {
 int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* path) {
   int p = gate(T, E, top_k, o);
   const bool forced = o.force_path != MOE_PATH_AUTO;
+  if (o.act_mode == MOE_ACT_GROUP_FP8) {
+    if (p == MOE_PATH_MFMA)
+      return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 runs on GATHER and STREAM only, not on a forced MFMA");
+    if (H % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 needs H %% 128 == 0 (got H=%d)", H);
+  }
   if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
     if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
     p = MOE_PATH_STREAM;
@@ -121,7 +136,7 @@ struct Layout {
   size_t total;
 };
 
-Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
+Layout layout_for(int path, int act, int T, int E, int H, int I, int top_k) {
   Layout L{};
   Carve c;
   const size_t P = (size_t)T * top_k;
@@ -144,6 +159,10 @@ Layout layout_for(int path, int T, int E, int H, int I, int top_k) {
     L.xs = c.take((size_t)T * 4);
     L.hq = c.take(P * (size_t)I);
     L.hs = c.take(P * 4);
+  }
+  if (act == MOE_ACT_GROUP_FP8) {
+    L.xq = c.take((size_t)T * H);  // x codes and one scale per (token, 128 columns)
+    L.xs = c.take((size_t)T * (H / 128) * 4);
   }
   L.total = c.off;
   return L;
@@ -247,7 +266,7 @@ int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe
   if ((st = check_opts(&o))) return st;
   const int p = gate(T, E, top_k, o);
   info->path = p;
-  info->act_mode = p == MOE_PATH_MFMA ? 1 : 0;
+  info->act_mode = act_of(p, o);
   const int64_t P = (int64_t)T * top_k;
   info->slots = (int)(P < E ? P : E);
   info->kernels = 0;
@@ -304,7 +323,7 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
   if (check_opts(&o)) return 0;
   int path = 0;
   if (resolve_path(T, E, H, I, top_k, o, &path)) return 0;
-  return layout_for(path, T, E, H, I, top_k).total;
+  return layout_for(path, act_of(path, o), T, E, H, I, top_k).total;
 }
 
 }  // extern "C"
@@ -339,7 +358,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   const int64_t P = (int64_t)T * top_k;
   if (info) {
     info->path = path;
-    info->act_mode = path == MOE_PATH_MFMA ? 1 : 0;
+    info->act_mode = act_of(path, o);
     info->slots = (int)(P < E ? P : E);
     info->kernels = 0;
   }
@@ -347,7 +366,8 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   if (!hidden || !logits || !out) return fail(MOE_ERR_ARG, "hidden, logits and out must be non-NULL");
   if (!aligned16(hidden)) return fail(MOE_ERR_ALIGN, "hidden must be 16-byte aligned");
   if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out must be 16-byte aligned");
-  const Layout L = layout_for(path, T, E, H, I, top_k);
+  const int act_mode = act_of(path, o);
+  const Layout L = layout_for(path, act_mode, T, E, H, I, top_k);
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -368,7 +388,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   Runner R{s, events, n_events, kinds};
 
   // small gather batches route inside GEMM1; everything else routes and sorts first
-  const bool fused = path == MOE_PATH_GATHER && moe::gemm1_fused_route_ok(T, top_k);
+  const bool fused = path == MOE_PATH_GATHER && act_mode == MOE_ACT_PATH && moe::gemm1_fused_route_ok(T, top_k);
   const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
   if (!fused) {
     for (int st = 0; st < moe::route_kernel_count((int)P); ++st)
@@ -381,7 +401,15 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
 
   if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) {
     float* h = at<float>(workspace, L.h);
-    const moe::Gemm1Args g1{hidden, logits, T, E, H, I, top_k, slots, b13, plan, h, fused ? 1 : 0, ids, w};
+    moe::Gemm1Args g1{hidden, logits, T, E, H, I, top_k, slots, b13, plan, h, fused ? 1 : 0, ids, w};
+    if (act_mode == MOE_ACT_GROUP_FP8) {
+      // one quantisation row per (token, 128 columns)
+      g1.xq = at<uint8_t>(workspace, L.xq);
+      g1.xs = at<float>(workspace, L.xs);
+      RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T * (H / 128), 128, at<uint8_t>(workspace, L.xq),
+                                                   at<float>(workspace, L.xs), s),
+          "quant launch");
+    }
     RUN(MOE_K_GEMM1, moe::launch_gemm1_w8a16(g1, s), "gemm1 launch");
     if (path == MOE_PATH_GATHER) {
       RUN(MOE_K_GEMM2, moe::launch_gemm2_gather(h, b2, ids, w, T, H, I, top_k, out, out_bf16, s), "gemm2 launch");

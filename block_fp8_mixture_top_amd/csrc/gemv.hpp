@@ -26,6 +26,25 @@ __device__ __forceinline__ float dot16_bf16(const u32x4& c, const u32x4& x0, con
   return acc;
 }
 
+// sum_i dec(c_i) * dec(x_i) over 16 weight codes and 16 activation codes: both are widened
+// to bf16 exactly and each product of two e4m3 values (at most 8 significant bits) is exact
+// in the float dot.
+__device__ __forceinline__ float dot16_e4m3(const u32x4& c, const u32x4& x) {
+  float acc = 0.0f;
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2 clo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[q], 1.0f, false);
+    const bf16x2 chi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[q], 1.0f, true);
+    const bf16x2 xlo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xw[q], 1.0f, false);
+    const bf16x2 xhi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xw[q], 1.0f, true);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(clo, xlo, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(chi, xhi, acc, false);
+  }
+  return acc;
+}
+
 // sum_i dec(code_i) * v_i over 16 codes and 16 floats.
 __device__ __forceinline__ float dot16_f32(const u32x4& c, const float* v) {
   float acc = 0.0f;

@@ -84,6 +84,11 @@ struct Gemm1Args {
   int fused;
   int32_t* ids_out;
   float* w_out;
+  // non-null: GEMM1 multiplies e4m3 activation codes [T, H] with one float scale per
+  // (token, 128-column group) [T, H/128] instead of the bf16 hidden states (H % 128 == 0,
+  // routing not fused)
+  const uint8_t* xq = nullptr;
+  const float* xs = nullptr;
 };
 bool gemm1_fused_route_ok(int T, int k);
 hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s);

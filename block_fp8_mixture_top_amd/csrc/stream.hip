@@ -42,12 +42,18 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // XL (T == 1 with long rows only): the token's x is staged once per workgroup in LDS instead
 // of being held in every lane's registers, which leaves room for more waves per SIMD; one
 // barrier, after the weight reads are issued, publishes it.
-template <int LPR, int MCH, int RP, int PER, bool XL = false>
+// A8 (PER == 0 only): the activations are e4m3 codes xq with one scale xs per (token,
+// 128-column group); a 16-code chunk lies in one group, so its block product takes the
+// weight block scale times the group's activation scale.
+template <int LPR, int MCH, int RP, int PER, bool XL = false, bool A8 = false>
 __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden,
                                                                const float* __restrict__ logits, int T, int E,
                                                                BankArg w13, Plan plan, int H, int I, int k,
                                                                float* __restrict__ h, int32_t* __restrict__ ids_out,
-                                                               float* __restrict__ w_out) {
+                                                               float* __restrict__ w_out,
+                                                               const uint8_t* __restrict__ xq,
+                                                               const float* __restrict__ xs) {
+  static_assert(!A8 || (PER == 0 && !XL), "e4m3 activations come with a routing plan");
   constexpr int GPW = kWave / LPR;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int grp = lane / LPR, gl = lane % LPR;
@@ -64,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   __shared__ int s_e, s_m;
   // x of token 0, issued before routing when T == 1 (XL: 16-byte pieces q = tid + kThreads*j
   // of the row, bound for LDS)
-  u32x4 x0[XL ? 1 : MCH], x1[XL ? 1 : MCH];
+  u32x4 x0[XL ? 1 : MCH], x1[XL || A8 ? 1 : MCH];
+  float xsm[A8 ? MCH : 1];  // A8: the activation scale of each chunk's group
   constexpr int XQ = XL ? (MCH * kWave * 2 + kThreads - 1) / kThreads : 1;
   __shared__ __align__(16) uint8_t s_x[XL ? MCH * kWave * 32 : 16];
   u32x4 xr[XQ];
@@ -217,8 +224,17 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   for (int q = 0; q < cnt; ++q) {
     const int p = single >= 0 ? single : pairs[q];
     if (!XL && single < 0) {
-      const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
-      if constexpr (!XL) {
+      if constexpr (A8) {
+        const uint8_t* xc = xq + (size_t)(p / k) * H;
+        const float* xg = xs + (size_t)(p / k) * (H / kScaleBlock);
+#pragma unroll
+        for (int m = 0; m < MCH; ++m) {
+          const int c = min(gl + LPR * m, NC - 1);
+          x0[m] = ld16(xc + (size_t)c * 16);
+          xsm[m] = xg[c / 8];
+        }
+      } else if constexpr (!XL) {
+        const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
 #pragma unroll
         for (int m = 0; m < MCH; ++m) {
           const int c = min(gl + LPR * m, NC - 1);
@@ -237,12 +253,17 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
           if constexpr (XL) {
             xa = *(const u32x4*)(s_x + (gl + LPR * m) * 32);
             xb = *(const u32x4*)(s_x + (gl + LPR * m) * 32 + 16);
-          } else {
+          } else if constexpr (!A8) {
             xa = x0[m];
             xb = x1[m];
           }
-          g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], xa, xb), g);
-          u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], xa, xb), u);
+          if constexpr (A8) {
+            g = __builtin_fmaf(sg[m] * xsm[m], dot16_e4m3(cg[r][m], x0[m]), g);
+            u = __builtin_fmaf(su[m] * xsm[m], dot16_e4m3(cu[r][m], x0[m]), u);
+          } else {
+            g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], xa, xb), g);
+            u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], xa, xb), u);
+          }
         }
       }
       g = group_sum<LPR>(g);
@@ -469,17 +490,27 @@ hipError_t g1(const Gemm1Args& a, hipStream_t s) {
   if constexpr (PER > 0 && LPR == kWave && MCH >= 4) {
     if (a.T == 1) {
       launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER, true>), grid, dim3(kThreads), 0, s, a.hidden, a.logits,
-                    a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
+                    a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out, a.xq, a.xs);
       return hipGetLastError();
     }
   }
   launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER>), grid, dim3(kThreads), 0, s, a.hidden, a.logits, a.T,
-                     a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out);
+                     a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out, a.xq, a.xs);
+  return hipGetLastError();
+}
+
+template <int LPR, int MCH, int RP>
+hipError_t g1a8(const Gemm1Args& a, hipStream_t s) {
+  const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
+  dim3 grid((a.I + rows - 1) / rows, a.slots);
+  launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, 0, false, true>), grid, dim3(kThreads), 0, s, a.hidden,
+                a.logits, a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out, a.xq, a.xs);
   return hipGetLastError();
 }
 
 template <int LPR, int MCH, int RP>
 hipError_t g1r(const Gemm1Args& a, hipStream_t s) {
+  if (a.xq != nullptr) return a.fused ? hipErrorInvalidValue : g1a8<LPR, MCH, RP>(a, s);
   if (!a.fused) return g1<LPR, MCH, RP, 0>(a, s);
   hipError_t err = hipErrorInvalidValue;
   MOE_TOPK_DISPATCH(a.E, err = (g1<LPR, MCH, RP, PER>(a, s)));

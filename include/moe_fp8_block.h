@@ -93,18 +93,32 @@ typedef struct {
   const float* bias;           /* device [E, N] float, 16-byte aligned, or NULL for no bias */
 } moe_fp8_bank;
 
+/*
+ * Activation precision (gaudi-cookbook "fp8-moe-gather", Who is affected: dynamic activation
+ * scales; The fix: up/gate as one native FP8 GEMM, the down projection in fp32).
+ */
+typedef enum {
+  MOE_ACT_PATH = 0,      /* the path's own: bf16 activations (exact W8A16) on GATHER and
+                            STREAM; e4m3 per token and per (token, slot) on MFMA */
+  MOE_ACT_ROW_FP8 = 1,   /* reported only: MFMA's per-row dynamic e4m3 on both GEMMs */
+  MOE_ACT_GROUP_FP8 = 2  /* GATHER / STREAM: GEMM1 on dynamic e4m3 activations with one scale
+                            per (token, 128-column group), scale = group amax/448; GEMM2 on
+                            float h. Needs H % 128 == 0; the gate then never picks MFMA. */
+} moe_act;
+
 /* Host-side options; NULL means the defaults below. */
 typedef struct {
   float gate_ratio;                  /* gather iff T*top_k <= gate_ratio*E (default 2.0, measured) */
   int32_t force_path;                /* moe_path; anything but AUTO is taken as asked or fails */
   int32_t mfma_min_tokens_per_expert;/* grouped work uses MFMA iff T*top_k >= this*E (default 2, measured) */
-  int32_t reserved;                  /* must be 0 */
+  int32_t act_mode;                  /* MOE_ACT_PATH (default) or MOE_ACT_GROUP_FP8 */
 } moe_opts;
 
 /* Filled by forward (host struct): what actually ran. */
 typedef struct {
   int32_t path;     /* moe_path taken (never AUTO) */
-  int32_t act_mode; /* 0: bf16 activations, exact W8A16; 1: per-row dynamic e4m3 (W8A8) */
+  int32_t act_mode; /* 0: bf16 activations, exact W8A16; 1: per-row dynamic e4m3 on both GEMMs
+                       (MFMA); 2: per-(token, 128-column) dynamic e4m3 on GEMM1, float GEMM2 */
   int32_t slots;    /* expert slots launched: min(E, T*top_k) */
   int32_t kernels;  /* kernel launches enqueued */
 } moe_run_info;

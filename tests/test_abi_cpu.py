@@ -43,7 +43,7 @@ def test_default_opts(lib):
     o = L.Opts()
     assert lib.moe_fp8_block_default_opts(ctypes.byref(o)) == 0
     assert o.gate_ratio == pytest.approx(2.0)
-    assert (o.force_path, o.mfma_min_tokens_per_expert, o.reserved) == (0, 2, 0)
+    assert (o.force_path, o.mfma_min_tokens_per_expert, o.act_mode) == (0, 2, 0)
     assert lib.moe_fp8_block_default_opts(None) == -1
     assert b"NULL" in lib.moe_fp8_block_last_error()
 
@@ -77,7 +77,8 @@ def test_gate_ratio_and_forced_paths(lib):
     for forced in (1, 2, 3):
         assert _path(lib, 4096, 256, 8, force_path=forced)[1].path == forced
     assert _path(lib, 1, 256, 8, force_path=7)[0] == -1
-    assert _path(lib, 1, 256, 8, reserved=1)[0] == -1
+    assert _path(lib, 1, 256, 8, act_mode=1)[0] == -1  # reported only, never asked for
+    assert _path(lib, 1, 256, 8, act_mode=3)[0] == -1
     assert _path(lib, 1, 256, 8, mfma_min_tokens_per_expert=0)[0] == -1
 
 
@@ -223,3 +224,27 @@ def test_binding_refuses_a_missing_library(tmp_path):
             L.load(str(tmp_path / "nope.so"))
     finally:
         L._lib = saved
+
+
+def test_group_fp8_activations_gate_and_checks(lib):
+    """MOE_ACT_GROUP_FP8 runs on GATHER and STREAM: the gate's MFMA choice becomes STREAM,
+    a forced MFMA is refused, and H must be a multiple of 128."""
+    st, info = _path(lib, 1, 256, 8, act_mode=2)
+    assert st == 0 and (info.path, info.act_mode) == (1, 2)
+    st, info = _path(lib, 4096, 256, 8, act_mode=2)
+    assert st == 0 and (info.path, info.act_mode) == (2, 2)
+    st, info = _path(lib, 4096, 256, 8)
+    assert st == 0 and (info.path, info.act_mode) == (3, 1)
+    o = L.Opts()
+    lib.moe_fp8_block_default_opts(ctypes.byref(o))
+    o.act_mode = 2
+    assert lib.moe_fp8_block_workspace_size(4096, 256, 2048, 512, 8, ctypes.byref(o)) > \
+        lib.moe_fp8_block_workspace_size(4096, 256, 2048, 512, 8, ctypes.byref(L.Opts(2.0, 2, 2, 0)))
+    o.force_path = 3
+    st, msg, _ = _forward(lib, T=64, opts=o)
+    assert st == -2 and "GROUP_FP8" in msg
+    o.force_path = 0
+    st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), opts=o)
+    assert st == -2 and "128" in msg
+    st, msg, _ = _forward(lib, opts=o, ws_bytes=16)
+    assert st == -5

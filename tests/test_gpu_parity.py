@@ -271,6 +271,52 @@ def test_mlp_bias_decode_and_prefill_sampled():
     check_out(out[torch.from_numpy(rows).to(DEV)], res, 1, "bias prefill T=4096 sampled")
 
 
+def test_group_quantisation_bit_exact():
+    """Activation codes and scales per (token, 128-column group) match the oracle bit for bit."""
+    say("group quantisation")
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(9, 1024, generator=g) * torch.rand(9, 8, generator=g).repeat_interleave(128, 1) * 9)
+    x[2, 256:384] = 0
+    x = x.to(torch.bfloat16)
+    codes, scales = M.quantize_rows(x.to(DEV).view(-1, 128))
+    q, sc = O.quantize_groups(O.bf16_to_f64(bf16_bits(x)).astype(np.float32))
+    assert np.array_equal(scales.cpu().numpy().reshape(9, 8), sc)
+    assert np.array_equal(codes.cpu().numpy().reshape(9, 1024), q)
+
+
+@pytest.mark.parametrize("path", ["gather", "stream"])
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_group_fp8_activations(path, T):
+    """GEMM1 on e4m3 activations per (token, 128 columns), GEMM2 on float h, with biases."""
+    c = W.make_case("decode", T=T, seed=61 + T, device=DEV, E=16, H=640, I=384, top_k=4, bias_std=0.2)
+    say("group fp8", path, T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path], act_mode=M.ACT_GROUP_FP8)
+    assert (info["path"], info["act_mode"]) == (path, 2)
+    check_out(out, oracle_out(c, act_mode=2), 2, f"group fp8 {path} T={T}")
+
+
+def test_group_fp8_decode_and_grouped():
+    """The decode workload (GATHER, bf16 out) and T=4096, where the gate takes STREAM instead
+    of MFMA (sampled rows)."""
+    banks = W.make_banks("decode", seed=1, device=DEV)
+    c = W.make_case("decode", T=1, seed=1, device=DEV, banks=banks)
+    say("group fp8 decode")
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16,
+                          act_mode=M.ACT_GROUP_FP8)
+    assert (info["path"], info["act_mode"]) == ("gather", 2)
+    check_out(out, oracle_out(c, act_mode=2), 2, "group fp8 decode T=1")
+    c = W.make_case("prefill", T=4096, seed=6, device=DEV, banks=banks)
+    say("group fp8 T=4096")
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16,
+                          act_mode=M.ACT_GROUP_FP8)
+    torch.cuda.synchronize()
+    assert (info["path"], info["act_mode"]) == ("stream", 2)
+    rows = np.array([0, 5, 2048, 4095])
+    check_out(out[torch.from_numpy(rows).to(DEV)], oracle_out(c, rows=rows, act_mode=2), 2,
+              "group fp8 T=4096 sampled")
+
+
 @pytest.mark.parametrize("T,path", [(1, None), (16, None), (16, "stream")])
 def test_large_expert_workload(T, path):
     """E=256, H=7168, I=2048, fp32 scales; only the routed experts are drawn, the rest
