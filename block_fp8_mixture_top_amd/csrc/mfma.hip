@@ -473,14 +473,29 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 
 // One workgroup per (expert, 128-pair tile, half of 64 pairs), 4 waves; the two halves of a
 // tile are consecutive workgroups of one XCD, so the second reads the expert's w2 from L2.
-// The half's h codes (e4m3 per (token, slot) row, scale amax/448, from the row quantiser)
-// are copied to LDS once: A = h codes (pairs as rows), B = w2 rows (features). The H
-// outputs go in chunks of 256; wave w owns features 64w .. 64w+64 of each chunk (FT = 4
-// MFMA tiles; a last chunk of 128 has work for waves 0 and 1 only), so lane (r16, kq) of a
-// result holds pairs 4kq..4kq+3 of feature r16. Each wave streams its own w2 rows, (chunk,
-// K block) after (chunk, K block), through a private 3-deep LDS ring. Each pair's y row =
-// s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
+// A = h codes (pairs as rows; e4m3 per (token, slot) row, scale amax/448, from the row
+// quantiser), B = w2 rows (features). The half's h codes are copied to LDS once and then
+// read into registers, every K block of them (at most 128 VGPRs), which leaves the whole
+// LDS to the w2 stream. The H outputs go in chunks of 256; wave w owns features 64w ..
+// 64w+64 of each chunk (FT = 4 MFMA tiles; a last chunk of 128 has work for waves 0 and 1
+// only), so lane (r16, kq) of a result holds pairs 4kq..4kq+3 of feature r16. Each wave
+// streams its own w2 rows, (chunk, K block) after (chunk, K block), through a private
+// kRing2-deep LDS ring with kRing2 - 1 stages in flight and no barriers. Each pair's y row
+// = s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
 // applies the router weights.
+constexpr int kRing2 = 4;
+
+// Wait for the copy of the stage issued `later` stages before the newest one: the loads of
+// the `later` younger stages (8 each) may stay outstanding. Loads complete in issue order,
+// so the count is exact for them; stores issued meanwhile (they may complete out of order)
+// can only make the wait longer, never shorter.
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= 3) wait_vm<24>();
+  else if (later == 2) wait_vm<16>();
+  else if (later == 1) wait_vm<8>();
+  else wait_vm<0>();
+}
+
 template <int KB>  // I / 128
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
@@ -491,8 +506,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   constexpr int NCH = 4 * FT * 16;
   constexpr int WB = 64 * kRowB;   // one wave's w2 rows of a stage
   constexpr int HB = HM * kRowB;   // the h codes of one K block
-  __shared__ __align__(16) uint8_t sH[KB * HB];
-  __shared__ __align__(16) uint8_t ring[4 * kStages * WB];
+  static_assert(KB * HB <= 4 * kRing2 * WB, "the h codes are staged in the ring");
+  static_assert(kRing2 - 1 <= 3, "wait_stage covers up to three younger stages");
+  __shared__ __align__(16) uint8_t ring[4 * kRing2 * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
 
   const int nitems = plan.tile_off[E] * 2;
@@ -521,114 +537,119 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const int b = i * 8 + lr;
     woff[i] = (uint32_t)(wave * 64 + b) * (uint32_t)I + (uint32_t)((lc ^ sw(b)) << 4);
   }
-  uint8_t* myring = ring + wave * kStages * WB;
+  uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
     const int c = st / KB, kb = st - c * KB;
     const uint8_t* src = wb + (size_t)c * NCH * I + kb * 128;
-    uint8_t* slot = myring + (st % kStages) * WB;
+    uint8_t* slot = myring + (st % kRing2) * WB;
 #pragma unroll
     for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + i * 1024);
   };
   stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
-  // (visible after the barrier that follows the h codes)
-  {
-    const int nvalid = pos_end - pos0 < HM ? pos_end - pos0 : HM;
-    // the half's h codes: 8 * KB copies of 8 rows x 128 bytes, 2 * KB per wave (rows past the
-    // expert's pairs copy the first row; their results are never stored)
+  const int nvalid = pos_end - pos0 < HM ? pos_end - pos0 : HM;
+  // the half's h codes into the ring space: 8 * KB copies of 8 rows x 128 bytes, 2 * KB per
+  // wave (rows past the expert's pairs copy the first row; their results are never stored)
 #pragma unroll
-    for (int i = 0; i < 2 * KB; ++i) {
-      const int q = wave * 2 * KB + i;
-      const int kb = q >> 3, r = (q & 7) * 8 + lr;
-      const int rr = r < nvalid ? r : 0;
-      g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), sH + kb * HB + (q & 7) * 1024);
+  for (int i = 0; i < 2 * KB; ++i) {
+    const int q = wave * 2 * KB + i;
+    const int kb = q >> 3, r = (q & 7) * 8 + lr;
+    const int rr = r < nvalid ? r : 0;
+    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q & 7) * 1024);
+  }
+  float hsc[4][4];
+  int prow[4][4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = pt * 16 + kq * 4 + q;
+      const bool ok = r < nvalid;
+      hsc[pt][q] = hs[pos0 + (ok ? r : 0)];
+      prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
     }
-    if (nst > 0) issue(0);
-    if (nst > 1) issue(1);
-    float hsc[4][4];
-    int prow[4][4];
+  wait_vm<0>();  // everyone's h codes and the block scales are in after the barrier
+  __syncthreads();
+  i32x8 a[KB][4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = pt * 16 + kq * 4 + q;
-        const bool ok = r < nvalid;
-        hsc[pt][q] = hs[pos0 + (ok ? r : 0)];
-        prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
-      }
-    wait_vm<0>();  // everyone's h codes are in after the barrier
-    __syncthreads();
+    for (int pt = 0; pt < 4; ++pt) a[kb][pt] = lds_operand(ring + kb * HB, pt * 16 + r16, kq);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's h reads are done
+  __syncthreads();                     // and everyone's, before the ring is refilled
 
-    f32x4 acc[FT][4];
-    for (int st = 0; st < nst; ++st) {
-      const int c = st / KB, kb = st - c * KB;
-      // the previous chunk's y stores are outstanding at a chunk start, and stores and
-      // loads may complete out of order: drain everything there
-      if (st + 1 < nst && kb != 0) wait_vm<8>();
-      else wait_vm<0>();
-      if (st + 2 < nst) issue(st + 2);
-      if (kb == 0) {
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft)
+  for (int s = 0; s < kRing2 - 1; ++s)
+    if (s < nst) issue(s);
+  f32x4 acc[FT][4];
+  // (chunk c, K block kb) is stage st = c * KB + kb; kb is unrolled so that the h operands
+  // are indexed statically and stay in registers
+  for (int c = 0; c < nch; ++c) {
 #pragma unroll
-          for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = c * KB + kb;
+    // stage st has landed once at most min(kRing2 - 2, nst - 1 - st) younger stages remain
+    wait_stage(min(kRing2 - 2, nst - 1 - st));
+    // the slot of stage st - 1 is free: its operands were read (and waited for) last step
+    if (st + kRing2 - 1 < nst) issue(st + kRing2 - 1);
+    if (kb == 0) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const uint8_t* slot = myring + (st % kRing2) * WB;
+    i32x8 bw[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
+    const int n0 = c * NCH + wave * 64;
+    // features n0 .. n0 + 63 share one 128-row scale block
+    const int nb = n0 / kScaleBlock;
+    // each MFMA starts from zero and its block product is scaled into the accumulator on
+    // the VALU while the next MFMA runs
+    const float sc = s_sc[nb * KB + kb];  // uniform
+    {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 pp = mfma_fp8(a[kb][0], bw[0], z);
+#pragma unroll
+      for (int j = 0; j < FT * 4; ++j) {
+        const int ft = j / 4, pt = j % 4;
+        f32x4 nx;
+        if (j + 1 < FT * 4) nx = mfma_fp8(a[kb][(j + 1) % 4], bw[(j + 1) / 4], z);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
+        if (j + 1 < FT * 4) pp = nx;
       }
-      const uint8_t* slot = myring + (st % kStages) * WB;
-      const uint8_t* hs_ = sH + kb * HB;
-      i32x8 a[4], bw[FT];
+    }
+    if (kb == KB - 1) {
+      // y of pair (pt, 4kq+q), features n0 .. n0+63, held by the 16 lanes of row kq (r16)
+      // times FT: stored in fp16 with one power-of-two exponent per (pair, 64 features)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) a[pt] = lds_operand(hs_, pt * 16 + r16, kq);
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
-      const int n0 = c * NCH + wave * 64;
-      // features n0 .. n0 + 63 share one 128-row scale block
-      const int nb = n0 / kScaleBlock;
-      // each MFMA starts from zero and its block product is scaled into the accumulator on
-      // the VALU while the next MFMA runs
-      const float sc = s_sc[nb * KB + kb];  // uniform
-      {
-        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4 pp = mfma_fp8(a[0], bw[0], z);
+        for (int q = 0; q < 4; ++q) {
+          float v[FT];
+          uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
 #pragma unroll
-        for (int j = 0; j < FT * 4; ++j) {
-          const int ft = j / 4, pt = j % 4;
-          f32x4 nx;
-          if (j + 1 < FT * 4) nx = mfma_fp8(a[(j + 1) % 4], bw[(j + 1) / 4], z);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
-          if (j + 1 < FT * 4) pp = nx;
-        }
-      }
-      if (kb == KB - 1) {
-        // y of pair (pt, 4kq+q), features n0 .. n0+63, held by the 16 lanes of row kq (r16)
-        // times FT: stored in fp16 with one power-of-two exponent per (pair, 64 features)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[FT];
-            uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
-#pragma unroll
-            for (int ft = 0; ft < FT; ++ft) {
-              v[ft] = acc[ft][pt][q] * hsc[pt][q];
-              m = max(m, __float_as_uint(__builtin_fabsf(v[ft])));
-            }
-            m = max(m, dpp_u32<0xB1, 0xF, 0xF>(0u, m));   // quad_perm [1,0,3,2]
-            m = max(m, dpp_u32<0x4E, 0xF, 0xF>(0u, m));   // quad_perm [2,3,0,1]
-            m = max(m, dpp_u32<0x124, 0xF, 0xF>(0u, m));  // row_ror:4
-            m = max(m, dpp_u32<0x128, 0xF, 0xF>(0u, m));  // row_ror:8
-            const int ey = y_exponent(m);
-            const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
-            if (prow[pt][q] < 0) continue;
-            _Float16* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
-#pragma unroll
-            for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = (_Float16)(v[ft] * down);
-            if (r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
+          for (int ft = 0; ft < FT; ++ft) {
+            v[ft] = acc[ft][pt][q] * hsc[pt][q];
+            m = max(m, __float_as_uint(__builtin_fabsf(v[ft])));
           }
-      }
+          m = max(m, dpp_u32<0xB1, 0xF, 0xF>(0u, m));   // quad_perm [1,0,3,2]
+          m = max(m, dpp_u32<0x4E, 0xF, 0xF>(0u, m));   // quad_perm [2,3,0,1]
+          m = max(m, dpp_u32<0x124, 0xF, 0xF>(0u, m));  // row_ror:4
+          m = max(m, dpp_u32<0x128, 0xF, 0xF>(0u, m));  // row_ror:8
+          const int ey = y_exponent(m);
+          const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
+          if (prow[pt][q] < 0) continue;
+          _Float16* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = (_Float16)(v[ft] * down);
+          if (r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
+        }
     }
   }
+  }
 }
-
 template <int KB>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
                int I, _Float16* y, int8_t* yexp, hipStream_t s) {
