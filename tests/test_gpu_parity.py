@@ -14,7 +14,7 @@ import torch
 import block_fp8_mixture_top_amd as M
 import oracle as O
 import workloads as W
-from helpers import REL_TOL, bank_numpy, bf16_bits, bf16_half_ulp, rel_err, rel_err_bf16
+from helpers import REL_TOL, bank_numpy, bf16_bits, bf16_half_ulp, fp8_ulp_diff, rel_err, rel_err_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -388,6 +388,24 @@ def test_paths_agree(decode_banks):
     b, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, force_path=M.PATH_STREAM)
     d = (a - b).abs().max().item() / a.abs().max().item()
     assert d <= 1e-5
+
+
+@pytest.mark.parametrize("act", ["path", "group_fp8"])
+def test_verify_gather_against_stream_in_fp8_ulps(decode_banks, act):
+    """The verify mode of gaudi-cookbook fp8-moe-gather: run the gathered path and the
+    grouped one on the same tokens and report outputs that differ by more than 2 fp8 ulps.
+    Both compute the same products in float, so none may."""
+    c = W.make_case("sweep", T=12, seed=14, device=DEV, banks=decode_banks)
+    a_mode = M.ACT_GROUP_FP8 if act == "group_fp8" else M.ACT_PATH
+    say("verify", act)
+    a, ia = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                      force_path=M.PATH_GATHER, act_mode=a_mode)
+    b, ib = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                      force_path=M.PATH_STREAM, act_mode=a_mode)
+    assert ia["act_mode"] == ib["act_mode"]
+    d = fp8_ulp_diff(a.cpu().numpy(), b.cpu().numpy())
+    say("verify", act, f"max {d.max():.3g} fp8 ulp")
+    assert int((d > 2).sum()) == 0
 
 
 def test_zero_tokens():

@@ -160,3 +160,20 @@ def test_dequant_power_of_two_codes_unit_scales():
     W_ = O.dequant_expert(bank, 0)
     want = np.vectorize(pw.get)(codes).astype(np.float64)
     assert np.array_equal(W_, want)
+
+
+def test_fp8_ulp_diff_counts_e4m3_steps():
+    """The verify unit: neighbouring e4m3 values are one ulp apart everywhere, normal and
+    subnormal, and the distance between any two codes of one binade is their code distance."""
+    from helpers import fp8_ulp_diff
+    lut = O.e4m3_lut()
+    pos = lut[:0x7F]  # 0 .. 448, ascending
+    d = fp8_ulp_diff(pos[1:], pos[:-1])
+    # steps inside a binade are one ulp; crossing up into the next binade the step below
+    # is measured in the larger value's ulp, i.e. half an ulp
+    upper = np.frexp(pos[1:])[1] != np.frexp(pos[:-1])[1]
+    assert np.all(d[~upper | (pos[1:] <= 2.0 ** -6)] == 1.0)
+    assert np.all(d[upper & (pos[1:] > 2.0 ** -6)] == 0.5)
+    assert fp8_ulp_diff(np.array([1.0]), np.array([1.25]))[0] == 2.0
+    assert fp8_ulp_diff(np.array([-3.0]), np.array([3.0]))[0] == 24.0  # spacing 0.25 in [2, 4)
+    assert fp8_ulp_diff(np.array([0.0]), np.array([0.0]))[0] == 0.0
