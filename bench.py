@@ -84,7 +84,7 @@ def parse():
 # kernel kinds of the library -> a substring of their symbol names
 KERNEL_SYMBOLS = {"route": "route_", "sort": "sort_", "quant": "quant_rows_bf16", "hquant": "quant_rows_f32",
                   "gemm1": "gemm1_", "gemm2": "gemm2_",
-                  "combine": "combine_kernel"}
+                  "combine": "combine_"}
 COPY_BYTES = 1 << 30
 
 
@@ -140,7 +140,7 @@ def traffic_record(args):
         "bytes_per_launch": round(kf * 1024.0 * f_scale + kw * 1024.0 * w_scale),
         "source_digest": source_digest(),
     }
-    path = os.path.join(ROOT, "profiles", f"traffic_{args.kernel}_{args.workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.kernel}_{traffic_key(args.workload, args.T)}.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -184,6 +184,11 @@ def source_digest() -> str:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_key(workload: str, T) -> str:
+    """Name of a workload's traffic record: the workload, plus T when it is not the default."""
+    return workload if T is None or T == WORKLOADS[workload]["T"] else f"{workload}_T{T}"
 
 
 def committed_traffic(kernel: str, workload: str):
@@ -347,12 +352,12 @@ def main():
                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
     roofline["kernel"] = dom
     roofline["kernel_ms"] = round(dom_ms, 5)
-    roofline["traffic"] = committed_traffic(dom, wl)
+    roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T))
     roofline["kernels_ms"] = {n: round(v, 5) for n, v in per_kernel.items()}
 
     cpu = None
-    if not args.no_cpu_baseline and wl != "prefill":
-        cpu = cpu_baseline(cases, k, args.cpu_seconds, w13_b + w2_b)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cases, k, args.cpu_seconds, w13_b + w2_b, prefill=wl == "prefill")
 
     if wl == "prefill":
         value, unit = tok_s, "tokens/s"
@@ -390,9 +395,11 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cases, k, seconds, expert_bytes):
+def cpu_baseline(cases, k, seconds, expert_bytes, prefill=False):
     """The float64 oracle (gathered formulation) on this host, repeated over the first sets
-    for about `seconds`; GB/s over the same routed bytes."""
+    for about `seconds`; GB/s over the same routed bytes. With `prefill`, the oracle in its
+    W8A8 mode (the MFMA path's reading) on successive 16-token slices of the first set,
+    reported in tokens/s."""
     import numpy as np
     import torch
 
@@ -415,6 +422,31 @@ def cpu_baseline(cases, k, seconds, expert_bytes):
         return dict(codes=codes, scales=scales, scale_dtype=bank.scale_dtype, E=bank.E, N=bank.N, K=bank.K,
                     expert_stride_bytes=st, scale_row_stride=bank.scale_row_stride,
                     scale_expert_stride=bank.scale_expert_stride)
+
+    if prefill:
+        c = cases[0]
+        hid_all = c.hidden.cpu().view(torch.int16).numpy().view(np.uint16)
+        lg_all = c.logits.cpu().numpy()
+        spent, tokens, q = 0.0, 0, 0
+        while spent < seconds and q * 16 < hid_all.shape[0]:
+            rows = slice(q * 16, (q + 1) * 16)
+            ids, _, _ = O.route(lg_all[rows], k)
+            used = [int(e) for e in O.routed_experts(ids)]
+            w13, w2 = host_bank(c.w13, used), host_bank(c.w2, used)
+            t0 = time.perf_counter()
+            O.forward(hid_all[rows], lg_all[rows], w13, w2, k, act_mode=1)
+            spent += time.perf_counter() - t0
+            tokens += 16
+            q += 1
+        return {
+            "value": round(tokens / spent, 2),
+            "unit": "tokens/s",
+            "cores": threads,
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{tokens} tokens of the first input set in 16-token slices (float64 gathered oracle, "
+                      f"W8A8 reading, {spent:.1f} s)",
+        }
 
     # host copies of the first few sets (only the routed experts' pages are ever touched),
     # then forwards over them in turn until about `seconds` of oracle time
