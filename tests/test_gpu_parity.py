@@ -408,6 +408,69 @@ def test_verify_gather_against_stream_in_fp8_ulps(decode_banks, act):
     assert int((d > 2).sum()) == 0
 
 
+@pytest.mark.parametrize("path,T", [("gather", 1), ("gather", 8), ("stream", 8), ("mfma", 64)])
+def test_graph_replays_match_eager(decode_banks, path, T):
+    """A forward captured in a HIP graph gives the eager result bit for bit on every replay,
+    with other GPU work and host synchronisation between the replays (the benchmark times
+    replayed graphs)."""
+    c = W.make_case("sweep", T=T, seed=15, device=DEV, banks=decode_banks)
+    say("graph", path, T)
+    kw = dict(out_dtype=torch.float32, force_path=PATHS[path])
+    eager, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, **kw)
+    ws = torch.empty(M.workspace_size(T, c.E, c.H, c.I, c.top_k, force_path=PATHS[path]), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty_like(eager)
+    M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out=out, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out=out, workspace=ws, **kw)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)  # stale workspace contents must not leak into the result
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+
+
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("E,k,T", [(1, 1, 3), (4, 4, 2), (8, 8, 5)])
+def test_degenerate_routings(path, E, k, T):
+    """One expert (a plain SwiGLU FFN) and top_k = E (every expert routed, a dense softmax
+    mixture), on every path."""
+    c = W.make_case("decode", T=T, seed=71 + E, device=DEV, E=E, H=256, I=128, top_k=k, bias_std=0.1)
+    say("degenerate", path, E, k, T)
+    act = 1 if path == "mfma" else 0
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path], return_routing=True)
+    res = oracle_out(c, act_mode=act)
+    assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
+    check_out(out, res, act, f"degenerate {path} E={E} k={k}")
+
+
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+def test_largest_expert_count_and_top_k(path):
+    """E = 1024 experts and top_k = 32, the ABI's limits, with small experts; only the routed
+    experts are drawn (the others hold NaN codes and scales)."""
+    E, k, T = 1024, 32, 3 if path != "mfma" else 70
+    logits = W.make_logits(T, E, "normal", seed=81, device="cpu")
+    ids, _, _ = O.route(logits.numpy(), k)
+    used = O.routed_experts(ids)
+    banks = W.make_banks("decode", seed=82, device=DEV, E=E, H=256, I=128, experts=used)
+    c = W.make_case("decode", T=T, seed=82, device=DEV, banks=banks, E=E, H=256, I=128, top_k=k)
+    c.logits = logits.to(DEV)
+    say("E=1024 k=32", path, T)
+    act = 1 if path == "mfma" else 0
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path], return_routing=True)
+    torch.cuda.synchronize()
+    assert info["path"] == path
+    rows = np.arange(T) if T <= 3 else np.array([0, 33, T - 1])
+    res = oracle_out(c, rows=rows, act_mode=act, experts=O.routed_experts(ids[rows]))
+    assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
+    check_out(out[torch.from_numpy(rows).to(DEV)], res, act, f"E=1024 k=32 {path}")
+
+
 def test_zero_tokens():
     c = W.make_case("tiny", T=1, seed=1).to(DEV)
     out, info = M.forward(c.hidden[:0], c.logits[:0], c.w13, c.w2, c.top_k, out_dtype=torch.float32)
