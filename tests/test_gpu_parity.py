@@ -345,8 +345,11 @@ def test_prefill_sampled(decode_banks, T):
     c = W.make_case("prefill", T=T, seed=6, device=DEV, banks=decode_banks)
     say("prefill", T)
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16, return_routing=True)
+    again, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert info["path"] == "mfma" and info["act_mode"] == 1
+    # every output, not only the sampled ones: the path is deterministic
+    assert torch.equal(out, again)
     rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(T).choice(T, 21, replace=False)]))
     res = oracle_out(c, rows=rows, act_mode=1)
     assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
