@@ -463,7 +463,8 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
 
 int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales, void* stream) {
   if (rows < 0 || cols <= 0) return fail(MOE_ERR_ARG, "rows must be >= 0 and cols > 0");
-  if (cols % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 16 (got %d)", cols);
+  if (cols % 16 != 0 || cols > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 16 and at most 8192 (got %d)", cols);
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(MOE_ERR_ARG, "x, codes and scales must be non-NULL");
   if (!aligned16(x) || !aligned16(codes)) return fail(MOE_ERR_ALIGN, "x and codes must be 16-byte aligned");

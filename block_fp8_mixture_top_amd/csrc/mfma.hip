@@ -39,6 +39,10 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
 // ---------------------------------------------------------------- per-row quantisation
 
 // One wave per row of bf16: amax, scale = amax/448 (1 if zero), codes = e4m3(x/scale).
+// Lane l holds the 8-value pieces l, l + 64, ... of the row: IT of them, all read up front
+// (pieces past the row end read its last piece and are ignored), so the row is read from
+// memory once and every read is in flight together.
+template <int IT>
 __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
@@ -46,21 +50,30 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
   if (row >= rows) return;
   const int lane = lane_id();
   const uint16_t* xr = x + (size_t)row * cols;
+  u32x4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    v[it] = *(const u32x4*)(xr + (c < cols ? c : cols - 8));
+  }
   float amax = 0.0f;
-  for (int c = lane * 8; c < cols; c += kWave * 8) {
-    const u32x4 v = *(const u32x4*)(xr + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const bool in = lane * 8 + it * kWave * 8 < cols;
+    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_lo(w[q])));
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_hi(w[q])));
+      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_lo(w[q])) : 0.0f);
+      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_hi(w[q])) : 0.0f);
     }
   }
   amax = wave_max(amax);
   const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
-  for (int c = lane * 8; c < cols; c += kWave * 8) {
-    const u32x4 v = *(const u32x4*)(xr + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    if (c >= cols) continue;
+    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
     uint32_t out[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -73,7 +86,9 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
   if (lane == 0) scales[row] = s;
 }
 
-// The same for rows of float (h before the down GEMM, in sorted-position order).
+// The same for rows of float (h before the down GEMM, in sorted-position order), two
+// 4-float reads per piece.
+template <int IT>
 __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __restrict__ x, int rows, int cols,
                                                              uint8_t* __restrict__ codes,
                                                              float* __restrict__ scales) {
@@ -81,16 +96,29 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
   if (row >= rows) return;
   const int lane = lane_id();
   const float* xr = x + (size_t)row * cols;
-  float amax = 0.0f;
-  for (int c = lane * 8; c < cols; c += kWave * 8) {
-    const f32x4 a = *(const f32x4*)(xr + c), b = *(const f32x4*)(xr + c + 4);
+  f32x4 va[IT], vb[IT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(a[q]), __builtin_fabsf(b[q])));
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    const int cc = c < cols ? c : cols - 8;
+    va[it] = *(const f32x4*)(xr + cc);
+    vb[it] = *(const f32x4*)(xr + cc + 4);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const bool in = lane * 8 + it * kWave * 8 < cols;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      amax = __builtin_fmaxf(amax, in ? __builtin_fmaxf(__builtin_fabsf(va[it][q]), __builtin_fabsf(vb[it][q])) : 0.0f);
   }
   amax = wave_max(amax);
   const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
-  for (int c = lane * 8; c < cols; c += kWave * 8) {
-    const f32x4 a = *(const f32x4*)(xr + c), b = *(const f32x4*)(xr + c + 4);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    if (c >= cols) continue;
+    const f32x4 a = va[it], b = vb[it];
     const uint32_t lo = enc2(a[0] / s, a[1] / s) | (enc2(a[2] / s, a[3] / s) << 16);
     const uint32_t hi = enc2(b[0] / s, b[1] / s) | (enc2(b[2] / s, b[3] / s) << 16);
     *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(lo, hi);
@@ -671,17 +699,31 @@ bool mfma_shape_ok(int H, int I) {
   return H % 128 == 0 && H > 0 && H <= kMaxH && I % 128 == 0 && I >= 128 && I <= kMaxI;
 }
 
+// Pieces of 8 values per lane, 512 columns per wave and piece; rows of up to 8192 columns.
+#define MOE_QUANT_LAUNCH(KERNEL, T)                                                                          \
+  static hipError_t launch_##KERNEL(const T* x, int rows, int cols, uint8_t* codes, float* scales,          \
+                                    hipStream_t s) {                                                         \
+    const dim3 grid((rows + 3) / 4), block(256);                                                             \
+    const int it = (cols + kWave * 8 - 1) / (kWave * 8);                                                     \
+    if (it <= 1) launch_kernel(KERNEL<1>, grid, block, 0, s, x, rows, cols, codes, scales);                   \
+    else if (it <= 2) launch_kernel(KERNEL<2>, grid, block, 0, s, x, rows, cols, codes, scales);              \
+    else if (it <= 4) launch_kernel(KERNEL<4>, grid, block, 0, s, x, rows, cols, codes, scales);              \
+    else if (it <= 8) launch_kernel(KERNEL<8>, grid, block, 0, s, x, rows, cols, codes, scales);              \
+    else if (it <= 16) launch_kernel(KERNEL<16>, grid, block, 0, s, x, rows, cols, codes, scales);            \
+    else return hipErrorInvalidValue;                                                                        \
+    return hipGetLastError();                                                                                \
+  }
+MOE_QUANT_LAUNCH(quant_rows_bf16_kernel, uint16_t)
+MOE_QUANT_LAUNCH(quant_rows_f32_kernel, float)
+#undef MOE_QUANT_LAUNCH
+
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                   hipStream_t s) {
-  const int blocks = (rows + 3) / 4;
-  launch_kernel(quant_rows_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, rows, cols, codes, scales);
-  return hipGetLastError();
+  return launch_quant_rows_bf16_kernel(x, rows, cols, codes, scales, s);
 }
 
 hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s) {
-  const int blocks = (rows + 3) / 4;
-  launch_kernel(quant_rows_f32_kernel, dim3(blocks), dim3(256), 0, s, x, rows, cols, codes, scales);
-  return hipGetLastError();
+  return launch_quant_rows_f32_kernel(x, rows, cols, codes, scales, s);
 }
 
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,

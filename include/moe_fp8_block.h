@@ -229,7 +229,8 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
  * The activation preparation of the MFMA path on its own: per-row dynamic e4m3.
  *   x [rows, cols] bf16; codes [rows, cols] uint8 out; scales [rows] float out, with
  *   scale = amax/448 (float division; 1 for an all-zero row) and code = e4m3 of x/scale
- *   (float division, nearest even, saturating). cols % 16 == 0, 16-byte aligned x/codes.
+ *   (float division, nearest even, saturating). cols % 16 == 0 and cols <= 8192
+ *   (MOE_ERR_UNSUPPORTED otherwise), 16-byte aligned x/codes.
  */
 int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                 void* stream);

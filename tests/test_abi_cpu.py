@@ -209,6 +209,7 @@ def test_route_argument_checks(lib):
 
 def test_small_entry_checks(lib):
     assert lib.moe_fp8_block_quantize_rows(FAKE, 4, 24, FAKE, FAKE, None) == -2
+    assert lib.moe_fp8_block_quantize_rows(FAKE, 4, 8208, FAKE, FAKE, None) == -2
     assert lib.moe_fp8_block_quantize_rows(None, 4, 32, FAKE, FAKE, None) == -1
     assert lib.moe_fp8_block_quantize_rows(ctypes.c_void_p(0x10004), 4, 32, FAKE, FAKE, None) == -4
     assert lib.moe_fp8_block_decode_e4m3(FAKE, FAKE, -1, None) == -1
