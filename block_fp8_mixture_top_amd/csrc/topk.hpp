@@ -2,6 +2,8 @@
 // weights (gaudi-cookbook "fp8-moe-gather", The fix: each token keeps its top_k experts).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -10,16 +12,19 @@ namespace moe {
 // lower id), and that logit. PER = logits held per lane, E <= 64 * PER. A NaN logit reads as
 // -inf, which keeps every id in [0, E). Call with all 64 lanes active.
 //
-// Each lane first sorts its PER (key, id) pairs best-first, so its current best is always
-// its head; a round is then one wave-wide max of the heads, a ballot of the lanes holding
-// that key (one lane unless logits tie exactly; the lowest id among tied heads is taken by a
-// min over them), and the winning lane advancing its head.
+// Each lane first sorts its PER keys best-first, so its current best is always its head
+// (the slot of each sorted key, hence its expert lane + 64 * slot, is kept four bits each
+// in one register); a round is then one wave-wide max of the heads, a ballot of the lanes
+// holding that key (one lane unless logits tie exactly; the lowest id among tied heads is
+// taken by a min over them), and the winning lane advancing its head with selects instead
+// of a branch.
 template <int PER>
 __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
                                               float& out_l) {
+  static_assert(PER <= 16, "slot indices are packed four bits each");
+  typedef typename std::conditional<PER <= 8, uint32_t, uint64_t>::type slot_t;
   const int lane = lane_id();
   uint32_t key[PER];
-  int idx[PER];
   float f[PER];
   // All loads first, in bounds and outside any branch, so that they are in flight together
   // (the empty asm keeps each one unconditional).
@@ -30,15 +35,18 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(f[i]));
+  // slot i holds expert lane + 64 i; after sorting, nibble i of `slot` is the slot of the
+  // i-th best key of this lane
+  slot_t slot = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + kWave * i;
     const float v = f[i] != f[i] ? -__builtin_inff() : f[i];
     key[i] = e < E ? order_key(v) : 0u;  // every real logit has a key > 0
-    idx[i] = e;
+    slot |= (slot_t)i << (4 * i);
   }
-  // insertion sort, best first: larger key, then lower id (ids rise with i, so a strict
-  // comparison keeps equal keys in id order)
+  // insertion sort, best first: larger key, then lower id (ids rise with the slot, so a
+  // strict comparison keeps equal keys in id order)
 #pragma unroll
   for (int i = 1; i < PER; ++i)
 #pragma unroll
@@ -46,12 +54,11 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
       const bool sw = key[j] > key[j - 1];
       const uint32_t tk = sw ? key[j] : key[j - 1];
       const uint32_t bk = sw ? key[j - 1] : key[j];
-      const int ti = sw ? idx[j] : idx[j - 1];
-      const int bi = sw ? idx[j - 1] : idx[j];
       key[j - 1] = tk;
       key[j] = bk;
-      idx[j - 1] = ti;
-      idx[j] = bi;
+      const slot_t a = (slot >> (4 * (j - 1))) & 15u, b = (slot >> (4 * j)) & 15u;
+      const slot_t cleared = slot & ~((slot_t)0xFF << (4 * (j - 1)));
+      slot = sw ? cleared | (b << (4 * (j - 1))) | (a << (4 * j)) : slot;
     }
   int my_id = 0;
   float my_l = 0.0f;
@@ -62,22 +69,21 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
     if (__popcll(cand) == 1) {
       win = __builtin_ctzll(cand);
     } else {
-      const uint32_t wid = wave_min_u32(key[0] == mk ? (uint32_t)idx[0] : 0xFFFFFFFFu);
+      // tied heads: the lowest expert id among them
+      const uint32_t hid = (uint32_t)(lane + kWave * (int)(slot & 15u));
+      const uint32_t wid = wave_min_u32(key[0] == mk ? hid : 0xFFFFFFFFu);
       win = (int)(wid & (kWave - 1));
     }
-    const int wid = __builtin_amdgcn_readlane(idx[0], win);
-    if (lane == j) {
-      my_id = wid;
-      my_l = key_to_float(mk);
-    }
-    if (lane == win) {  // advance this lane's head
+    const int wslot = __builtin_amdgcn_readlane((int)(uint32_t)(slot & 15u), win);
+    const int wid = win + kWave * wslot;
+    my_id = lane == j ? wid : my_id;
+    my_l = lane == j ? key_to_float(mk) : my_l;
+    // the winning lane advances its head; branch-free, so no lane waits on an exec switch
+    const bool adv = lane == win;
 #pragma unroll
-      for (int i = 0; i + 1 < PER; ++i) {
-        key[i] = key[i + 1];
-        idx[i] = idx[i + 1];
-      }
-      key[PER - 1] = 0u;
-    }
+    for (int i = 0; i + 1 < PER; ++i) key[i] = adv ? key[i + 1] : key[i];
+    key[PER - 1] = adv ? 0u : key[PER - 1];
+    slot = adv ? slot >> 4 : slot;
   }
   out_id = my_id;
   out_l = my_l;
