@@ -19,6 +19,7 @@ Also reported on the same JSON line:
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--workload decode|sweep|large|prefill] [--T T]
+                  [--path auto|gather|stream|mfma] [--act path|group_fp8]
 
 Two helpers turn rocprofv3 counters into the HBM traffic the roofline reports:
   python bench.py --copy-calibration
@@ -65,6 +66,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--path", default="auto", choices=["auto", "gather", "stream", "mfma"],
+                    help="force a path instead of the gate's choice")
+    ap.add_argument("--act", default="path", choices=["path", "group_fp8"],
+                    help="activation precision (group_fp8: e4m3 per token and 128 columns on GEMM1)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--sets", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
@@ -236,7 +241,10 @@ def main():
     banks = [W.make_banks(wl, seed=args.seed + 100 * r, device=dev) for r in range(R)]
     cases = [W.make_case(wl, T=T, seed=args.seed + 1000 + i, device=dev, banks=banks[i % R]) for i in range(S)]
     outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
-    nbytes = max(M.workspace_size(T, E, H, I, k), 1)
+    fopts = dict(force_path={"auto": M.PATH_AUTO, "gather": M.PATH_GATHER, "stream": M.PATH_STREAM,
+                             "mfma": M.PATH_MFMA}[args.path],
+                 act_mode=M.ACT_GROUP_FP8 if args.act == "group_fp8" else M.ACT_PATH)
+    nbytes = max(M.workspace_size(T, E, H, I, k, **fopts), 1)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     w13_b, w2_b = banks[0][0].expert_bytes, banks[0][1].expert_bytes
 
@@ -250,7 +258,7 @@ def main():
 
     def step(i):
         c = cases[i]
-        return M.forward(c.hidden, c.logits, c.w13, c.w2, k, out=outs[i], workspace=ws)[1]
+        return M.forward(c.hidden, c.logits, c.w13, c.w2, k, out=outs[i], workspace=ws, **fopts)[1]
 
     info = step(0)
     torch.cuda.synchronize()
@@ -314,7 +322,7 @@ def main():
     for i in range(KS):
         c = cases[i]
         b13, b2 = M.bank_struct(c.w13), M.bank_struct(c.w2)
-        o = M.make_opts()
+        o = M.make_opts(**fopts)
         ri = L.RunInfo()
         L.check(M.lib().moe_fp8_block_forward_timed(
             ctypes.c_void_p(c.hidden.data_ptr()), ctypes.c_void_p(c.logits.data_ptr()), ctypes.byref(b13),
@@ -374,7 +382,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / CPU_REFERENCE_GBS, 2) if unit == "GB/s" and wl == "decode" else None,
-        "dtype": "fp8e4m3 x bf16 -> fp32" if info["path"] != "mfma" else "fp8e4m3 x fp8e4m3 -> fp32",
+        "dtype": {0: "fp8e4m3 x bf16 -> fp32", 1: "fp8e4m3 x fp8e4m3 -> fp32",
+                  2: "fp8e4m3 x fp8e4m3 -> fp32 (gate/up), fp8e4m3 x fp32 (down)"}[info["act_mode"]],
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: E={E} H={H} I={I} top_k={k} T={T}, bf16 hidden/out, fp8-e4m3 banks with "

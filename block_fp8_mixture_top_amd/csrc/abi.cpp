@@ -308,7 +308,7 @@ int moe_fp8_block_route(const float* logits, int T, int E, int top_k, int32_t* i
     const size_t o_act = c.take((size_t)slots * 4);
     const size_t o_n = c.take(4);
     const size_t o_scr = c.take(moe::sort_scratch_bytes(P, E));
-    for (int st = 0; st < moe::route_kernel_count(P); ++st)
+    for (int st = 0; st < moe::route_kernel_count(T, top_k); ++st)
       HIP_CHECK(moe::launch_route_stage(st, logits, T, E, top_k, ids, weights, counts, offsets, sorted_pairs,
                                         at<int32_t>(workspace, o_act), at<int32_t>(workspace, o_n), slots, 0,
                                         nullptr, at<void>(workspace, o_scr), s),
@@ -391,7 +391,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   const bool fused = path == MOE_PATH_GATHER && act_mode == MOE_ACT_PATH && moe::gemm1_fused_route_ok(T, top_k);
   const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
   if (!fused) {
-    for (int st = 0; st < moe::route_kernel_count((int)P); ++st)
+    for (int st = 0; st < moe::route_kernel_count(T, top_k); ++st)
       RUN(st == 0 ? MOE_K_ROUTE : MOE_K_SORT,
           moe::launch_route_stage(st, logits, T, E, top_k, ids, w, counts, offsets, sorted, act, n_act, slots,
                                   tile_m, tile_off, at<void>(workspace, L.scratch), s),

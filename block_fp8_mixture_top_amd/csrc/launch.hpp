@@ -66,7 +66,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 
 // Routing plus the sort: 1 kernel (route and sort in one workgroup) for P <= kSmallSortPairs,
 // else 4 (top-k, then histogram, chunk scan and scatter); stage picks which.
-int route_kernel_count(int P);
+int route_kernel_count(int T, int k);
 hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int k, int32_t* ids, float* w,
                               int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* act, int32_t* n_act,
                               int slots, int tile_m, int32_t* tile_off, void* scratch, hipStream_t s);

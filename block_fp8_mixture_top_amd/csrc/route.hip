@@ -102,10 +102,13 @@ __device__ void wave_active_list(const int* counts, int E, int slots, int32_t* a
   }
 }
 
-// Routing and the whole sort in one workgroup, for small P: 16 waves route the tokens, then
-// counts in LDS, offsets by a wave scan, and one wave walks the pairs in rounds of 64,
-// placing each by its rank among equal experts.
-template <int PER>
+// Routing and the whole sort in one workgroup, for small P. ROUTE: 16 waves route the tokens
+// (each reading its next token's logits while it selects the current one's experts);
+// otherwise the ids come from route_topk_kernel, which spreads the tokens over many CUs (the
+// selection of many tokens on the one CU of this workgroup is bound by its VALU). Then counts
+// in LDS, offsets by a wave scan, and one wave walks the pairs in rounds of 64, placing each
+// by its rank among equal experts.
+template <int PER, bool ROUTE>
 __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ weights,
                                                           int32_t* __restrict__ counts,
@@ -120,15 +123,27 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
   const int nwaves = blockDim.x / kWave;
   const int P = T * k;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  if constexpr (!ROUTE) {
+    for (int p = threadIdx.x; p < P; p += blockDim.x) sid[p] = ids[p];
+  } else {
+  // a wave's tokens are t = wave, wave + nwaves, ...; the next token's logits are read while
+  // the current one is selected (a wave with no token reads the last row and drops it)
+  float fcur[PER], fnext[PER];
+  wave_topk_load<PER>(logits + (size_t)min(wave, T - 1) * E, E, fcur);
   for (int t = wave; t < T; t += nwaves) {
+    wave_topk_load<PER, false>(logits + (size_t)min(t + nwaves, T - 1) * E, E, fnext);
     int id;
-    float w;
-    wave_topk<PER>(logits + (size_t)t * E, E, k, id, w);
+    float l;
+    wave_topk_select<PER>(fcur, E, k, id, l);
+    const float w = wave_topk_weight(l, k);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) fcur[i] = fnext[i];
     if (lane < k) {
       sid[t * k + lane] = id;
       ids[(size_t)t * k + lane] = id;
       weights[(size_t)t * k + lane] = w;
     }
+  }
   }
   __syncthreads();
   for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[sid[p]], 1);
@@ -257,15 +272,29 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   return hipGetLastError();
 }
 
-int route_kernel_count(int P) { return P <= kSmallSortPairs ? 1 : 4; }
+// Up to this many tokens (one per wave of the plan kernel) are routed inside it; more go to
+// route_topk_kernel first.
+constexpr int kPlanRouteTokens = 16;
+
+int route_kernel_count(int T, int k) {
+  const int P = T * k;
+  if (P <= kSmallSortPairs) return T <= kPlanRouteTokens ? 1 : 2;
+  return 4;
+}
 
 hipError_t launch_route_stage(int stage, const float* logits, int T, int E, int k, int32_t* ids, float* w,
                               int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* act, int32_t* n_act,
                               int slots, int tile_m, int32_t* tile_off, void* scratch, hipStream_t s) {
   const int P = T * k;
   if (P <= kSmallSortPairs) {
-    MOE_TOPK_DISPATCH(E, launch_kernel((route_plan_kernel<PER>), dim3(1), dim3(1024), 0, s, logits, T, E, k,
-                                            ids, w, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off));
+    if (T <= kPlanRouteTokens) {
+      MOE_TOPK_DISPATCH(E, launch_kernel((route_plan_kernel<PER, true>), dim3(1), dim3(1024), 0, s, logits, T, E,
+                                         k, ids, w, counts, offsets, sorted, act, n_act, slots, tile_m, tile_off));
+      return hipGetLastError();
+    }
+    if (stage == 0) return launch_route_topk(logits, T, E, k, ids, w, s);
+    launch_kernel((route_plan_kernel<1, false>), dim3(1), dim3(1024), 0, s, logits, T, E, k, ids, w, counts,
+                  offsets, sorted, act, n_act, slots, tile_m, tile_off);
     return hipGetLastError();
   }
   const int nchunks = (P + kChunk - 1) / kChunk;

@@ -8,9 +8,29 @@
 
 namespace moe {
 
-// Selection: lane j < k receives slot j, the expert with the j-th largest logit (ties to the
-// lower id), and that logit. PER = logits held per lane, E <= 64 * PER. A NaN logit reads as
-// -inf, which keeps every id in [0, E). Call with all 64 lanes active.
+// The logits a lane selects from: f[i] = row[lane + 64 i] (entries past E read the last one
+// and are ignored by the selection). All loads are issued together, in bounds and outside
+// any branch. PIN: an empty asm then uses each value, which keeps every load where it is
+// written but also waits for it there; a prefetch leaves it out so that the wait falls at
+// the first use.
+template <int PER, bool PIN = true>
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E, float (&f)[PER]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    f[i] = row[e < E ? e : E - 1];
+  }
+  if constexpr (PIN) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(f[i]));
+  }
+}
+
+// Selection from logits loaded by wave_topk_load: lane j < k receives slot j, the expert
+// with the j-th largest logit (ties to the lower id), and that logit. PER = logits held per
+// lane, E <= 64 * PER. A NaN logit reads as -inf, which keeps every id in [0, E). Call with
+// all 64 lanes active.
 //
 // Each lane first sorts its PER keys best-first, so its current best is always its head
 // (the slot of each sorted key, hence its expert lane + 64 * slot, is kept four bits each
@@ -19,22 +39,11 @@ namespace moe {
 // taken by a min over them), and the winning lane advancing its head with selects instead
 // of a branch.
 template <int PER>
-__device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
-                                              float& out_l) {
+__device__ __forceinline__ void wave_topk_select(const float (&f)[PER], int E, int k, int& out_id, float& out_l) {
   static_assert(PER <= 16, "slot indices are packed four bits each");
   typedef typename std::conditional<PER <= 8, uint32_t, uint64_t>::type slot_t;
   const int lane = lane_id();
   uint32_t key[PER];
-  float f[PER];
-  // All loads first, in bounds and outside any branch, so that they are in flight together
-  // (the empty asm keeps each one unconditional).
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + kWave * i;
-    f[i] = row[e < E ? e : E - 1];
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(f[i]));
   // slot i holds expert lane + 64 i; after sorting, nibble i of `slot` is the slot of the
   // i-th best key of this lane
   slot_t slot = 0;
@@ -87,6 +96,15 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
   }
   out_id = my_id;
   out_l = my_l;
+}
+
+// Load and selection together.
+template <int PER>
+__device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
+                                              float& out_l) {
+  float f[PER];
+  wave_topk_load<PER>(row, E, f);
+  wave_topk_select<PER>(f, E, k, out_id, out_l);
 }
 
 // Weights of the selected slots: lane j < k gets exp(l_j - l_0) / sum_i exp(l_i - l_0),
