@@ -596,11 +596,13 @@ hipError_t launch_gemm2_gather(const float* h, const BankArg& w2, const int32_t*
                                int H, int I, int k, void* out, int out_bf16, hipStream_t s) {
   const int F = k * (I / 16);
   const int mc = (F + kThreads - 1) / kThreads;
-  // rows per workgroup: enough workgroups to cover the chip at small T
+  // rows per workgroup: enough workgroups to cover the chip at small T; from a few tokens on,
+  // more rows per workgroup read each token's h fewer times (16 rows measured 1.5-3% faster
+  // than 8 per forward from T=4 to 64 at H=2048, I=512, top_k=8)
   const bool few = (size_t)T * H < 256 * 8 * 4;
   switch (mc) {
     case 1: return few ? g2g<1, 4>(h, w2, ids, w, T, H, I, k, out, out_bf16, s)
-                       : g2g<1, 8>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
+                       : g2g<1, 16>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
     case 2: return few ? g2g<2, 4>(h, w2, ids, w, T, H, I, k, out, out_bf16, s)
                        : g2g<2, 8>(h, w2, ids, w, T, H, I, k, out, out_bf16, s);
     case 3:
