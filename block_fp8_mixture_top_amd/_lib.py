@@ -116,8 +116,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m block_fp8_mixture_top_amd.build` "
-            "(or __graft_entry__.build()); there is no fallback implementation"
+            f"{path} is missing: build it with `python -m block_fp8_mixture_top_amd.build`; "
+            "there is no fallback implementation"
         )
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():

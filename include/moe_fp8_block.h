@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_ARG = -1,         /* null pointer, non-positive size, top_k out of range, bad enum */
-  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. H % 128) */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement (e.g. H % 16) */
   MOE_ERR_STRIDE = -3,      /* a bank stride smaller than the unpadded extent it must hold */
   MOE_ERR_ALIGN = -4,       /* a pointer or stride that breaks the 16-byte alignment rule */
   MOE_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the size query returned */

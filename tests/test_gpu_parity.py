@@ -128,6 +128,14 @@ def test_route_ties_and_extremes():
     _route_check(torch.randn(3, 1, generator=g), 1, "E=1")
 
 
+@pytest.mark.parametrize("T,E,k", [(16, 256, 8), (17, 256, 8), (64, 64, 8), (512, 128, 1), (40, 1024, 12)])
+def test_route_plan_boundaries(T, E, k):
+    """Around the routing split: up to 16 tokens are routed inside the one-workgroup sort,
+    more are routed by one wave per token first; up to 512 pairs use the one-workgroup sort."""
+    g = torch.Generator().manual_seed(T * 1000 + E + k)
+    _route_check(torch.randn(T, E, generator=g) * 1.5, k, f"T={T} E={E} k={k}")
+
+
 def test_route_empty():
     r = M.route(torch.empty((0, 16), dtype=torch.float32, device=DEV), 4)
     assert r["ids"].numel() == 0
