@@ -139,9 +139,10 @@ int moe_fp8_block_default_opts(moe_opts* opts);
  * VLLM_HPU_MOE_GATHER_RATIO row of its table): GATHER iff T*top_k <= gate_ratio*E,
  * else MFMA iff T*top_k >= mfma_min_tokens_per_expert*E, else STREAM. The defaults are the
  * crossovers measured on MI355X by block_fp8_mixture_top_amd/tune_gate.py (the page's
- * ratio 0.4 was chosen for another device). A forced path is reported unchanged; forward
- * runs STREAM where the gate says MFMA for a shape the MFMA kernels do not take. Writes
- * path, act_mode and slots into *info; no HIP call.
+ * ratio 0.4 was chosen for another device). With act_mode MOE_ACT_GROUP_FP8 the gate
+ * never picks MFMA (STREAM instead). A forced path is reported unchanged; forward runs
+ * STREAM where the gate says MFMA for a shape the MFMA kernels do not take. Writes path,
+ * act_mode and slots into *info; no HIP call.
  */
 int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe_run_info* info);
 
