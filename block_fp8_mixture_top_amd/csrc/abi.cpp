@@ -388,7 +388,10 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   Runner R{s, events, n_events, kinds};
 
   // small gather batches route inside GEMM1; everything else routes and sorts first
-  const bool fused = path == MOE_PATH_GATHER && act_mode == MOE_ACT_PATH && moe::gemm1_fused_route_ok(T, top_k);
+  // group-fp8 activations fuse too, quantised inside GEMM1, where x is not staged in LDS
+  const bool fused = path == MOE_PATH_GATHER &&
+                     (act_mode == MOE_ACT_PATH ? moe::gemm1_fused_route_ok(T, top_k)
+                                               : act_mode == MOE_ACT_GROUP_FP8 && moe::gemm1_fused_qx_ok(T, top_k, H));
   const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
   if (!fused) {
     for (int st = 0; st < moe::route_kernel_count(T, top_k); ++st)
@@ -402,7 +405,9 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   if (path == MOE_PATH_GATHER || path == MOE_PATH_STREAM) {
     float* h = at<float>(workspace, L.h);
     moe::Gemm1Args g1{hidden, logits, T, E, H, I, top_k, slots, b13, plan, h, fused ? 1 : 0, ids, w};
-    if (act_mode == MOE_ACT_GROUP_FP8) {
+    if (act_mode == MOE_ACT_GROUP_FP8 && fused) {
+      g1.qx = 1;
+    } else if (act_mode == MOE_ACT_GROUP_FP8) {
       // one quantisation row per (token, 128 columns)
       g1.xq = at<uint8_t>(workspace, L.xq);
       g1.xs = at<float>(workspace, L.xs);

@@ -89,8 +89,13 @@ struct Gemm1Args {
   // routing not fused)
   const uint8_t* xq = nullptr;
   const float* xs = nullptr;
+  // nonzero (with fused routing): the same e4m3 activations, quantised inside GEMM1 from the
+  // bf16 hidden states
+  int qx = 0;
 };
 bool gemm1_fused_route_ok(int T, int k);
+// Fused routing with the e4m3 activations quantised inside GEMM1 (not with x staged in LDS).
+bool gemm1_fused_qx_ok(int T, int k, int H);
 hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s);
 
 // Whether the token-major GEMM2 supports this (k, I) (its per-thread register budget).

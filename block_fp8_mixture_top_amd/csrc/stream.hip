@@ -45,7 +45,10 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // A8 (PER == 0 only): the activations are e4m3 codes xq with one scale xs per (token,
 // 128-column group); a 16-code chunk lies in one group, so its block product takes the
 // weight block scale times the group's activation scale.
-template <int LPR, int MCH, int RP, int PER, bool XL = false, bool A8 = false>
+// QX (PER > 0, not XL): the same e4m3 activations, quantised here from the bf16 x in
+// registers: a group's 8 chunks sit in 8 neighbouring lanes of a lane group, so its amax is
+// a 3-step butterfly; scale and codes are computed as the row quantiser does.
+template <int LPR, int MCH, int RP, int PER, bool XL = false, bool A8 = false, bool QX = false>
 __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* __restrict__ hidden,
                                                                const float* __restrict__ logits, int T, int E,
                                                                BankArg w13, Plan plan, int H, int I, int k,
@@ -54,6 +57,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
                                                                const uint8_t* __restrict__ xq,
                                                                const float* __restrict__ xs) {
   static_assert(!A8 || (PER == 0 && !XL), "e4m3 activations come with a routing plan");
+  static_assert(!QX || (PER > 0 && !XL && !A8), "in-register quantisation is for fused routing");
   constexpr int GPW = kWave / LPR;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int grp = lane / LPR, gl = lane % LPR;
@@ -71,7 +75,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   // x of token 0, issued before routing when T == 1 (XL: 16-byte pieces q = tid + kThreads*j
   // of the row, bound for LDS)
   u32x4 x0[XL ? 1 : MCH], x1[XL || A8 ? 1 : MCH];
-  float xsm[A8 ? MCH : 1];  // A8: the activation scale of each chunk's group
+  float xsm[A8 || QX ? MCH : 1];  // A8, QX: the activation scale of each chunk's group
+  u32x4 xq8[QX ? MCH : 1];        // QX: the chunk's e4m3 codes
   constexpr int XQ = XL ? (MCH * kWave * 2 + kThreads - 1) / kThreads : 1;
   __shared__ __align__(16) uint8_t s_x[XL ? MCH * kWave * 32 : 16];
   u32x4 xr[XQ];
@@ -243,6 +248,28 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
         }
       }
     }
+    if constexpr (QX) {
+      // every lane quantises its chunks (chunks past NC form whole groups of their own,
+      // unused), so the butterfly runs with all lanes active
+#pragma unroll
+      for (int m = 0; m < MCH; ++m) {
+        const uint32_t w[8] = {x0[m].x, x0[m].y, x0[m].z, x0[m].w, x1[m].x, x1[m].y, x1[m].z, x1[m].w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(w[q])), __builtin_fabsf(bf16_hi(w[q]))));
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, kWave));
+        const float sx = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+        uint32_t cw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          cw[q] = enc2(bf16_lo(w[2 * q]) / sx, bf16_hi(w[2 * q]) / sx) |
+                  (enc2(bf16_lo(w[2 * q + 1]) / sx, bf16_hi(w[2 * q + 1]) / sx) << 16);
+        xq8[m] = u32x4{cw[0], cw[1], cw[2], cw[3]};
+        xsm[m] = sx;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
       float g = 0.0f, u = 0.0f;
@@ -260,6 +287,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
           if constexpr (A8) {
             g = __builtin_fmaf(sg[m] * xsm[m], dot16_e4m3(cg[r][m], x0[m]), g);
             u = __builtin_fmaf(su[m] * xsm[m], dot16_e4m3(cu[r][m], x0[m]), u);
+          } else if constexpr (QX) {
+            g = __builtin_fmaf(sg[m] * xsm[m], dot16_e4m3(cg[r][m], xq8[m]), g);
+            u = __builtin_fmaf(su[m] * xsm[m], dot16_e4m3(cu[r][m], xq8[m]), u);
           } else {
             g = __builtin_fmaf(sg[m], dot16_bf16(cg[r][m], xa, xb), g);
             u = __builtin_fmaf(su[m], dot16_bf16(cu[r][m], xa, xb), u);
@@ -487,6 +517,14 @@ template <int LPR, int MCH, int RP, int PER>
 hipError_t g1(const Gemm1Args& a, hipStream_t s) {
   const int rows = (kThreads / kWave) * (kWave / LPR) * RP;
   dim3 grid((a.I + rows - 1) / rows, a.slots);
+  if constexpr (PER > 0) {
+    if (a.qx) {  // the caller has checked that the XL variant does not apply (gemm1_fused_qx_ok)
+      launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER, false, false, true>), grid, dim3(kThreads), 0, s,
+                    a.hidden, a.logits, a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out, a.xq,
+                    a.xs);
+      return hipGetLastError();
+    }
+  }
   if constexpr (PER > 0 && LPR == kWave && MCH >= 4) {
     if (a.T == 1) {
       launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER, true>), grid, dim3(kThreads), 0, s, a.hidden, a.logits,
@@ -529,6 +567,12 @@ hipError_t g2e(const float* h, const BankArg& w, const Plan& p, int slots, int H
 }  // namespace
 
 bool gemm1_fused_route_ok(int T, int k) { return T >= 1 && T <= kFuseTokens && T * k <= kFuseMaxPairs; }
+
+bool gemm1_fused_qx_ok(int T, int k, int H) {
+  const Layout L = pick_layout(H);
+  const bool xl = T == 1 && L.lpr == kWave && L.mch >= 4;  // x staged in LDS: not with QX
+  return gemm1_fused_route_ok(T, k) && !xl && H % kScaleBlock == 0;
+}
 
 hipError_t launch_gemm1_w8a16(const Gemm1Args& a, hipStream_t s) {
   const Layout L = pick_layout(a.H);
