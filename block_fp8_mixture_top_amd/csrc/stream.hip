@@ -261,11 +261,19 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
 #pragma unroll
         for (int off = 1; off < 8; off <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, kWave));
         const float sx = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+        // x / sx rounded to float, as the row quantiser divides, but by one double reciprocal
+        // per group: float((double)x * (1 / (double)sx)) equals the correctly rounded float
+        // quotient for bf16 x. The double product is within 2^-52 of x / sx, while x / sx is
+        // never a float rounding midpoint (an odd 25-bit significand times sx cannot fit the
+        // 8 bits of x) and, when not one, is at least 2^-49 away from any (x - m * sx is a
+        // multiple of the 49-bit product's ulp), so both round to the same float.
+        const double rx = 1.0 / (double)sx;
+        auto qd = [&](float v) { return (float)((double)v * rx); };
         uint32_t cw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          cw[q] = enc2(bf16_lo(w[2 * q]) / sx, bf16_hi(w[2 * q]) / sx) |
-                  (enc2(bf16_lo(w[2 * q + 1]) / sx, bf16_hi(w[2 * q + 1]) / sx) << 16);
+          cw[q] = enc2(qd(bf16_lo(w[2 * q])), qd(bf16_hi(w[2 * q]))) |
+                  (enc2(qd(bf16_lo(w[2 * q + 1])), qd(bf16_hi(w[2 * q + 1]))) << 16);
         xq8[m] = u32x4{cw[0], cw[1], cw[2], cw[3]};
         xsm[m] = sx;
       }

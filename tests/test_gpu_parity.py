@@ -304,6 +304,20 @@ def test_group_fp8_activations(path, T):
     check_out(out, oracle_out(c, act_mode=2), 2, f"group fp8 {path} T={T}")
 
 
+@pytest.mark.parametrize("H", [2048, 640])
+def test_group_fp8_in_register_quantisation_matches_row_quantiser(H):
+    """At 4 tokens GEMM1 routes and quantises x itself; at 5 the separate row quantiser
+    (bit-exact against the oracle) does it. A token's output does not depend on the others,
+    so the first 4 rows of the 5-token forward must equal the 4-token forward bit for bit."""
+    c = W.make_case("decode", T=5, seed=91 + H, device=DEV, E=32, H=H, I=256, top_k=4)
+    say("group fp8 fused vs row quantiser", H)
+    kw = dict(out_dtype=torch.float32, force_path=M.PATH_GATHER, act_mode=M.ACT_GROUP_FP8)
+    five, i5 = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, **kw)
+    four, i4 = M.forward(c.hidden[:4].contiguous(), c.logits[:4].contiguous(), c.w13, c.w2, c.top_k, **kw)
+    assert i4["kernels"] < i5["kernels"]  # the fused path ran at 4 tokens
+    assert torch.equal(four, five[:4])
+
+
 def test_group_fp8_decode_and_grouped():
     """The decode workload (GATHER, bf16 out) and T=4096, where the gate takes STREAM instead
     of MFMA (sampled rows)."""
