@@ -38,6 +38,15 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
 
 // ---------------------------------------------------------------- per-row quantisation
 
+// x / s rounded to float, for a float x and a positive float s given as rs = 1 / (double)s:
+// the double product float((double)x * rs) is within 2^-52 of x / s, and x / s is never a
+// float rounding midpoint (an odd 25-bit significand times s cannot fit the 24 bits of x)
+// and otherwise lies at least 2^-49 from one (x - m * s is a multiple of the 49-bit product's
+// ulp), so it rounds to the correctly rounded float quotient that a division gives, at the
+// cost of one double multiply per value and one double division per row. Quotients small
+// enough to be float subnormals round to the e4m3 zero either way.
+__device__ __forceinline__ float quot(float x, double rs) { return (float)((double)x * rs); }
+
 // One wave per row of bf16: amax, scale = amax/448 (1 if zero), codes = e4m3(x/scale).
 // Lane l holds the 8-value pieces l, l + 64, ... of the row: IT of them, all read up front
 // (pieces past the row end read its last piece and are ignored), so the row is read from
@@ -69,6 +78,7 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
   }
   amax = wave_max(amax);
   const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+  const double rs = 1.0 / (double)s;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int c = lane * 8 + it * kWave * 8;
@@ -77,8 +87,8 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
     uint32_t out[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t a = enc2(bf16_lo(w[2 * q]) / s, bf16_hi(w[2 * q]) / s);
-      const uint32_t b = enc2(bf16_lo(w[2 * q + 1]) / s, bf16_hi(w[2 * q + 1]) / s);
+      const uint32_t a = enc2(quot(bf16_lo(w[2 * q]), rs), quot(bf16_hi(w[2 * q]), rs));
+      const uint32_t b = enc2(quot(bf16_lo(w[2 * q + 1]), rs), quot(bf16_hi(w[2 * q + 1]), rs));
       out[q] = a | (b << 16);
     }
     *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(out[0], out[1]);
@@ -114,13 +124,14 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
   }
   amax = wave_max(amax);
   const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+  const double rs = 1.0 / (double)s;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int c = lane * 8 + it * kWave * 8;
     if (c >= cols) continue;
     const f32x4 a = va[it], b = vb[it];
-    const uint32_t lo = enc2(a[0] / s, a[1] / s) | (enc2(a[2] / s, a[3] / s) << 16);
-    const uint32_t hi = enc2(b[0] / s, b[1] / s) | (enc2(b[2] / s, b[3] / s) << 16);
+    const uint32_t lo = enc2(quot(a[0], rs), quot(a[1], rs)) | (enc2(quot(a[2], rs), quot(a[3], rs)) << 16);
+    const uint32_t hi = enc2(quot(b[0], rs), quot(b[1], rs)) | (enc2(quot(b[2], rs), quot(b[3], rs)) << 16);
     *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(lo, hi);
   }
   if (lane == 0) scales[row] = s;
