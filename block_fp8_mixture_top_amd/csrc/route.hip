@@ -19,12 +19,13 @@ namespace {
 template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ __align__(16) uint64_t s_cand[256 / kWave][kWave];
   const int lane = lane_id();
   const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
   if (t >= T) return;
   int id;
   float w;
-  wave_topk<PER>(logits + (size_t)t * E, E, k, id, w);
+  wave_topk<PER>(logits + (size_t)t * E, E, k, s_cand[threadIdx.x / kWave], id, w);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     weights[(size_t)t * k + lane] = w;
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
   __shared__ int cnt[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS];
   __shared__ int sid[kSmallSortPairs];
+  __shared__ __align__(16) uint64_t s_cand[ROUTE ? 1024 / kWave : 1][kWave];
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int nwaves = blockDim.x / kWave;
   const int P = T * k;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
     wave_topk_load<PER, false>(logits + (size_t)min(t + nwaves, T - 1) * E, E, fnext);
     int id;
     float l;
-    wave_topk_select<PER>(fcur, E, k, id, l);
+    wave_topk_select_lds<PER>(fcur, E, k, s_cand[wave], id, l);
     const float w = wave_topk_weight(l, k);
 #pragma unroll
     for (int i = 0; i < PER; ++i) fcur[i] = fnext[i];

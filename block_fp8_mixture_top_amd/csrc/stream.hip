@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   __shared__ int s_ids[PER > 0 ? kFuseMaxPairs : 1];
   __shared__ int s_pairs[PER > 0 ? kFuseMaxPairs : 1];
   __shared__ uint32_t s_bits[MAX_EXPERTS / 32];
+  __shared__ __align__(16) uint64_t s_cand[PER > 0 ? kThreads / kWave : 1][kWave];  // top-k candidates
   __shared__ int s_e, s_m;
   // x of token 0, issued before routing when T == 1 (XL: 16-byte pieces q = tid + kThreads*j
   // of the row, bound for LDS)
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
           x1[m] = ld16((const uint8_t*)hidden + (size_t)c * 32 + 16);
         }
       }
-      wave_topk_ids<PER>(logits, E, k, my_id, my_l);
+      wave_topk_ids_lds<PER>(logits, E, k, s_cand[wave], my_id, my_l);
       route_wave = wave == 0;
       int rank = 0;
       for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(my_id, j) < my_id ? 1 : 0;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
       const int P = T * k;
       if (threadIdx.x < MAX_EXPERTS / 32) s_bits[threadIdx.x] = 0u;
       if (wave < T) {
-        wave_topk_ids<PER>(logits + (size_t)wave * E, E, k, my_id, my_l);
+        wave_topk_ids_lds<PER>(logits + (size_t)wave * E, E, k, s_cand[wave], my_id, my_l);
         route_wave = true;
         route_tok = wave;
         if (lane < k) s_ids[wave * k + lane] = my_id;

@@ -98,6 +98,90 @@ __device__ __forceinline__ void wave_topk_select(const float (&f)[PER], int E, i
   out_l = my_l;
 }
 
+// Keeps the compiler from moving one wave's LDS accesses across this point; the LDS itself
+// serves a wave's accesses in the order they are issued.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The same selection as wave_topk_select, for k <= 8, by filtering and then ranking the few
+// logits that pass. `cand` is 64 entries of LDS (16-byte aligned) that belong to this wave
+// alone; their contents are overwritten.
+//
+// Filter: lanes 8q .. 8q+7 form group q (q < 8). The eight group maxima are eight distinct
+// logits, so the smallest of them, t, is at most the k-th largest logit when k <= 8, and
+// every expert to be selected has a logit >= t (about 20 of 256 logits pass for Gaussian or
+// uniform logits).
+// Rank: each passing expert is stored as key << 32 | ~id, which makes a larger logit, or an
+// equal logit with a lower id, the larger integer; the number of larger entries is its slot.
+// When more than 64 logits pass (widely tied logits), or k > 8, the round-based selection
+// runs instead.
+template <int PER>
+__device__ __forceinline__ void wave_topk_select_lds(const float (&f)[PER], int E, int k, uint64_t* cand,
+                                                     int& out_id, float& out_l) {
+  if (k > 8) {
+    wave_topk_select<PER>(f, E, k, out_id, out_l);
+    return;
+  }
+  const int lane = lane_id();
+  uint32_t key[PER];
+  uint32_t g = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    const float v = f[i] != f[i] ? -__builtin_inff() : f[i];
+    key[i] = e < E ? order_key(v) : 0u;  // every real logit has a key > 0
+    g = max(g, key[i]);
+  }
+  g = max(g, dpp_u32<0x111, 0xF, 0xF>(0u, g));  // row_shr:1
+  g = max(g, dpp_u32<0x112, 0xF, 0xF>(0u, g));  // row_shr:2
+  g = max(g, dpp_u32<0x114, 0xF, 0xF>(0u, g));  // row_shr:4; lane 8q+7 now holds group q's max
+  uint32_t t = 0xFFFFFFFFu;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) t = min(t, (uint32_t)__builtin_amdgcn_readlane((int)g, 8 * q + 7));
+  t = max(t, 1u);  // with E < 64 a group may hold padding only; then every real logit passes
+  uint64_t m[PER];
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    m[i] = __ballot(key[i] >= t);
+    n += __popcll(m[i]);
+  }
+  if (n > kWave) {
+    wave_topk_select<PER>(f, E, k, out_id, out_l);
+    return;
+  }
+  // compact the candidates into cand[0, n) and zero-fill to a multiple of 8
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int below =
+        (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[i], 0u));
+    if (key[i] >= t) cand[base + below] = ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)(lane + kWave * i));
+    base += __popcll(m[i]);
+  }
+  const int n8 = (n + 7) & ~7;
+  if (lane >= n && lane < n8) cand[lane] = 0ull;  // below every real entry
+  wave_lds_sync();
+  const uint64_t mine = cand[lane];  // lanes >= n hold no candidate; their rank is unused
+  int rank = 0;
+  for (int j = 0; j < n8; j += 8) {
+    uint64_t c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) c[q] = cand[j + q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rank += c[q] > mine ? 1 : 0;
+  }
+  wave_lds_sync();
+  if (lane < n && rank < k) cand[rank] = mine;
+  wave_lds_sync();
+  const uint64_t r = cand[lane < k ? lane : 0];
+  out_id = lane < k ? (int)~(uint32_t)r : 0;
+  out_l = lane < k ? key_to_float((uint32_t)(r >> 32)) : 0.0f;
+}
+
 // Load and selection together.
 template <int PER>
 __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
@@ -105,6 +189,15 @@ __device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int
   float f[PER];
   wave_topk_load<PER>(row, E, f);
   wave_topk_select<PER>(f, E, k, out_id, out_l);
+}
+
+// Load and the filtered selection (`cand` as for wave_topk_select_lds).
+template <int PER>
+__device__ __forceinline__ void wave_topk_ids_lds(const float* __restrict__ row, int E, int k, uint64_t* cand,
+                                                  int& out_id, float& out_l) {
+  float f[PER];
+  wave_topk_load<PER>(row, E, f);
+  wave_topk_select_lds<PER>(f, E, k, cand, out_id, out_l);
 }
 
 // Weights of the selected slots: lane j < k gets exp(l_j - l_0) / sum_i exp(l_i - l_0),
@@ -123,11 +216,12 @@ __device__ __forceinline__ float wave_topk_weight(float my_l, int k) {
   return (float)(ex / tot);
 }
 
-// Both: ids and weights.
+// Both: ids and weights (`cand` as for wave_topk_select_lds).
 template <int PER>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& out_id, float& out_w) {
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, uint64_t* cand, int& out_id,
+                                          float& out_w) {
   float l;
-  wave_topk_ids<PER>(row, E, k, out_id, l);
+  wave_topk_ids_lds<PER>(row, E, k, cand, out_id, l);
   out_w = wave_topk_weight(l, k);
 }
 

@@ -126,6 +126,17 @@ def test_route_ties_and_extremes():
     _route_check(big, 32, "E=1024 k=32")
     _route_check(torch.randn(5000, 1024, generator=g), 1, "E=1024 k=1 multi-block sort")
     _route_check(torch.randn(3, 1, generator=g), 1, "E=1")
+    # E=256, k=8: coarse ties that the candidate filter ranks by id (T=40: one wave per
+    # token), and rows of one value, where too many logits pass the filter and the
+    # round-based selection runs (T=4: routed inside the sort)
+    coarse = (torch.randn(40, 256, generator=g) * 2).round() / 2
+    _route_check(coarse, 8, "E=256 coarse ties")
+    _route_check(coarse[:4], 8, "E=256 coarse ties, T=4")
+    flat = torch.full((4, 256), 0.5)
+    flat[1, 200] = 1.0
+    flat[2, ::3] = -0.0
+    _route_check(flat, 8, "E=256 equal rows")
+    _route_check(flat.repeat(10, 1), 8, "E=256 equal rows, T=40")
 
 
 @pytest.mark.parametrize("T,E,k", [(16, 256, 8), (17, 256, 8), (64, 64, 8), (512, 128, 1), (40, 1024, 12)])
@@ -471,6 +482,25 @@ def test_degenerate_routings(path, E, k, T):
     res = oracle_out(c, act_mode=act)
     assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
     check_out(out, res, act, f"degenerate {path} E={E} k={k}")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_fused_routing_with_ties(T):
+    """Decode GEMM1 routes inside the kernel; tied logits must select the lower ids, both when
+    few logits tie (ranked candidates) and when a whole row ties (round-based selection)."""
+    c = W.make_case("decode", T=T, seed=91 + T, device=DEV, H=256, I=128)
+    g = torch.Generator().manual_seed(92 + T)
+    tied = (torch.randn(T, c.logits.shape[1], generator=g) * 2).round() / 2
+    if T > 1:
+        tied[1] = 0.25
+    c.logits = tied.to(DEV)
+    say("fused routing ties", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS["gather"], return_routing=True)
+    res = oracle_out(c, act_mode=0)
+    assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
+    assert np.array_equal(info["weights"].cpu().numpy(), res["w32"])
+    check_out(out, res, 0, f"fused routing ties T={T}")
 
 
 @pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
