@@ -31,7 +31,7 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // consecutive row pairs (gate i, up I+i) of the slot's expert, loads their codes once and
 // applies them to every token routed to that expert.
 //
-// PER > 0 routes inside the kernel (wave_topk_ids with PER logits per lane):
+// PER > 0 routes inside the kernel (wave_topk_ids_lds with PER logits per lane):
 //   T == 1: every wave routes the token itself, with no barrier; the slot-th expert in
 //   ascending id is the one whose id ranks `slot` among the token's top_k distinct ids.
 //   2 <= T <= 4: one wave per token, an LDS bitmap of routed experts gives the slot-th one

@@ -182,15 +182,6 @@ __device__ __forceinline__ void wave_topk_select_lds(const float (&f)[PER], int 
   out_l = lane < k ? key_to_float((uint32_t)(r >> 32)) : 0.0f;
 }
 
-// Load and selection together.
-template <int PER>
-__device__ __forceinline__ void wave_topk_ids(const float* __restrict__ row, int E, int k, int& out_id,
-                                              float& out_l) {
-  float f[PER];
-  wave_topk_load<PER>(row, E, f);
-  wave_topk_select<PER>(f, E, k, out_id, out_l);
-}
-
 // Load and the filtered selection (`cand` as for wave_topk_select_lds).
 template <int PER>
 __device__ __forceinline__ void wave_topk_ids_lds(const float* __restrict__ row, int E, int k, uint64_t* cand,
