@@ -147,6 +147,18 @@ def test_route_plan_boundaries(T, E, k):
     _route_check(torch.randn(T, E, generator=g) * 1.5, k, f"T={T} E={E} k={k}")
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 40, 8), (3, 100, 8), (20, 300, 8), (33, 512, 8), (70, 1024, 8),
+                                   (5, 1024, 7), (2, 8, 8)])
+def test_route_filtered_top_k_shapes(T, E, k):
+    """The candidate-filter top-k (k <= 8) across expert counts: padding lanes (E < 64 and
+    E not a multiple of 64), 2 to 16 logits per lane, one wave per token and routing inside
+    the sort; plain and coarsely tied logits."""
+    g = torch.Generator().manual_seed(T * 7 + E + k)
+    plain = torch.randn(T, E, generator=g) * 1.5
+    _route_check(plain, k, f"T={T} E={E} k={k}")
+    _route_check((plain * 2).round() / 2, k, f"T={T} E={E} k={k} tied")
+
+
 def test_route_empty():
     r = M.route(torch.empty((0, 16), dtype=torch.float32, device=DEV), 4)
     assert r["ids"].numel() == 0
