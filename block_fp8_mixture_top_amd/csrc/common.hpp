@@ -98,6 +98,14 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
 }
 
+// Keeps the compiler from moving one wave's LDS accesses across this point; the LDS itself
+// serves a wave's accesses in the order they are issued.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0x111, 0xF, 0xF>(0u, v));  // row_shr:1
   v = max(v, dpp_u32<0x112, 0xF, 0xF>(0u, v));  // row_shr:2

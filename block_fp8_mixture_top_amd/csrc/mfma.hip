@@ -521,7 +521,9 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 // streams its own w2 rows, (chunk, K block) after (chunk, K block), through a private
 // kRing2-deep LDS ring with kRing2 - 1 stages in flight and no barriers. Each pair's y row
 // = s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
-// applies the router weights.
+// applies the router weights. The fp16 values of 16 pairs x 64 features pass through a 2 KB
+// LDS area of the wave so that each lane stores 32 contiguous bytes: 8 store instructions
+// per chunk instead of 64 two-byte ones, all of which count against the w2 copies' wait.
 constexpr int kRing2 = 4;
 
 // Wait for the copy of the stage issued `later` stages before the newest one: the loads of
@@ -549,6 +551,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   static_assert(kRing2 - 1 <= 3, "wait_stage covers up to three younger stages");
   __shared__ __align__(16) uint8_t ring[4 * kRing2 * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
+  __shared__ __align__(16) _Float16 s_y[4][16 * 64];  // per wave: pairs 4kq+q x 64 features
 
   const int nitems = plan.tile_off[E] * 2;
   const int L = xcd_item(blockIdx.x, nitems);
@@ -606,6 +609,15 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
       hsc[pt][q] = hs[pos0 + (ok ? r : 0)];
       prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
     }
+  // the y stores from LDS: lane (srow, sseg) writes features 16 sseg .. 16 sseg + 15 of pair
+  // pt * 16 + srow
+  const int srow = lane >> 2, sseg = lane & 3;
+  int prow_st[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    const int r = pt * 16 + srow;
+    prow_st[pt] = r < nvalid ? plan.sorted[pos0 + r] : -1;
+  }
   wait_vm<0>();  // everyone's h codes and the block scales are in after the barrier
   __syncthreads();
   i32x8 a[KB][4];
@@ -628,7 +640,11 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const int st = c * KB + kb;
     // stage st has landed once at most min(kRing2 - 2, nst - 1 - st) younger stages remain
     wait_stage(min(kRing2 - 2, nst - 1 - st));
-    // the slot of stage st - 1 is free: its operands were read (and waited for) last step
+    // the slot of stage st - 1 is refilled next, so this wave's reads of it must have
+    // completed: the compiler waits for them only where their values are used, which it may
+    // schedule after this refill, and nothing orders a pending LDS read before direct loads
+    // into the same bytes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (st + kRing2 - 1 < nst) issue(st + kRing2 - 1);
     if (kb == 0) {
 #pragma unroll
@@ -662,8 +678,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     if (kb == KB - 1) {
       // y of pair (pt, 4kq+q), features n0 .. n0+63, held by the 16 lanes of row kq (r16)
       // times FT: stored in fp16 with one power-of-two exponent per (pair, 64 features)
+      _Float16* sy = s_y[wave];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float v[FT];
@@ -679,12 +696,20 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
           m = max(m, dpp_u32<0x128, 0xF, 0xF>(0u, m));  // row_ror:8
           const int ey = y_exponent(m);
           const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
-          if (prow[pt][q] < 0) continue;
-          _Float16* yr = y + (size_t)prow[pt][q] * H + n0 + r16;
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) yr[ft * 16] = (_Float16)(v[ft] * down);
-          if (r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
+          for (int ft = 0; ft < FT; ++ft) sy[(kq * 4 + q) * 64 + ft * 16 + r16] = (_Float16)(v[ft] * down);
+          if (prow[pt][q] >= 0 && r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
         }
+        wave_lds_sync();
+        const u32x4 lo = *(const u32x4*)(sy + srow * 64 + sseg * 16);
+        const u32x4 hi = *(const u32x4*)(sy + srow * 64 + sseg * 16 + 8);
+        if (prow_st[pt] >= 0) {
+          u32x4* yr = (u32x4*)(y + (size_t)prow_st[pt] * H + n0 + sseg * 16);
+          yr[0] = lo;
+          yr[1] = hi;
+        }
+        wave_lds_sync();  // the reads are done before the next pair tile overwrites the area
+      }
     }
   }
   }

@@ -98,14 +98,6 @@ __device__ __forceinline__ void wave_topk_select(const float (&f)[PER], int E, i
   out_l = my_l;
 }
 
-// Keeps the compiler from moving one wave's LDS accesses across this point; the LDS itself
-// serves a wave's accesses in the order they are issued.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // The same selection as wave_topk_select, for k <= 8, by filtering and then ranking the few
 // logits that pass. `cand` is 64 entries of LDS (16-byte aligned) that belong to this wave
 // alone; their contents are overwritten.
