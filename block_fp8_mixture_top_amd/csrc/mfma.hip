@@ -523,7 +523,8 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 // = s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
 // applies the router weights. The fp16 values of 16 pairs x 64 features pass through a 2 KB
 // LDS area of the wave so that each lane stores 32 contiguous bytes: 8 store instructions
-// per chunk instead of 64 two-byte ones, all of which count against the w2 copies' wait.
+// per chunk instead of 64 two-byte ones, all of which count against the w2 copies' wait. The
+// 64 exponents of a chunk go the same way, one byte store instead of 16.
 constexpr int kRing2 = 4;
 
 // Wait for the copy of the stage issued `later` stages before the newest one: the loads of
@@ -552,6 +553,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   __shared__ __align__(16) uint8_t ring[4 * kRing2 * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
   __shared__ __align__(16) _Float16 s_y[4][16 * 64];  // per wave: pairs 4kq+q x 64 features
+  __shared__ int8_t s_e[4][64];                       // per wave: the y exponents of a chunk
 
   const int nitems = plan.tile_off[E] * 2;
   const int L = xcd_item(blockIdx.x, nitems);
@@ -618,6 +620,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const int r = pt * 16 + srow;
     prow_st[pt] = r < nvalid ? plan.sorted[pos0 + r] : -1;
   }
+  const int prow_e = lane < nvalid ? plan.sorted[pos0 + lane] : -1;  // lane's pair for the exponents
   wait_vm<0>();  // everyone's h codes and the block scales are in after the barrier
   __syncthreads();
   i32x8 a[KB][4];
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
           const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) sy[(kq * 4 + q) * 64 + ft * 16 + r16] = (_Float16)(v[ft] * down);
-          if (prow[pt][q] >= 0 && r16 == 0) yexp[(size_t)prow[pt][q] * (H / 64) + n0 / 64] = (int8_t)ey;
+          if (r16 == 0) s_e[wave][pt * 16 + kq * 4 + q] = (int8_t)ey;
         }
         wave_lds_sync();
         const u32x4 lo = *(const u32x4*)(sy + srow * 64 + sseg * 16);
@@ -710,6 +713,10 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
         }
         wave_lds_sync();  // the reads are done before the next pair tile overwrites the area
       }
+      // one byte store for the chunk's 64 exponents instead of one per (pair tile, q)
+      const int8_t ee = s_e[wave][lane];
+      if (prow_e >= 0) yexp[(size_t)prow_e * (H / 64) + n0 / 64] = ee;
+      wave_lds_sync();
     }
   }
   }
