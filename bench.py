@@ -7,16 +7,24 @@ The metric is routed-weight GB/s: the bytes of the distinct experts each forward
 to (codes plus their block scales), divided by the time per forward.
 
 A step is one whole forward (route, sort, GEMM1 + silu*up, GEMM2 + combine) over one
-batch of synthetic input already resident in HBM. Steps rotate over 64 pre-drawn
+batch of synthetic input already resident in HBM. Steps rotate over up to 64 pre-drawn
 routings and 4 replicas of the banks (about 3.2 GB), so the 256 MB Infinity Cache cannot
-serve a routed expert from an earlier step. The steps are captured into one HIP graph
-(64 forwards) and replayed back to back.
+serve a routed expert from an earlier step. K steps are captured into HIP graphs: one of
+S = min(64, K) forwards, replayed K // S times, and one of the K % S remaining forwards;
+each is replayed once before the timed region. The timed region is queued behind a spin
+kernel, so it measures the GPU running K forwards back to back (HIP events on the stream),
+not the host's graph launches.
 
 Also reported on the same JSON line:
   roofline      the dominant kernel's algorithmic bytes per launch over its mean duration,
                 timed with HIP events the library attaches to that kernel's dispatch on
                 its own stream (moe_fp8_block_forward_timed), against the 8 TB/s HBM peak;
-  cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample.
+  cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample;
+  prefill_T4096, prefill_T16384, large_T1
+                the same measurement (fewer steps) at the prefill workload (E=256, H=2048,
+                I=512, top_k=8, uniform logits; tokens/s and % of fp8 MFMA peak) and the
+                large-expert decode workload (H=7168, I=2048; routed GB/s), each with its
+                dominant kernel's roofline (--no-extra skips them).
 
   python bench.py [--steps K] [--warmup W] [--workload decode|sweep|large|prefill] [--T T]
                   [--path auto|gather|stream|mfma] [--act path|group_fp8]
@@ -75,6 +83,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and large-expert figures")
     ap.add_argument("--kernel-steps", type=int, default=64, help="steps timed per kernel with events")
     ap.add_argument("--copy-calibration", action="store_true", help="copy 1 GiB three times and exit")
     ap.add_argument("--traffic-record", action="store_true", help="write profiles/traffic_<kernel>_<workload>.json")
@@ -209,6 +218,200 @@ def committed_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _forward_timed_kernels(M, L, hip, cases, outs, ws, fopts, T, E, H, I, k, nk, steps):
+    """Per-kernel durations (ms per forward, summed over a kind's kernels) from HIP events the
+    library attaches to each kernel's dispatch on the stream the kernels run on. A spin
+    kernel first lets the host enqueue every forward before the GPU reaches them."""
+    import numpy as np
+    import torch
+
+    evs = [hip.events(2 * nk) for _ in range(steps)]
+    kinds = (ctypes.c_int32 * nk)()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(steps):
+        c = cases[i % len(cases)]
+        b13 = M.bank_struct(c.w13, E, 2 * I, H, c.hidden.device)
+        b2 = M.bank_struct(c.w2, E, H, I, c.hidden.device)
+        o = M.make_opts(**fopts)
+        ri = L.RunInfo()
+        L.check(M.lib().moe_fp8_block_forward_timed(
+            ctypes.c_void_p(c.hidden.data_ptr()), ctypes.c_void_p(c.logits.data_ptr()), ctypes.byref(b13),
+            ctypes.byref(b2), T, E, H, I, k, ctypes.c_void_p(outs[i % len(outs)].data_ptr()), L.MOE_BF16,
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None, None, ctypes.byref(o), ctypes.byref(ri),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), evs[i], 2 * nk, kinds))
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for j in range(nk):
+        name = L.KERNEL_NAMES.get(kinds[j], str(kinds[j]))
+        d = [hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(steps)]
+        per_kernel.setdefault(name, []).append(float(np.mean(d)))
+    for e_ in evs:
+        hip.destroy(e_)
+    return {n: sum(v) for n, v in per_kernel.items()}
+
+
+def measure(wl, T, steps, warmup, sets, replicas, path, act, seed, kernel_steps, quiet=False):
+    """Times `steps` whole forwards of one workload and returns its figures.
+
+    The forwards are captured into HIP graphs: one of S = min(sets, steps) forwards over S
+    pre-drawn input sets (cycling over `replicas` copies of the banks), replayed steps // S
+    times, and one of the remaining steps % S forwards. Every graph the timed region replays
+    is replayed once before it. The timed region starts behind a spin kernel, so the host's
+    graph launches are queued before the GPU reaches the first forward: what is timed is the
+    GPU running `steps` forwards back to back, bracketed by HIP events on the stream.
+    """
+    import numpy as np
+    import torch
+
+    import block_fp8_mixture_top_amd as M
+    import workloads as W
+    from block_fp8_mixture_top_amd import _lib as L
+
+    dev = torch.device("cuda:0")
+    shp = W.SHAPES[wl]
+    E, H, I, k = shp["E"], shp["H"], shp["I"], shp["top_k"]
+    S = max(1, min(sets, steps))
+    R = max(1, min(replicas, S))
+    log = (lambda *a: None) if quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
+    log(f"workload {wl} T={T} E={E} H={H} I={I} top_k={k}: {R} bank replicas, {S} input sets")
+    banks = [W.make_banks(wl, seed=seed + 100 * r, device=dev) for r in range(R)]
+    cases = [W.make_case(wl, T=T, seed=seed + 1000 + i, device=dev, banks=banks[i % R]) for i in range(S)]
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    fopts = dict(force_path={"auto": M.PATH_AUTO, "gather": M.PATH_GATHER, "stream": M.PATH_STREAM,
+                             "mfma": M.PATH_MFMA}[path],
+                 act_mode=M.ACT_GROUP_FP8 if act == "group_fp8" else M.ACT_PATH)
+    nbytes = max(M.workspace_size(T, E, H, I, k, **fopts), 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    w13_b, w2_b = banks[0][0].expert_bytes, banks[0][1].expert_bytes
+
+    # routed experts of every set (their bytes are the decode metric's numerator)
+    d_e = []
+    for c in cases:
+        r = M.route(c.logits, k, sort=False)
+        d_e.append(int(torch.unique(r["ids"]).numel()))
+    torch.cuda.synchronize()
+    step_bytes = [d * (w13_b + w2_b) for d in d_e]
+
+    def step(i):
+        c = cases[i % S]
+        return M.forward(c.hidden, c.logits, c.w13, c.w2, k, out=outs[i % S], workspace=ws, **fopts)[1]
+
+    info = step(0)
+    torch.cuda.synchronize()
+    log(f"path {info['path']}, {info['kernels']} kernels per forward")
+
+    graphs = {}
+
+    def graph_of(n):  # a graph of forwards 0 .. n-1 (input sets cycled)
+        if n not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    step(i)
+            graphs[n] = [g, False]
+        return graphs[n]
+
+    def run(nsteps):
+        plan = [S] * (nsteps // S) + ([nsteps % S] if nsteps % S else [])
+        for n in plan:
+            g = graph_of(n)
+            g[0].replay()
+            g[1] = True
+
+    def bytes_of(nsteps):
+        full, rem = divmod(nsteps, S)
+        return full * sum(step_bytes) + sum(step_bytes[:rem])
+
+    log(f"warmup {warmup} steps")
+    run(warmup)
+    for n in [S] * (steps // S > 0) + ([steps % S] if steps % S else []):
+        g = graph_of(n)
+        if not g[1]:  # a graph the timed region uses is replayed once first
+            g[0].replay()
+            g[1] = True
+    torch.cuda.synchronize()
+
+    log(f"timing {steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(int(4e6))  # about 2 ms: the launches below are queued behind it
+    start.record()
+    run(steps)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    gbs = bytes_of(steps) / (ms * 1e-3) / 1e9
+    tok_s = steps * T / (ms * 1e-3)
+
+    hip = Hip()
+    nk = info["kernels"]
+    per_kernel = _forward_timed_kernels(M, L, hip, cases, outs, ws, fopts, T, E, H, I, k, nk,
+                                        min(kernel_steps, max(S, 8)))
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+    mean_de = float(np.mean(d_e))
+    flops = 6.0 * T * k * H * I
+    if info["path"] == "mfma":
+        share = {"gemm1": 2.0 / 3.0, "gemm2": 1.0 / 3.0}.get(dom)
+        achieved = flops * share / (dom_ms * 1e-3) / 1e12 if share else None
+        roofline = dict(bound="mfma", achieved=round(achieved, 2) if achieved else None, peak=FP8_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4) if achieved else None)
+    else:
+        # algorithmic bytes of one launch of the dominant kernel
+        if dom == "gemm1":
+            kb = mean_de * w13_b + T * H * 2 + T * k * I * 4
+        elif dom == "gemm2":
+            kb = mean_de * w2_b + T * k * I * 4 + T * H * 2
+        else:
+            kb = None
+        achieved = kb / (dom_ms * 1e-3) / 1e9 if kb else None
+        roofline = dict(bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
+    roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T))
+    roofline["kernel"] = dom
+    roofline["kernel_ms"] = round(dom_ms, 5)
+    roofline["kernels_ms"] = {n: round(v, 5) for n, v in per_kernel.items()}
+    return dict(
+        wl=wl, T=T, E=E, H=H, I=I, k=k, info=info, ms=ms, steps=steps, S=S, R=R, wall=wall, gbs=gbs,
+        tok_s=tok_s, flops=flops, mean_de=mean_de, total_bytes=bytes_of(steps), roofline=roofline,
+        scale_dtype=banks[0][0].scale_dtype, cases=cases, expert_bytes=w13_b + w2_b,
+        tflops=flops * steps / (ms * 1e-3) / 1e12,
+    )
+
+
+def summary(m):
+    """The compact object a secondary workload contributes to the JSON line."""
+    ms_step = m["ms"] / m["steps"]
+    d = {
+        "workload": f"{m['wl']}: E={m['E']} H={m['H']} I={m['I']} top_k={m['k']} T={m['T']}",
+        "path": m["info"]["path"],
+        "steps": m["steps"],
+        "ms_per_step": round(ms_step, 6),
+    }
+    if m["info"]["path"] == "mfma":
+        d.update(tokens_per_s=round(m["tok_s"], 1), tflops=round(m["tflops"], 2),
+                 pct_fp8_mfma_peak=round(100.0 * m["tflops"] / FP8_PEAK_TFLOPS, 2),
+                 pct_hbm_peak_on_weights=round(100.0 * m["gbs"] / HBM_PEAK_GBS, 2))
+    else:
+        d.update(routed_gbs=round(m["gbs"], 1), pct_hbm_peak=round(100.0 * m["gbs"] / HBM_PEAK_GBS, 2),
+                 tokens_per_s=round(m["tok_s"], 1))
+    d["roofline"] = m["roofline"]
+    return d
+
+
+# Secondary workloads reported beside the headline decode line: (name, workload, T, steps,
+# warmup, input sets, bank replicas). One replica suffices where a forward already touches
+# more than the 256 MB Infinity Cache holds.
+EXTRAS = [
+    ("prefill_T4096", "prefill", 4096, 40, 4, 4, 1),
+    ("prefill_T16384", "prefill", 16384, 12, 2, 2, 1),
+    ("large_T1", "large", 1, 64, 8, 16, 1),
+]
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -221,156 +424,33 @@ def main():
               "benchmark (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import block_fp8_mixture_top_amd as M
-    import workloads as W
-
-    dev = torch.device("cuda:0")
     wl = args.workload
     T = args.T or WORKLOADS[wl]["T"]
-    shp = W.SHAPES[wl]
-    E, H, I, k = shp["E"], shp["H"], shp["I"], shp["top_k"]
-    S, R = args.sets, args.replicas
-    if wl == "large":
-        R = min(R, 1)  # 11.3 GB per replica; 256 experts x 44 MB already exceed the cache
-    print(f"[bench] workload {wl} T={T} E={E} H={H} I={I} top_k={k}: drawing {R} bank replicas, {S} input sets",
-          file=sys.stderr, flush=True)
-
-    banks = [W.make_banks(wl, seed=args.seed + 100 * r, device=dev) for r in range(R)]
-    cases = [W.make_case(wl, T=T, seed=args.seed + 1000 + i, device=dev, banks=banks[i % R]) for i in range(S)]
-    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
-    fopts = dict(force_path={"auto": M.PATH_AUTO, "gather": M.PATH_GATHER, "stream": M.PATH_STREAM,
-                             "mfma": M.PATH_MFMA}[args.path],
-                 act_mode=M.ACT_GROUP_FP8 if args.act == "group_fp8" else M.ACT_PATH)
-    nbytes = max(M.workspace_size(T, E, H, I, k, **fopts), 1)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    w13_b, w2_b = banks[0][0].expert_bytes, banks[0][1].expert_bytes
-
-    # routed experts of every set (their bytes are the metric's numerator)
-    d_e = []
-    for c in cases:
-        r = M.route(c.logits, k, sort=False)
-        d_e.append(int(torch.unique(r["ids"]).numel()))
-    torch.cuda.synchronize()
-    step_bytes = [d * (w13_b + w2_b) for d in d_e]
-
-    def step(i):
-        c = cases[i]
-        return M.forward(c.hidden, c.logits, c.w13, c.w2, k, out=outs[i], workspace=ws, **fopts)[1]
-
-    info = step(0)
-    torch.cuda.synchronize()
-    print(f"[bench] path {info['path']}, {info['kernels']} kernels per forward", file=sys.stderr, flush=True)
-
-    # one graph of S forwards, plus S single-forward graphs for a remainder
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(S):
-            step(i)
-    singles = []
-    for i in range(S):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(i)
-        singles.append(g)
-
-    def run(nsteps):
-        for _ in range(nsteps // S):
-            graph.replay()
-        for i in range(nsteps % S):
-            singles[i].replay()
-
-    def bytes_of(nsteps):
-        full, rem = divmod(nsteps, S)
-        return full * sum(step_bytes) + sum(step_bytes[:rem])
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    run(args.warmup)
-    torch.cuda.synchronize()
-
+    R = min(args.replicas, 1) if wl == "large" else args.replicas  # 11.3 GB per replica
+    m = measure(wl, T, args.steps, args.warmup, args.sets, R, args.path, args.act, args.seed, args.kernel_steps)
     K = args.steps
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    run(K)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / K
-    total_bytes = bytes_of(K)
-    gbs = total_bytes / (ms * 1e-3) / 1e9
-    tok_s = K * T / (ms * 1e-3)
+    info = m["info"]
 
-    # per-kernel durations: HIP events the library attaches to each kernel's dispatch on the
-    # stream the kernels run on (start and end of that kernel's execution); a spin kernel
-    # first lets the host enqueue everything before the GPU reaches it
-    hip = Hip()
-    nk = info["kernels"]
-    KS = min(args.kernel_steps, S)
-    evs = [hip.events(2 * nk) for _ in range(KS)]
-    kinds = (ctypes.c_int32 * nk)()
-    torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2e8))
-    from block_fp8_mixture_top_amd import _lib as L
-
-    for i in range(KS):
-        c = cases[i]
-        b13, b2 = M.bank_struct(c.w13), M.bank_struct(c.w2)
-        o = M.make_opts(**fopts)
-        ri = L.RunInfo()
-        L.check(M.lib().moe_fp8_block_forward_timed(
-            ctypes.c_void_p(c.hidden.data_ptr()), ctypes.c_void_p(c.logits.data_ptr()), ctypes.byref(b13),
-            ctypes.byref(b2), T, E, H, I, k, ctypes.c_void_p(outs[i].data_ptr()), L.MOE_BF16,
-            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None, None, ctypes.byref(o), ctypes.byref(ri),
-            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), evs[i], 2 * nk, kinds))
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for j in range(nk):
-        name = L.KERNEL_NAMES.get(kinds[j], str(kinds[j]))
-        d = [hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(KS)]
-        per_kernel.setdefault(name, []).append(float(np.mean(d)))
-    for e_ in evs:
-        hip.destroy(e_)
-    per_kernel = {n: sum(v) for n, v in per_kernel.items()}  # ms per forward, summed over a kind's kernels
-    dom = max(per_kernel, key=per_kernel.get)
-    dom_ms = per_kernel[dom]
-
-    mean_de = float(np.mean(d_e))
-    if info["path"] == "mfma":
-        flops = 6.0 * T * k * H * I
-        achieved = flops * (2.0 / 3.0 if dom == "gemm1" else 1.0 / 3.0) / (dom_ms * 1e-3) / 1e12
-        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / FP8_PEAK_TFLOPS, 4))
-    else:
-        # algorithmic bytes of one launch of the dominant kernel
-        if dom == "gemm1":
-            kb = mean_de * w13_b + T * H * 2 + T * k * I * 4
-        elif dom == "gemm2":
-            kb = mean_de * w2_b + T * k * I * 4 + T * H * 2
-        else:
-            kb = None
-        achieved = kb / (dom_ms * 1e-3) / 1e9 if kb else None
-        roofline = dict(bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=HBM_PEAK_GBS,
-                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
-    roofline["kernel"] = dom
-    roofline["kernel_ms"] = round(dom_ms, 5)
-    roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T))
-    roofline["kernels_ms"] = {n: round(v, 5) for n, v in per_kernel.items()}
+    extras = {}
+    if wl == "decode" and T == 1 and args.path == "auto" and args.act == "path" and not args.no_extra:
+        for name, ewl, eT, esteps, ewarm, esets, erep in EXTRAS:
+            torch.cuda.empty_cache()
+            em = measure(ewl, eT, esteps, ewarm, esets, erep, "auto", "path", args.seed, 8)
+            extras[name] = summary(em)
+            print(f"[bench] {name}: {json.dumps(extras[name])}", file=sys.stderr, flush=True)
+            del em
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cases, k, args.cpu_seconds, w13_b + w2_b, prefill=wl == "prefill")
+        cpu = cpu_baseline(m["cases"], m["k"], args.cpu_seconds, m["expert_bytes"], prefill=wl == "prefill")
 
-    if wl == "prefill":
-        value, unit = tok_s, "tokens/s"
+    if info["path"] == "mfma" or wl == "prefill":
+        value, unit = m["tok_s"], "tokens/s"
     else:
-        value, unit = gbs, "GB/s"
+        value, unit = m["gbs"], "GB/s"
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -378,7 +458,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(m["ms"] / K, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / CPU_REFERENCE_GBS, 2) if unit == "GB/s" and wl == "decode" else None,
@@ -386,21 +466,27 @@ def main():
                   2: "fp8e4m3 x fp8e4m3 -> fp32 (gate/up), fp8e4m3 x fp32 (down)"}[info["act_mode"]],
         "data": "synthetic",
         "config": {
-            "workload": f"{wl}: E={E} H={H} I={I} top_k={k} T={T}, bf16 hidden/out, fp8-e4m3 banks with "
-                        f"{banks[0][0].scale_dtype} 128x128 block scales",
+            "workload": f"{wl}: E={m['E']} H={m['H']} I={m['I']} top_k={m['k']} T={T}, bf16 hidden/out, "
+                        f"fp8-e4m3 banks with {m['scale_dtype']} 128x128 block scales",
             "path": info["path"],
-            "kernels_per_forward": nk,
-            "routed_experts_mean": mean_de,
-            "routed_bytes_per_step": round(total_bytes / K),
-            "bank_replicas": R,
-            "input_sets": S,
-            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-            "tokens_per_s": round(tok_s, 1),
-            "wall_s": round(wall, 4),
+            "kernels_per_forward": info["kernels"],
+            "routed_experts_mean": m["mean_de"],
+            "routed_bytes_per_step": round(m["total_bytes"] / K),
+            "bank_replicas": m["R"],
+            "input_sets": m["S"],
+            "timing": f"{K // m['S']} replays of a {m['S']}-forward graph"
+                      + (f" + one {K % m['S']}-forward graph" if K % m["S"] else "")
+                      + ", queued behind a spin kernel; HIP events on the stream",
+            "pct_hbm_peak": round(100.0 * m["gbs"] / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(m["tok_s"], 1),
+            "wall_s": round(m["wall"], 4),
         },
-        "roofline": roofline,
+        "roofline": m["roofline"],
         "cpu_baseline": cpu,
     }
+    if info["path"] == "mfma":
+        rec["config"]["pct_fp8_mfma_peak"] = round(100.0 * m["tflops"] / FP8_PEAK_TFLOPS, 2)
+    rec.update(extras)
     print(json.dumps(rec), flush=True)
 
 

@@ -29,7 +29,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "abi_version", "lib", "make_opts", "select_path", "route_workspace_size", "route", "workspace_size",
+    "abi_version", "lib", "make_opts", "bank_struct", "check_bank_extents", "select_path", "route_workspace_size", "route", "workspace_size",
     "forward", "quantize_rows", "decode_e4m3", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
     "PATH_STREAM", "PATH_MFMA", "PATH_NAMES", "ACT_PATH", "ACT_ROW_FP8", "ACT_GROUP_FP8",
 ]
@@ -92,14 +92,51 @@ def select_path(T: int, E: int, top_k: int, **opts) -> dict:
     return _info_dict(info)
 
 
-def bank_struct(bank) -> L.Bank:
+def check_bank_extents(bank, E: int, N: int, K: int) -> None:
+    """Raise ValueError unless the bank's tensors hold every element a call reading E
+    experts of [N, K] codes may touch (see bank_struct). Host-only; reads shapes, not data."""
+    for name, want in (("E", E), ("N", N), ("K", K)):
+        have = getattr(bank, name, None)
+        if have is not None and int(have) != int(want):
+            raise ValueError(f"bank has {name}={have}, the call needs {name}={want}")
+    es, srow, sexp = int(bank.expert_stride_bytes), int(bank.scale_row_stride), int(bank.scale_expert_stride)
+    if es < N * K or srow < -(-K // 128) or sexp < 0:
+        raise ValueError(f"bank strides too small for [{N}, {K}] experts (the library reports which)")
+    need_codes = (E - 1) * es + N * K
+    if bank.codes.numel() < need_codes:
+        raise ValueError(f"bank.codes holds {bank.codes.numel()} bytes, {E} experts of [{N}, {K}] with "
+                         f"expert stride {es} need {need_codes}")
+    need_scales = (E - 1) * sexp + (-(-N // 128) - 1) * srow + -(-K // 128)
+    if bank.scales.numel() < need_scales:
+        raise ValueError(f"bank.scales holds {bank.scales.numel()} elements, the strides need {need_scales}")
+    bias = getattr(bank, "bias", None)
+    if bias is not None and bias.numel() < E * N:
+        raise ValueError(f"bank.bias holds {bias.numel()} floats, [{E}, {N}] needs {E * N}")
+
+
+def bank_struct(bank, E: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None,
+                device=None) -> L.Bank:
     """A moe_fp8_bank from an object with codes/scales tensors, the stride fields and an
-    optional float32 [E, N] MLP bias (``bias``, None for none)."""
-    _need(bank.codes, "bank.codes", torch.uint8)
+    optional float32 [E, N] MLP bias (``bias``, None for none).
+
+    With E, N and K (what the call will read: E experts of [N, K] codes), the tensors are
+    checked to hold every byte the kernels may read before anything is launched, since the
+    C ABI only sees raw pointers: codes at least (E-1)*expert_stride_bytes + N*K bytes,
+    scales at least (E-1)*scale_expert_stride + (ceil(N/128)-1)*scale_row_stride +
+    ceil(K/128) elements (FreeToken PR #662, commit "honor padded fp8 scale strides": the
+    shape check asserts that the unpadded extent is present), a bias at least E*N floats.
+    A bank that states its own E, N or K must agree with them.
+    """
+    _need(bank.codes, "bank.codes", torch.uint8, device)
     if bank.scales.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("bank.scales must be bfloat16 or float32")
     if bank.scales.device != bank.codes.device or not bank.scales.is_contiguous():
         raise ValueError("bank.scales must be contiguous and on the codes' device")
+    bias = getattr(bank, "bias", None)
+    if bias is not None:
+        _need(bias, "bank.bias", torch.float32, bank.codes.device)
+    if E is not None:
+        check_bank_extents(bank, E, N, K)
     b = L.Bank()
     b.codes = bank.codes.data_ptr()
     b.expert_stride_bytes = int(bank.expert_stride_bytes)
@@ -108,9 +145,7 @@ def bank_struct(bank) -> L.Bank:
     b.reserved = 0
     b.scale_row_stride = int(bank.scale_row_stride)
     b.scale_expert_stride = int(bank.scale_expert_stride)
-    bias = getattr(bank, "bias", None)
     if bias is not None:
-        _need(bias, "bank.bias", torch.float32, bank.codes.device)
         b.bias = bias.data_ptr()
     return b
 
@@ -161,11 +196,13 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out
     _need(hidden, "hidden", torch.bfloat16)
     dev = hidden.device
     _need(logits, "logits", torch.float32, dev)
+    if hidden.dim() != 2 or logits.dim() != 2:
+        raise ValueError("hidden must be [T, H] and logits [T, E]")
     T, H = hidden.shape
     E = logits.shape[1]
     if logits.shape[0] != T:
         raise ValueError("hidden and logits disagree on T")
-    I = w2.K
+    I = int(w2.K)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=dev)
     if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (T, H):
@@ -175,7 +212,9 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out
     nbytes = int(lib().moe_fp8_block_workspace_size(T, E, H, I, top_k, ctypes.byref(o)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    b13, b2 = bank_struct(w13), bank_struct(w2)
+    _need(workspace, "workspace", torch.uint8, dev)
+    b13 = bank_struct(w13, E, 2 * I, H, dev)
+    b2 = bank_struct(w2, E, H, I, dev)
     ids = w = None
     if return_routing:
         ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
