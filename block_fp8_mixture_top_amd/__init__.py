@@ -30,7 +30,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "abi_version", "lib", "make_opts", "bank_struct", "check_bank_extents", "select_path", "route_workspace_size", "route", "workspace_size",
-    "forward", "quantize_rows", "decode_e4m3", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
+    "forward", "mfma_up", "mfma_down", "quantize_rows", "decode_e4m3", "decode_e4m3_paths", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
     "PATH_STREAM", "PATH_MFMA", "PATH_NAMES", "ACT_PATH", "ACT_ROW_FP8", "ACT_GROUP_FP8",
 ]
 
@@ -230,6 +230,41 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out
     return out, d
 
 
+def mfma_up(hidden: torch.Tensor, logits: torch.Tensor, w13, top_k: int, I: int) -> torch.Tensor:
+    """Test export: the MFMA path's first half. Returns h [T*top_k, I] float32, row p for the
+    pair at sorted position p."""
+    _need(hidden, "hidden", torch.bfloat16)
+    dev = hidden.device
+    _need(logits, "logits", torch.float32, dev)
+    T, H = hidden.shape
+    E = logits.shape[1]
+    b13 = bank_struct(w13, E, 2 * I, H, dev)
+    ws = torch.empty(max(workspace_size(T, E, H, I, top_k, force_path=PATH_MFMA), 1), dtype=torch.uint8, device=dev)
+    h = torch.empty((T * top_k, I), dtype=torch.float32, device=dev)
+    L.check(lib().moe_fp8_block_mfma_up(_ptr(hidden), _ptr(logits), ctypes.byref(b13), T, E, H, I, top_k, _ptr(h),
+                                        _ptr(ws), ws.numel(), _stream(hidden)))
+    return h
+
+
+def mfma_down(h: torch.Tensor, logits: torch.Tensor, w2, top_k: int, H: int, out_dtype=torch.float32) -> torch.Tensor:
+    """Test export: the MFMA path's second half on h [T*top_k, I] float32 in sorted-position
+    order. Returns out [T, H]."""
+    _need(h, "h", torch.float32)
+    dev = h.device
+    _need(logits, "logits", torch.float32, dev)
+    T, E = logits.shape
+    I = h.shape[1]
+    if h.shape[0] != T * top_k:
+        raise ValueError("h must have T*top_k rows")
+    b2 = bank_struct(w2, E, H, I, dev)
+    ws = torch.empty(max(workspace_size(T, E, H, I, top_k, force_path=PATH_MFMA), 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    L.check(lib().moe_fp8_block_mfma_down(_ptr(h), _ptr(logits), ctypes.byref(b2), T, E, H, I, top_k, _ptr(out),
+                                          L.MOE_BF16 if out_dtype == torch.bfloat16 else L.MOE_F32, _ptr(ws),
+                                          ws.numel(), _stream(h)))
+    return out
+
+
 def quantize_rows(x: torch.Tensor):
     """Per-row dynamic e4m3 of a bf16 [rows, cols] tensor -> (codes uint8, scales float32)."""
     _need(x, "x", torch.bfloat16)
@@ -244,6 +279,17 @@ def decode_e4m3(codes: torch.Tensor) -> torch.Tensor:
     _need(codes, "codes", torch.uint8)
     out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
     L.check(lib().moe_fp8_block_decode_e4m3(_ptr(codes), _ptr(out), codes.numel(), _stream(codes)))
+    return out
+
+
+def decode_e4m3_paths(chunks: torch.Tensor) -> torch.Tensor:
+    """Every decode path of the kernels on [n, 16] uint8 chunks of finite codes -> [n, 16, 5]
+    float32 (see moe_fp8_block_decode_e4m3_paths)."""
+    _need(chunks, "chunks", torch.uint8)
+    if chunks.dim() != 2 or chunks.shape[1] != 16:
+        raise ValueError("chunks must be [n, 16]")
+    out = torch.empty((chunks.shape[0], 16, 5), dtype=torch.float32, device=chunks.device)
+    L.check(lib().moe_fp8_block_decode_e4m3_paths(_ptr(chunks), _ptr(out), chunks.shape[0], _stream(chunks)))
     return out
 
 

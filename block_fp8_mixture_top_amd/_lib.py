@@ -8,7 +8,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8_block.so")
 
-ABI_VERSION = 2  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 3  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
 
 MOE_OK = 0
 STATUS_NAMES = {
@@ -35,8 +35,11 @@ EXPORTS = [
     "moe_fp8_block_workspace_size",
     "moe_fp8_block_forward",
     "moe_fp8_block_forward_timed",
+    "moe_fp8_block_mfma_up",
+    "moe_fp8_block_mfma_down",
     "moe_fp8_block_quantize_rows",
     "moe_fp8_block_decode_e4m3",
+    "moe_fp8_block_decode_e4m3_paths",
     "moe_fp8_block_encode_e4m3",
 ]
 
@@ -101,8 +104,11 @@ _SIGS = {
          ctypes.POINTER(Opts), ctypes.POINTER(RunInfo), _P, ctypes.POINTER(ctypes.c_void_p), _I,
          ctypes.POINTER(ctypes.c_int32)],
     ),
+    "moe_fp8_block_mfma_up": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_fp8_block_mfma_down": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P]),
     "moe_fp8_block_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_fp8_block_decode_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
+    "moe_fp8_block_decode_e4m3_paths": (_I, [_P, _P, ctypes.c_int64, _P]),
     "moe_fp8_block_encode_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
 }
 

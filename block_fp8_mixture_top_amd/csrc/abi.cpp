@@ -243,6 +243,13 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
                  int T, int E, int H, int I, int top_k, void* out, int out_dtype, void* workspace,
                  size_t workspace_bytes, int32_t* ids_out, float* weights_out, const moe_opts* opts,
                  moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds);
+int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
+            const Layout& L, int T, int E, int H, int I, int top_k, float* hf);
+int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Plan& plan, void* workspace,
+              const Layout& L, int T, int E, int H, int I, int top_k, void* out, int out_bf16);
+int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, const char* bank_name, int64_t N,
+                    int64_t K, int T, int E, int H, int I, int top_k, void* workspace, size_t workspace_bytes,
+                    Layout* Lout, moe::Plan* plan);
 
 }  // namespace
 
@@ -424,22 +431,80 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
       RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
     }
   } else {
-    uint8_t* xq = at<uint8_t>(workspace, L.xq);
-    float* xs = at<float>(workspace, L.xs);
     float* hf = at<float>(workspace, L.h);
-    RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
-    RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s),
-        "gemm1 mfma launch");
-    uint8_t* hq = at<uint8_t>(workspace, L.hq);
-    float* hs = at<float>(workspace, L.hs);
-    RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, hq, hs, s), "h quant launch");
-    _Float16* y16 = at<_Float16>(workspace, L.y);
-    int8_t* yexp = at<int8_t>(workspace, L.yexp);
-    RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
-    RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, w, ids, b2.bias, T, H, top_k, out, out_bf16, s), "combine launch");
+    int st2 = mfma_up(R, hidden, b13, plan, workspace, L, T, E, H, I, top_k, hf);
+    if (st2 == MOE_OK) st2 = mfma_down(R, hf, b2, plan, workspace, L, T, E, H, I, top_k, out, out_bf16);
+    if (st2 != MOE_OK) return st2;
   }
   if (info) info->kernels = R.n;
   return ok();
+}
+
+// The MFMA path's first half: x quantised per token, then GEMM1 + silu*up into hf (float,
+// [P, I] in sorted-position order).
+int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
+            const Layout& L, int T, int E, int H, int I, int top_k, float* hf) {
+  hipStream_t s = R.s;
+  const int64_t P = (int64_t)T * top_k;
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* xs = at<float>(workspace, L.xs);
+  RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
+  RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s), "gemm1 mfma launch");
+  return MOE_OK;
+}
+
+// The second half: h quantised per (token, slot) row, the down GEMM and the combine.
+int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Plan& plan, void* workspace,
+              const Layout& L, int T, int E, int H, int I, int top_k, void* out, int out_bf16) {
+  hipStream_t s = R.s;
+  const int64_t P = (int64_t)T * top_k;
+  uint8_t* hq = at<uint8_t>(workspace, L.hq);
+  float* hs = at<float>(workspace, L.hs);
+  RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, hq, hs, s), "h quant launch");
+  _Float16* y16 = at<_Float16>(workspace, L.y);
+  int8_t* yexp = at<int8_t>(workspace, L.yexp);
+  RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
+  RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, plan.w, plan.ids, b2.bias, T, H, top_k, out, out_bf16, s),
+      "combine launch");
+  return MOE_OK;
+}
+
+// Checks and routing shared by the two test exports of the MFMA halves: the sizes, the
+// bank, the workspace of a forward forced onto MFMA, then route + sort into the workspace.
+int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, const char* bank_name, int64_t N,
+                    int64_t K, int T, int E, int H, int I, int top_k, void* workspace, size_t workspace_bytes,
+                    Layout* Lout, moe::Plan* plan) {
+  int st = check_sizes(T, E, top_k);
+  if (st) return st;
+  if (!moe::mfma_shape_ok(H, I))
+    return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
+  if ((st = check_bank(bank, bank_name, E, N, K))) return st;
+  if (T == 0) return ok();
+  if (!logits) return fail(MOE_ERR_ARG, "logits must be non-NULL");
+  const Layout L = layout_for(MOE_PATH_MFMA, MOE_ACT_ROW_FP8, T, E, H, I, top_k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const int64_t P = (int64_t)T * top_k;
+  const int slots = (int)(P < E ? P : E);
+  int32_t* ids = at<int32_t>(workspace, L.ids);
+  float* w = at<float>(workspace, L.w);
+  int32_t* counts = at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* act = at<int32_t>(workspace, L.act);
+  int32_t* tile_off = at<int32_t>(workspace, L.tile_off);
+  hipStream_t s = R.s;
+  for (int stg = 0; stg < moe::route_kernel_count(T, top_k); ++stg)
+    RUN(stg == 0 ? MOE_K_ROUTE : MOE_K_SORT,
+        moe::launch_route_stage(stg, logits, T, E, top_k, ids, w, counts, offsets, sorted, act,
+                                at<int32_t>(workspace, L.n_act), slots, moe::kMfmaTileM, tile_off,
+                                at<void>(workspace, L.scratch), s),
+        "route launch");
+  *Lout = L;
+  *plan = moe::Plan{ids, w, counts, offsets, sorted, act, tile_off};
+  return MOE_OK;
 }
 
 }  // namespace
@@ -466,6 +531,35 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
                       weights_out, opts, info, stream, events, n_events, kinds);
 }
 
+int moe_fp8_block_mfma_up(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, int T, int E, int H,
+                          int I, int top_k, float* h, void* workspace, size_t workspace_bytes, void* stream) {
+  Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
+  Layout L{};
+  moe::Plan plan{};
+  int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, workspace, workspace_bytes,
+                           &L, &plan);
+  if (st != MOE_OK || T == 0) return st;
+  if (!hidden || !h) return fail(MOE_ERR_ARG, "hidden and h must be non-NULL");
+  if (!aligned16(hidden) || !aligned16(h)) return fail(MOE_ERR_ALIGN, "hidden and h must be 16-byte aligned");
+  st = mfma_up(R, hidden, bank_arg(w13), plan, workspace, L, T, E, H, I, top_k, h);
+  return st != MOE_OK ? st : ok();
+}
+
+int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_bank* w2, int T, int E, int H, int I,
+                            int top_k, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
+  Layout L{};
+  moe::Plan plan{};
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
+  int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, workspace, workspace_bytes, &L, &plan);
+  if (st != MOE_OK || T == 0) return st;
+  if (!h || !out) return fail(MOE_ERR_ARG, "h and out must be non-NULL");
+  if (!aligned16(h) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h and out must be 16-byte aligned");
+  st = mfma_down(R, h, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out, out_dtype == MOE_BF16);
+  return st != MOE_OK ? st : ok();
+}
+
 int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales, void* stream) {
   if (rows < 0 || cols <= 0) return fail(MOE_ERR_ARG, "rows must be >= 0 and cols > 0");
   if (cols % 16 != 0 || cols > 8192)
@@ -482,6 +576,15 @@ int moe_fp8_block_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void*
   if (n == 0) return ok();
   if (!codes || !out) return fail(MOE_ERR_ARG, "codes and out must be non-NULL");
   HIP_CHECK(moe::launch_decode_e4m3(codes, out, n, (hipStream_t)stream), "decode launch");
+  return ok();
+}
+
+int moe_fp8_block_decode_e4m3_paths(const uint8_t* chunks, float* out, int64_t n, void* stream) {
+  if (n < 0) return fail(MOE_ERR_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!chunks || !out) return fail(MOE_ERR_ARG, "chunks and out must be non-NULL");
+  if (!aligned16(chunks)) return fail(MOE_ERR_ALIGN, "chunks must be 16-byte aligned");
+  HIP_CHECK(moe::launch_decode_paths(chunks, out, n, (hipStream_t)stream), "decode paths launch");
   return ok();
 }
 

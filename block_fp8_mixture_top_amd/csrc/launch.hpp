@@ -138,5 +138,6 @@ hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
 hipError_t launch_encode_e4m3(const float* x, uint8_t* codes, int64_t n, hipStream_t s);
+hipError_t launch_decode_paths(const uint8_t* chunks, float* out, int64_t n, hipStream_t s);
 
 }  // namespace moe

@@ -45,7 +45,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a struct, an enum or an entry point's meaning. */
-#define MOE_FP8_BLOCK_ABI_VERSION 2
+#define MOE_FP8_BLOCK_ABI_VERSION 3
 
 /* Limits checked on every call. */
 #define MOE_FP8_BLOCK_MAX_EXPERTS 1024
@@ -227,6 +227,27 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
                                 void* const* events, int n_events, int32_t* kinds);
 
 /*
+ * Test exports: the two halves of the MFMA path (route + sort first in each), so that each
+ * half can be checked against a reference on its own inputs. Both take the workspace of a
+ * forward forced onto MFMA (moe_fp8_block_workspace_size with force_path MOE_PATH_MFMA)
+ * and need H a multiple of 128 up to 8192 and I in {128, 256, 384, 512}
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ *   mfma_up:   x quantised per token (as quantize_rows), GEMM1 on the fp8 matrix cores and
+ *              h = silu(gate) * up written in float to h [T*top_k, I], row p holding the
+ *              pair at sorted position p (the sorted_pairs order of moe_fp8_block_route).
+ *   mfma_down: h [T*top_k, I] float in the same sorted-position order is quantised per row
+ *              (scale amax/448), multiplied by w2 on the matrix cores and combined with the
+ *              router weights into out [T, H] (out_dtype float or bf16), exactly as the
+ *              forward's second half.
+ * Pointers are device pointers, hidden/h/out 16-byte aligned. T = 0 is a no-op.
+ */
+int moe_fp8_block_mfma_up(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, int T, int E, int H,
+                          int I, int top_k, float* h, void* workspace, size_t workspace_bytes, void* stream);
+int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_bank* w2, int T, int E, int H, int I,
+                            int top_k, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * The activation preparation of the MFMA path on its own: per-row dynamic e4m3.
  *   x [rows, cols] bf16; codes [rows, cols] uint8 out; scales [rows] float out, with
  *   scale = amax/448 (float division; 1 for an all-zero row) and code = e4m3 of x/scale
@@ -239,6 +260,15 @@ int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* 
 /* Device decode of n e4m3 codes to float with the kernels' own conversion (codes and
  * out device, n >= 0). Exposed so tests can check the decode over all 256 codes. */
 int moe_fp8_block_decode_e4m3(const uint8_t* codes, float* out, int64_t n, void* stream);
+
+/* Every decode the kernels use, on n chunks of 16 codes (device, 16-byte aligned) into out
+ * [n, 16, 5] float (device): for code j of chunk i, out[i][j][0] is the word conversion to
+ * float (both halves of each 32-bit word), [1] the conversion to bf16 with unit scale (both
+ * halves) widened to float, [2] the W8A16 dot helper (codes x bf16) against a one-hot bf16
+ * activation at j, [3] the e4m3 x e4m3 dot helper against a one-hot e4m3 1.0 at j, [4] the
+ * codes x float dot helper against a one-hot float at j. Each must equal the code's value.
+ * Chunks must hold finite codes only (a NaN code times a zero activation is NaN). */
+int moe_fp8_block_decode_e4m3_paths(const uint8_t* chunks, float* out, int64_t n, void* stream);
 
 /* Device float -> e4m3 with the kernels' own conversion (nearest even, saturating at
  * 448, sign of zero kept). Exposed so tests can sweep rounding midpoints. */

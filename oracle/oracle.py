@@ -35,8 +35,14 @@ Pins (tests/test_oracle_*.py, run without a GPU):
                     exactly zero; E=1,k=1 is a textbook SwiGLU FFN (torch), with and
                     without biases; expert permutation and token independence invariants;
                     act_mode 2 against scalar loops over group-dequantised activations.
-  w8a8 flags        parity unpinned beyond the self-consistency checks: the ambiguity
-                    window is an analysis bound (documented), not a value the pages give.
+  e4m3_midpoint_distance
+                    a linear walk over every finite value at every value, midpoint and
+                    its float32 neighbours, and at random magnitudes.
+  h_drift / flags   GEMM1 evaluated on the CPU with float32 sums in several orders and
+                    with a truncating aligned accumulator: every h stays within the bound
+                    and every code that changes is flagged; on the GPU, the MFMA path's h
+                    lies within the bound at every element. The constants are a reading
+                    (the pages fix no accumulation precision), documented at ACC_MMA.
 """
 
 from __future__ import annotations
@@ -103,7 +109,7 @@ def e4m3_encode(v) -> np.ndarray:
 def e4m3_midpoint_distance(v32: np.ndarray):
     """Distance from |v| to the midpoint of its bracketing e4m3 pair, and that pair's step.
 
-    Used for the W8A8 ambiguity flags: a value within the fp32 drift window of a midpoint
+    Used for the W8A8 ambiguity flags: a value within the drift bound of a midpoint
     may round either way. Values at or past 448 have no midpoint above them.
     """
     a = np.abs(np.asarray(v32, dtype=np.float64))
@@ -273,65 +279,118 @@ def _expert_cache(w13: dict, w2: dict):
 
     def get(e):
         if e not in cache:
+            cache.clear()  # one expert at a time: the large banks hold hundreds of MB each
             cache[e] = (dequant_expert(w13, e), dequant_expert(w2, e), expert_bias(w13, e), expert_bias(w2, e))
         return cache[e]
     return get
 
 
-# Drift window for the W8A8 re-quantisation of h. An fp32 evaluation of a K-term dot
-# product drifts from the exact value by about 2^-24 * sqrt(K) * (root sum of squares of
-# the terms); the window is SAFETY times that, plus 16 fp32 ulps of |h| for the
-# elementwise SiLU and product. Sequential fp32 summation over K=2048 reaches about 1.06
-# times the estimate at its worst and 128-blocked summation about 0.15 times, so SAFETY
-# leaves a margin of four over the least favourable order. It is an analysis bound, not
-# a value from the pages.
-SAFETY = 4.0
+# Drift bound for the W8A8 re-quantisation of h. The pages fix no accumulation order and
+# no accumulation precision for the fp8 matrix products ([cpu] PR body: results differ
+# only in summation order; [cpu] commit "add float64 parity reference": a loose tolerance
+# cannot see accumulator precision loss), so an h element whose scaled value lies close to
+# an e4m3 rounding midpoint may legitimately round either way. h_drift bounds how far an
+# implementation's h may sit from the exact h:
+#   * fp32 evaluation: 2^-24 * sqrt(K) * (root sum of squares of the K terms), F32_RW
+#     times. Summing exact code products in float32 in any order (sequential, pairwise,
+#     128-blocked, with float32 block-scale multiplies) stays within 0.15 of it.
+#   * fp8 matrix-core accumulation: the matrix cores sum a block of 128 code products in a
+#     fixed-width aligned adder, which drops low bits of the products relative to the
+#     block's largest one (measured on gfx950: at most 2^-11 of that product's binade per
+#     block, about 2^-15 typically). The bound per row is ACC_MMA times the root sum of
+#     squares over the K blocks of each block's largest |product|.
+#   * the elementwise SiLU and product: H_REL * |h|.
+# A test evaluates GEMM1 on the CPU with a truncating aligned accumulator and with float32
+# sums in several orders; a GPU test checks that the MFMA path's h lies within the bound
+# for every element. These constants are a reading (the pages are silent), not page values.
+F32_RW = 1.0
+ACC_MMA = 3.0e-4
+H_REL = 2.0 ** -22
 U32 = 2.0 ** -24
 
 
-def h_drift(W13, xrow, g, u, h):
-    """Estimated fp32 drift of each h_i = silu(g_i) * u_i (see SAFETY)."""
-    I = g.shape[0]
-    K = xrow.shape[0]
-    sg = np.sqrt(((W13[:I] * xrow) ** 2).sum(axis=1))
-    su = np.sqrt(((W13[I:] * xrow) ** 2).sum(axis=1))
-    dg = np.abs(_silu_grad(g) * u) * sg
-    du = np.abs(silu(g)) * su
-    return SAFETY * U32 * (math.sqrt(K) * (dg + du) + 16.0 * np.abs(h))
+def acc_bound(W, X, coarse: bool = False):
+    """Accumulation bound of W @ x for every row x of X: [n, N].
 
-
-def _expert_mlp(W13, W2, xrow, act_mode: int, b13=None, b2=None):
-    """One (token, expert) pair: a = W13 x + b13, h = silu(a[:I]) * a[I:], y = W2 h + b2.
-
-    Gate rows are 0..I-1 and up rows I..2I-1 ([tpu] review of the w1 DMA: gate half
-    first, up half second); the optional MLP biases follow the same rows ([tpu] review of
-    the w1 bias DMA). act_mode 1 re-quantises h per pair before the down GEMM and
-    flags the elements of h whose rounding an fp32 evaluation could decide either way:
-    |v - midpoint| <= drift(h_i)/s + |v| * drift(h_r)/amax, where r is the row's argmax
-    (the second term is the scale moving with amax).
+    F32_RW * 2^-24 * sqrt(K) * (root sum of squares of the K terms W[i,k] x[k]) plus
+    ACC_MMA * sqrt(sum over 128-wide K blocks of the block's largest |W[i,k] x[k]|^2).
+    coarse: each block's largest term replaced by the product of the block's largest |W|
+    and largest |x| (never smaller, and cheap for many rows).
     """
+    X = np.atleast_2d(X)
+    n, K = X.shape
+    N = W.shape[0]
+    rss = np.sqrt((W * W) @ (X * X).T).T  # [n, N]
+    nkb = -(-K // BLOCK)
+    aw = np.zeros((N, nkb * BLOCK))
+    aw[:, :K] = np.abs(W)
+    aw = aw.reshape(N, nkb, BLOCK)
+    ax = np.zeros((n, nkb * BLOCK))
+    ax[:, :K] = np.abs(X)
+    ax = ax.reshape(n, nkb, BLOCK)
+    if coarse:
+        wm, xm = aw.max(axis=2), ax.max(axis=2)  # [N, nkb], [n, nkb]
+        mb = np.sqrt((xm * xm) @ (wm * wm).T)
+    else:
+        mb = np.empty((n, N))
+        for i in range(n):
+            m = (aw * ax[i][None]).max(axis=2)  # [N, nkb]
+            mb[i] = np.sqrt((m * m).sum(axis=1))
+    return F32_RW * U32 * math.sqrt(K) * rss + ACC_MMA * mb
+
+
+def h_drift(W13, X, g, u, h, coarse: bool = False):
+    """Bound on |h_impl - h| for each h = silu(g) * u, rows of X the tokens ([n, I]; first
+    order in the gate and up errors; see ACC_MMA; coarse as in acc_bound)."""
+    I = np.atleast_2d(g).shape[1]
+    b = acc_bound(W13, X, coarse)
+    return np.abs(_silu_grad(g) * u) * b[:, :I] + np.abs(silu(g)) * b[:, I:] + H_REL * np.abs(h)
+
+
+def _expert_up(W13, X, b13=None):
+    """a = W13 x (+ b13) for each row x of X; gate rows 0..I-1 and up rows I..2I-1 ([tpu]
+    review of the w1 DMA: gate half first, up half second; the bias follows the rows, [tpu]
+    review of the w1 bias DMA). Returns g, u and h = silu(g) * u, each [n, I]."""
     I = W13.shape[0] // 2
-    a = W13 @ xrow
+    A = np.atleast_2d(X) @ W13.T
     if b13 is not None:
-        a = a + b13
-    g, u = a[:I], a[I:]
-    h = silu(g) * u
-    zb = 0.0 if b2 is None else b2
-    if act_mode == 0:
-        return W2 @ h + zb, None
+        A = A + b13[None, :]
+    g, u = A[:, :I], A[:, I:]
+    return g, u, silu(g) * u
+
+
+def _requantize_h(W13, X, g, u, h):
+    """act_mode 1: h re-quantised per (token, slot) row to e4m3 (scale amax/448, in float32
+    emulation) before the down GEMM, and the elements whose rounding an implementation may
+    decide either way flagged: |v - midpoint| <= drift(h_i)/s + |v| * drift(h_r)/amax,
+    with r the row's argmax (the second term is the scale moving with amax)."""
     h32 = h.astype(np.float32)
-    q, s = quantize_rows(h32[None, :])
-    q, s = q[0], s[0]
-    h_deq = _LUT[q] * np.float64(s)
-    d = h_drift(W13, xrow, g, u, h)
-    amax = float(np.max(np.abs(h32)))
-    r = int(np.argmax(np.abs(h32)))
-    v = (h32 / np.float32(s)).astype(np.float64)
+    q, s = quantize_rows(h32)
+    h_deq = _LUT[q] * s.astype(np.float64)[:, None]
+    d = h_drift(W13, X, g, u, h)
+    amax = np.max(np.abs(h32), axis=1).astype(np.float64)
+    r = np.argmax(np.abs(h32), axis=1)
+    v = (h32 / s[:, None]).astype(np.float32).astype(np.float64)
     dist, step = e4m3_midpoint_distance(v)
-    rho = d / float(s) + (np.abs(v) * d[r] / amax if amax > 0 else 0.0)
-    flags = dist <= rho
-    extra = dict(h_codes=q, h_scale=s, flags=flags, step=step)
-    return W2 @ h_deq + zb, extra
+    dr = d[np.arange(len(r)), r]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale_term = np.where(amax[:, None] > 0, np.abs(v) * (dr / amax)[:, None], 0.0)
+    flags = dist <= d / s.astype(np.float64)[:, None] + scale_term
+    return h_deq, dict(h_codes=q, h_scale=s, flags=flags, step=step, drift=d)
+
+
+def _expert_mlp(W13, W2, X, act_mode: int, b13=None, b2=None):
+    """The tokens X [n, H] routed to one expert: a = W13 x + b13, h = silu(a[:I]) * a[I:],
+    y = W2 h + b2, for each row. act_mode 1 re-quantises h first (_requantize_h). Returns
+    Y [n, H] and, for act_mode 1, the per-row h codes, scales, flags and steps."""
+    g, u, h = _expert_up(W13, X, b13)
+    extra = None
+    if act_mode == 1:
+        h, extra = _requantize_h(W13, np.atleast_2d(X), g, u, h)
+    Y = h @ W2.T
+    if b2 is not None:
+        Y = Y + b2[None, :]
+    return Y, extra
 
 
 def _x_used(x, act_mode: int, res: dict):
@@ -350,6 +409,12 @@ def _x_used(x, act_mode: int, res: dict):
     raise ValueError(f"act_mode {act_mode}")
 
 
+def _pairs_by_expert(ids):
+    """{expert: array of pairs p = t*k + j routed to it}, experts ascending."""
+    flat = np.asarray(ids).ravel()
+    return {int(e): np.nonzero(flat == e)[0] for e in np.unique(flat)}
+
+
 def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
     """Gathered formulation: out[t] = sum_j w_tj * expert_{ids[t,j]}(x_t).
 
@@ -360,9 +425,11 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     gathered, up/gate run as one GEMM and the down projection follows); act_mode 2 is
     the gather variant of [gather] The fix: the up/gate GEMM on e4m3 activations quantised
     per (token, 128-column group) and the down projection on h in full precision.
-    Returns a dict with out (float64 [T, H]), routing, the x quantisation for act_modes 1
-    and 2, and for act_mode 1 the h quantisation and the per-output allowance for
-    ambiguous h roundings.
+    Only the routed experts are read; each is evaluated once on all the tokens routed to
+    it (one matrix product per expert), and its contribution w_tj * y is added to each of
+    those tokens. Returns a dict with out (float64 [T, H]), routing, the x quantisation for
+    act_modes 1 and 2, and for act_mode 1 the h quantisation (per pair p = t*k + j) and the
+    per-output allowance for ambiguous h roundings.
     """
     x = bf16_to_f64(hidden_bf16)
     T, H = x.shape
@@ -377,25 +444,68 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     allowance = np.zeros((T, H), dtype=np.float64)
     n_flag = 0
     h_codes, h_scales = {}, {}
-    for t in range(T):
-        for j in range(top_k):
-            e = int(ids[t, j])
-            W13, W2, b13, b2 = get(e)
-            y, extra = _expert_mlp(W13, W2, x_used[t], h_mode, b13, b2)
-            out[t] += w[t, j] * y
+    wf = w.ravel()
+    for e, pairs in _pairs_by_expert(ids).items():
+        W13, W2, b13, b2 = get(e)
+        toks = pairs // top_k
+        for c0 in range(0, len(pairs), 64):
+            sl = slice(c0, c0 + 64)
+            Y, extra = _expert_mlp(W13, W2, x_used[toks[sl]], h_mode, b13, b2)
+            out[toks[sl]] += wf[pairs[sl], None] * Y  # a token holds each expert once
             if extra is not None:
                 f = extra["flags"]
                 n_flag += int(f.sum())
-                if f.any():
-                    amt = np.where(f, extra["step"] * float(extra["h_scale"]), 0.0)
-                    allowance[t] += abs(w[t, j]) * (np.abs(W2) @ amt)
-                h_codes[t * top_k + j] = extra["h_codes"]
-                h_scales[t * top_k + j] = extra["h_scale"]
+                amt = np.where(f, extra["step"] * extra["h_scale"].astype(np.float64)[:, None], 0.0)
+                allowance[toks[sl]] += np.abs(wf[pairs[sl], None]) * (amt @ np.abs(W2).T)
+                for r, p in enumerate(pairs[sl]):
+                    h_codes[int(p)] = extra["h_codes"][r]
+                    h_scales[int(p)] = extra["h_scale"][r]
     res["out"] = out
     if act_mode == 1:
         res.update(allowance=allowance, n_flagged=n_flag, n_h=T * top_k * (w13["N"] // 2),
                    h_codes=h_codes, h_scales=h_scales)
     return res
+
+
+def up_w8a8(hidden_bf16, ids, w13: dict, pairs=None, coarse: bool = False):
+    """The first half of act_mode 1 on its own: h = silu(gate) * up for every pair
+    p = t*k + j (or the listed pairs), float64 [len(pairs), I] in the order given, from x
+    quantised per token. Also returns the drift bound of each h (h_drift, coarse or not)."""
+    x = bf16_to_f64(hidden_bf16)
+    xu = _x_used(x, 1, {})
+    ids = np.asarray(ids)
+    k = ids.shape[1]
+    pairs = np.arange(ids.size) if pairs is None else np.asarray(pairs)
+    I = w13["N"] // 2
+    h = np.empty((len(pairs), I))
+    d = np.empty((len(pairs), I))
+    flat = ids.ravel()[pairs]
+    for e in np.unique(flat):
+        W13 = dequant_expert(w13, int(e))
+        b13 = expert_bias(w13, int(e))
+        rows = np.nonzero(flat == e)[0]
+        X = xu[pairs[rows] // k]
+        g, u, hh = _expert_up(W13, X, b13)
+        h[rows] = hh
+        d[rows] = h_drift(W13, X, g, u, hh, coarse)
+    return h, d
+
+
+def down_w8a8(h32_pairs, ids, w, w2: dict):
+    """The second half of act_mode 1 on its own: each pair's float32 h row [T*k, I] (pair
+    p = t*k + j) is quantised per row (quantize_rows), multiplied by its expert's w2 and
+    added to out[t] with the router weight w[t, j]. Returns out float64 [T, H]."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    q, s = quantize_rows(np.asarray(h32_pairs, dtype=np.float32))
+    hd = _LUT[q] * s.astype(np.float64)[:, None]
+    out = np.zeros((T, w2["N"]))
+    wf = np.asarray(w, dtype=np.float64).ravel()
+    for e, pairs in _pairs_by_expert(ids).items():
+        W2 = dequant_expert(w2, e)
+        b2 = expert_bias(w2, e)
+        out[pairs // k] += wf[pairs, None] * (hd[pairs] @ W2.T + b2[None, :])
+    return out
 
 
 def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
@@ -418,9 +528,8 @@ def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode
     for e in range(E):
         W13, W2 = dequant_expert(w13, e), dequant_expert(w2, e)
         b13, b2 = expert_bias(w13, e), expert_bias(w2, e)
-        for t in range(T):
-            y, _ = _expert_mlp(W13, W2, x_used[t], 1 if act_mode == 1 else 0, b13, b2)
-            out[t] += C[t, e] * y
+        Y, _ = _expert_mlp(W13, W2, x_used, 1 if act_mode == 1 else 0, b13, b2)
+        out += C[:, e:e + 1] * Y
     return out
 
 

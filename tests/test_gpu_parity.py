@@ -2,9 +2,11 @@
 
 Routing, sort and every integer result must match bit for bit; float outputs must satisfy
 max|out - ref| / max|ref| <= 2e-3 (after the bf16 output rounding for bf16 outputs, and
-with the per-output allowance for e4m3 roundings of h that an fp32 evaluation may decide
-either way on the W8A8 path). Inputs come from the seeded generators; the oracle sees host
-copies of exactly the tensors the library reads.
+with the per-output allowance for the e4m3 roundings of h that the oracle's drift bound
+leaves undecided on the W8A8 path). The W8A8 path is also checked in halves: GEMM1's h
+against the drift bound at every element, and the down GEMM + combine on the oracle's own h
+against a per-output accumulation bound. Inputs come from the seeded generators; the oracle
+sees host copies of exactly the tensors the library reads.
 """
 
 import numpy as np
@@ -13,6 +15,7 @@ import torch
 
 import block_fp8_mixture_top_amd as M
 import oracle as O
+import oracle.oracle as OO
 import workloads as W
 from helpers import REL_TOL, bank_numpy, bf16_bits, bf16_half_ulp, fp8_ulp_diff, rel_err, rel_err_bf16
 
@@ -43,10 +46,12 @@ def check_out(out, res, act_mode, what):
     err = np.abs(o - ref)
     if out.dtype == torch.bfloat16:
         err = np.maximum(0.0, err - bf16_half_ulp(np.maximum(np.abs(o), np.abs(ref))))
+    extra = ""
     if act_mode == 1:
         err = np.maximum(0.0, err - res["allowance"])
+        extra = f"allowance max {float(np.max(res['allowance'])) / den:.3e} flagged {res['n_flagged'] / res['n_h']:.3%}"
     r = float(np.max(err)) / den
-    say(what, f"rel={r:.3e}", f"raw={rel_err(o, ref):.3e}")
+    say(what, f"rel={r:.3e}", f"raw={rel_err(o, ref):.3e}", extra)
     assert np.isfinite(o).all(), what
     assert r <= REL_TOL, f"{what}: {r}"
     return r
@@ -62,6 +67,45 @@ def test_decode_every_code_exactly():
     finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
     assert np.array_equal(got[finite], lut[finite])
     assert np.array_equal(np.signbit(got[finite]), np.signbit(lut[finite]))
+
+
+def test_every_decode_path_on_every_code_and_position():
+    """Every decode the kernels use (word conversion to float, both halves; conversion to
+    bf16 with unit scale, both halves; the codes x bf16, e4m3 x e4m3 and codes x float dot
+    helpers against one-hot activations) gives every finite code's value exactly, bit for
+    bit and with its sign, at every one of the 16 byte positions of a chunk."""
+    say("decode paths")
+    lut = O.e4m3_lut()
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    n = len(finite)  # 254; chunk i holds finite[(i + 17 j) % 254] at byte j
+    idx = (np.arange(n)[:, None] + 17 * np.arange(16)[None, :]) % n
+    chunks = finite[idx]
+    got = M.decode_e4m3_paths(torch.from_numpy(chunks).to(DEV)).cpu().numpy().astype(np.float64)
+    want = lut[chunks]
+    for path in range(5):
+        g = got[:, :, path]
+        bad = np.nonzero((g != want) | (np.signbit(g) != np.signbit(want)))
+        assert bad[0].size == 0, (path, [(hex(chunks[i, j]), g[i, j], want[i, j]) for i, j in zip(*bad)][:6])
+    # every code reached every position
+    for j in range(16):
+        assert sorted(chunks[:, j].tolist()) == sorted(finite.tolist())
+
+
+@pytest.mark.parametrize("path,H", [("gather", 272), ("stream", 272), ("gather", 256), ("stream", 256),
+                                    ("mfma", 256)])
+def test_subnormal_only_banks(path, H):
+    """Banks of subnormal codes only (+-1..7 * 2^-9, unit scales), at the tiny shape and at a
+    ragged H (272: a partial last scale block), float output: a flushed or mis-decoded
+    subnormal in any kernel moves the output by far more than the bar."""
+    c = W.make_case("tiny", T=4, seed=12, H=H, kind="subnormal").to(DEV)
+    say("subnormal banks", path, H)
+    act = 1 if path == "mfma" else 0
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    assert info["path"] == path
+    res = oracle_out(c, act_mode=act)
+    assert np.abs(res["out"]).max() > 0
+    check_out(out, res, act, f"subnormal {path} H={H}")
 
 
 def test_encode_matches_oracle():
@@ -398,9 +442,87 @@ def test_prefill_sampled(decode_banks, T):
     rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(T).choice(T, 21, replace=False)]))
     res = oracle_out(c, rows=rows, act_mode=1)
     assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
-    assert res["n_flagged"] <= 0.01 * res["n_h"]
+    assert res["n_flagged"] <= 0.05 * res["n_h"]
     sub = out[torch.from_numpy(rows).to(DEV)]
     check_out(sub, res, 1, f"prefill T={T} sampled")
+
+
+def _tiles_of(offsets, tile=128):
+    """(expert, tile, half) triples of a routing: each expert's pairs in 128-pair tiles, each
+    tile in two halves of 64."""
+    out = set()
+    for e in range(len(offsets) - 1):
+        for p in range(int(offsets[e]), int(offsets[e + 1])):
+            q = p - int(offsets[e])
+            out.add((e, q // tile, (q % tile) // 64))
+    return out
+
+
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_mfma_up_h_within_drift_bound(decode_banks, T):
+    """The MFMA path's first half on its own: GEMM1's h for every (token, slot) pair, in
+    sorted order, against the oracle's exact h. Every element of every tile must lie within
+    the oracle's drift bound (coarse for all pairs; exact for all pairs of two experts), the
+    claim the oracle's W8A8 flags rest on."""
+    c = W.make_case("prefill", T=T, seed=6, device=DEV, banks=decode_banks)
+    say("mfma up", T)
+    hg = M.mfma_up(c.hidden, c.logits, c.w13, c.top_k, c.I)
+    torch.cuda.synchronize()
+    hid = bf16_bits(c.hidden)
+    ids, w, _ = O.route(c.logits.cpu().numpy(), c.top_k)
+    counts, offsets, sp = O.sort_pairs(ids, c.E)
+    w13 = bank_numpy(c.w13)
+    hgn = hg.cpu().numpy().astype(np.float64)
+    h, d = O.up_w8a8(hid, ids, w13, pairs=sp, coarse=True)
+    r = np.abs(hgn - h) / d
+    say("mfma up", T, f"max |h_gpu - h| / coarse bound {r.max():.3f}")
+    assert np.isfinite(hgn).all() and r.max() <= 1.0
+    covered = _tiles_of(offsets)
+    assert len(covered) >= c.E and all(cnt > 0 for cnt in counts)
+    for e in (0, int(np.argmax(counts))):  # exact bound: the first expert and the busiest one
+        pos = np.arange(offsets[e], offsets[e + 1])
+        he, de = O.up_w8a8(hid, ids, w13, pairs=sp[pos])
+        re = np.abs(hgn[pos] - he) / de
+        say("mfma up", T, f"expert {e}: {len(pos)} pairs, max |h_gpu - h| / bound {re.max():.3f}")
+        assert re.max() <= 1.0
+
+
+@pytest.mark.parametrize("T", [4096, 16384])
+def test_mfma_down_on_oracle_h_every_output(decode_banks, T):
+    """The MFMA path's second half on its own, fed the oracle's h (float32 of the exact h of
+    every pair): h quantisation, the down GEMM and the combine against the oracle's
+    definition of the same, on every output of every token. The h codes then follow the
+    same float32 inputs on both sides, so no rounding is ambiguous; the bound per output is
+    the accumulation bound of the down GEMM (coarse), the fp16 storage of y (2^-11 of the
+    largest |y| of its 64-output group) and the float32 combine, weighted by |w|."""
+    c = W.make_case("prefill", T=T, seed=7, device=DEV, banks=decode_banks)
+    say("mfma down", T)
+    hid = bf16_bits(c.hidden)
+    ids, w, _ = O.route(c.logits.cpu().numpy(), c.top_k)
+    counts, offsets, sp = O.sort_pairs(ids, c.E)
+    w13, w2 = bank_numpy(c.w13), bank_numpy(c.w2)
+    h, _ = O.up_w8a8(hid, ids, w13, coarse=True)
+    h32 = h.astype(np.float32)
+    out = M.mfma_down(torch.from_numpy(h32[sp]).to(DEV), c.logits, c.w2, c.top_k, c.H)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    ref = O.down_w8a8(h32, ids, w, w2)
+    # the bound, pair by pair from the oracle's own y
+    q, s = O.quantize_rows(h32)
+    hd = O.e4m3_lut()[q] * s.astype(np.float64)[:, None]
+    bound = np.zeros_like(ref)
+    k = c.top_k
+    for e, pairs in OO._pairs_by_expert(ids).items():
+        W2 = O.dequant_expert(w2, e)
+        y = hd[pairs] @ W2.T
+        g64 = np.repeat(np.abs(y).reshape(len(pairs), -1, 64).max(axis=2), 64, axis=1)
+        per = O.acc_bound(W2, hd[pairs], coarse=True) + 2.0 ** -11 * 1.01 * g64 + 2.0 ** -21 * np.abs(y)
+        bound[pairs // k] += np.abs(w.ravel()[pairs])[:, None] * per
+    err = np.abs(o - ref)
+    say("mfma down", T, f"max err/max|ref| {err.max() / np.abs(ref).max():.3e}, max err/bound {(err / bound).max():.3f}")
+    assert np.isfinite(o).all()
+    assert np.all(err <= bound)
+    assert len(_tiles_of(offsets)) >= c.E
 
 
 @pytest.mark.parametrize("T", [40, 100])

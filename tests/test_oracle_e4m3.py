@@ -177,3 +177,40 @@ def test_fp8_ulp_diff_counts_e4m3_steps():
     assert fp8_ulp_diff(np.array([1.0]), np.array([1.25]))[0] == 2.0
     assert fp8_ulp_diff(np.array([-3.0]), np.array([3.0]))[0] == 24.0  # spacing 0.25 in [2, 4)
     assert fp8_ulp_diff(np.array([0.0]), np.array([0.0]))[0] == 0.0
+
+
+def _brute_midpoint(a: float):
+    """Distance from a >= 0 to the midpoint of the two neighbouring finite e4m3 values
+    that bracket it, found by walking the list of all finite values, and that pair's
+    spacing; infinite distance at or past the largest value."""
+    vals = sorted({abs(float(x)) for x in O.e4m3_lut()[FINITE]})
+    if a >= vals[-1]:
+        return math.inf, None
+    for lo, hi in zip(vals, vals[1:]):
+        if lo <= a < hi:
+            return abs(a - (lo + hi) / 2.0), hi - lo
+    raise AssertionError("unreachable")
+
+
+def test_midpoint_distance_matches_brute_force():
+    """e4m3_midpoint_distance (used by the W8A8 ambiguity flags) against a linear walk over
+    every finite value: at every value, every midpoint and its float32 neighbours, between
+    every pair of neighbours, at random magnitudes and signs, and past the largest value."""
+    pos = sorted({abs(float(x)) for x in O.e4m3_lut()[FINITE]})
+    mids = [(a + b) / 2 for a, b in zip(pos, pos[1:])]
+    g = np.random.default_rng(5)
+    probes = list(pos) + mids
+    probes += [float(np.nextafter(np.float32(m), np.float32(np.inf))) for m in mids]
+    probes += [float(np.nextafter(np.float32(m), np.float32(-np.inf))) for m in mids]
+    probes += [a + (b - a) * f for a, b in zip(pos, pos[1:]) for f in (0.1, 0.3, 0.7, 0.9)]
+    probes += list(np.exp(g.uniform(np.log(2.0 ** -12), np.log(460.0), 3000)))
+    probes += [448.0, 449.0, 1e6]
+    v = np.array(probes, dtype=np.float64)
+    v = np.concatenate([v, -v])
+    dist, step = O.e4m3_midpoint_distance(v)
+    for x, d, s in zip(v, dist, step):
+        bd, bs = _brute_midpoint(abs(float(x)))
+        if math.isinf(bd):
+            assert math.isinf(d), x
+            continue
+        assert d == bd and s == bs, (x, d, bd, s, bs)

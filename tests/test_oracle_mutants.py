@@ -43,17 +43,17 @@ def _failures():
     return n
 
 
-def _mlp_swapped(W13, W2, xrow, act_mode, b13=None, b2=None):
+def _mlp_swapped(W13, W2, X, act_mode, b13=None, b2=None):
     I = W13.shape[0] // 2
-    a = W13 @ xrow + (0.0 if b13 is None else b13)
-    g, u = a[I:], a[:I]
-    return W2 @ (OO.silu(g) * u) + (0.0 if b2 is None else b2), None
+    A = np.atleast_2d(X) @ W13.T + (0.0 if b13 is None else b13[None, :])
+    g, u = A[:, I:], A[:, :I]
+    return (OO.silu(g) * u) @ W2.T + (0.0 if b2 is None else b2[None, :]), None
 
 
-def _mlp_no_silu(W13, W2, xrow, act_mode, b13=None, b2=None):
+def _mlp_no_silu(W13, W2, X, act_mode, b13=None, b2=None):
     I = W13.shape[0] // 2
-    a = W13 @ xrow + (0.0 if b13 is None else b13)
-    return W2 @ (a[:I] * a[I:]) + (0.0 if b2 is None else b2), None
+    A = np.atleast_2d(X) @ W13.T + (0.0 if b13 is None else b13[None, :])
+    return (A[:, :I] * A[:, I:]) @ W2.T + (0.0 if b2 is None else b2[None, :]), None
 
 
 def _bias_halves_swapped(bank, e):

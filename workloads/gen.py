@@ -175,6 +175,8 @@ def make_bank(
     """Draw an fp8 block bank expert by expert.
 
     kind ``uniform``: codes uniform over the finite e4m3 codes, scales 2^U(-10,-6).
+    kind ``subnormal``: codes uniform over the 14 nonzero subnormal codes (+-1..7 * 2^-9),
+    every scale 1.
     kind ``normal``: weights N(0, std) quantised per 128x128 block with scale
     amax/448 (stored in ``scale_dtype``) and torch's e4m3fn cast of weight/scale.
     Scale padding holds ``pad_fill`` (NaN by default, so a reader of padding sees it);
@@ -199,6 +201,12 @@ def make_bank(
             codes[e, : N * K] = finite[idx]
             u = torch.rand((rows, cols), generator=g, device=device, dtype=torch.float64)
             scales[e, :, :cols] = torch.exp2(-10.0 + 4.0 * u).to(scale_dtype)
+        elif kind == "subnormal":
+            sub = torch.tensor([m | sgn for sgn in (0x00, 0x80) for m in range(1, 8)], dtype=torch.uint8,
+                               device=device)
+            idx = torch.randint(0, sub.numel(), (N * K,), generator=g, device=device)
+            codes[e, : N * K] = sub[idx]
+            scales[e, :, :cols] = 1.0
         elif kind == "normal":
             w = torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * std
             wp = torch.zeros((rows * BLOCK, cols * BLOCK), dtype=torch.float32, device=device)
@@ -290,28 +298,31 @@ class MoECase:
 
 def make_banks(name: str, seed: int, device="cpu", *, E: Optional[int] = None, H: Optional[int] = None,
                I: Optional[int] = None, pad: Optional[str] = None, code_pad_bytes: int = 0,
-               scale_dtype: Optional[torch.dtype] = None, experts=None, bias_std: Optional[float] = None) -> tuple:
-    """The (w13, w2) banks of a workload; shapes may be overridden for tests."""
+               scale_dtype: Optional[torch.dtype] = None, experts=None, bias_std: Optional[float] = None,
+               kind: Optional[str] = None) -> tuple:
+    """The (w13, w2) banks of a workload; shapes (and the bank kind) may be overridden for tests."""
     shp = dict(SHAPES[name])
     E = E or shp["E"]
     H = H or shp["H"]
     I = I or shp["I"]
     if name == "tiny":
-        kind, sdt, rule = "uniform", torch.float32, "none"
+        kind_, sdt, rule = "uniform", torch.float32, "none"
     elif name == "large":
-        kind, sdt, rule = "normal", torch.float32, "row16"
+        kind_, sdt, rule = "normal", torch.float32, "row16"
     else:
-        kind, sdt, rule = "normal", torch.bfloat16, "row16"
+        kind_, sdt, rule = "normal", torch.bfloat16, "row16"
+    if kind is not None:
+        kind_ = kind
     if scale_dtype is not None:
         sdt = scale_dtype
     if pad is not None:
         rule = pad
     # the decode, sweep and prefill workloads share one set of banks
     bank_seed = _seed(seed, _BANK_FAMILY[name])
-    w13 = make_bank(E, 2 * I, H, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
+    w13 = make_bank(E, 2 * I, H, kind=kind_, scale_dtype=sdt, pad=rule, seed=bank_seed,
                     tensor_id=_TID_W13, device=device, code_pad_bytes=code_pad_bytes, experts=experts,
                     bias_std=bias_std)
-    w2 = make_bank(E, H, I, kind=kind, scale_dtype=sdt, pad=rule, seed=bank_seed,
+    w2 = make_bank(E, H, I, kind=kind_, scale_dtype=sdt, pad=rule, seed=bank_seed,
                    tensor_id=_TID_W2, device=device, code_pad_bytes=code_pad_bytes, experts=experts,
                    bias_std=bias_std)
     return w13, w2
