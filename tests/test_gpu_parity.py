@@ -84,7 +84,10 @@ def test_every_decode_path_on_every_code_and_position():
     want = lut[chunks]
     for path in range(5):
         g = got[:, :, path]
-        bad = np.nonzero((g != want) | (np.signbit(g) != np.signbit(want)))
+        # the conversions keep the sign of zero; a dot helper's sum starts at +0, and
+        # +0 + (-0) is +0, so for paths 2..4 only the value of 0x80 is compared
+        sign = (np.signbit(g) != np.signbit(want)) & ((want != 0) | (path < 2))
+        bad = np.nonzero((g != want) | sign)
         assert bad[0].size == 0, (path, [(hex(chunks[i, j]), g[i, j], want[i, j]) for i, j in zip(*bad)][:6])
     # every code reached every position
     for j in range(16):
