@@ -30,7 +30,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "abi_version", "lib", "make_opts", "bank_struct", "check_bank_extents", "select_path", "route_workspace_size", "route", "workspace_size",
-    "forward", "mfma_up", "mfma_down", "quantize_rows", "decode_e4m3", "decode_e4m3_paths", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
+    "forward", "forward_static", "mfma_up", "mfma_down", "quantize_rows", "decode_e4m3", "decode_e4m3_paths", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
     "PATH_STREAM", "PATH_MFMA", "PATH_NAMES", "ACT_PATH", "ACT_ROW_FP8", "ACT_GROUP_FP8",
 ]
 
@@ -228,6 +228,38 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out
     if return_routing:
         d.update(ids=ids, weights=w)
     return out, d
+
+
+def forward_static(hidden: torch.Tensor, logits: torch.Tensor, w13, w2, top_k: int, out: torch.Tensor,
+                   ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None, **opts) -> dict:
+    """moe_fp8_block_forward_static: the forward with the library's static device workspace
+    (no workspace argument, nothing allocated by the call). `out` [T, H] float32 or
+    bfloat16 must be given; ids / weights [T, top_k] optional. Returns the info dict."""
+    _need(hidden, "hidden", torch.bfloat16)
+    dev = hidden.device
+    _need(logits, "logits", torch.float32, dev)
+    T, H = hidden.shape
+    E = logits.shape[1]
+    if logits.shape[0] != T:
+        raise ValueError("hidden and logits disagree on T")
+    I = int(w2.K)
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H] float32 or bfloat16")
+    _need(out, "out", out.dtype, dev)
+    for t, name, dt in ((ids, "ids", torch.int32), (weights, "weights", torch.float32)):
+        if t is not None:
+            _need(t, name, dt, dev)
+            if tuple(t.shape) != (T, top_k):
+                raise ValueError(f"{name} must be [T, top_k]")
+    o = make_opts(**opts)
+    b13 = bank_struct(w13, E, 2 * I, H, dev)
+    b2 = bank_struct(w2, E, H, I, dev)
+    info = L.RunInfo()
+    L.check(lib().moe_fp8_block_forward_static(
+        _ptr(hidden), _ptr(logits), ctypes.byref(b13), ctypes.byref(b2), T, E, H, I, top_k, _ptr(out),
+        L.MOE_BF16 if out.dtype == torch.bfloat16 else L.MOE_F32, _ptr(ids), _ptr(weights), ctypes.byref(o),
+        ctypes.byref(info), _stream(hidden)))
+    return _info_dict(info)
 
 
 def mfma_up(hidden: torch.Tensor, logits: torch.Tensor, w13, top_k: int, I: int) -> torch.Tensor:

@@ -8,6 +8,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8_block.so")
 
+STATIC_WORKSPACE_BYTES = 64 << 20  # MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES
 ABI_VERSION = 3  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
 
 MOE_OK = 0
@@ -35,6 +36,7 @@ EXPORTS = [
     "moe_fp8_block_workspace_size",
     "moe_fp8_block_forward",
     "moe_fp8_block_forward_timed",
+    "moe_fp8_block_forward_static",
     "moe_fp8_block_mfma_up",
     "moe_fp8_block_mfma_down",
     "moe_fp8_block_quantize_rows",
@@ -103,6 +105,11 @@ _SIGS = {
         [_P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P, _P,
          ctypes.POINTER(Opts), ctypes.POINTER(RunInfo), _P, ctypes.POINTER(ctypes.c_void_p), _I,
          ctypes.POINTER(ctypes.c_int32)],
+    ),
+    "moe_fp8_block_forward_static": (
+        _I,
+        [_P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _P,
+         ctypes.POINTER(Opts), ctypes.POINTER(RunInfo), _P],
     ),
     "moe_fp8_block_mfma_up": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "moe_fp8_block_mfma_down": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P]),

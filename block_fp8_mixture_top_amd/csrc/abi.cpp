@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_fp8_block.h"
@@ -242,7 +243,8 @@ struct Runner {
 int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, const moe_fp8_bank* w2,
                  int T, int E, int H, int I, int top_k, void* out, int out_dtype, void* workspace,
                  size_t workspace_bytes, int32_t* ids_out, float* weights_out, const moe_opts* opts,
-                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds);
+                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds,
+                 size_t* checks_only = nullptr);
 int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
             const Layout& L, int T, int E, int H, int I, int top_k, float* hf);
 int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Plan& plan, void* workspace,
@@ -250,6 +252,43 @@ int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Pla
 int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, const char* bank_name, int64_t N,
                     int64_t K, int T, int E, int H, int I, int top_k, void* workspace, size_t workspace_bytes,
                     Layout* Lout, moe::Plan* plan);
+
+}  // namespace
+
+// The workspace of moe_fp8_block_forward_static: a device array of this library, one copy
+// per GPU, held until the process ends. Host code never passes the array's name to a
+// kernel (in host code it is a host-side stand-in): each device's own address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, which must be the device of
+// `stream` (the symbol is looked up with that device current).
+int static_workspace(void* stream, void** ws) {
+  int cur = 0;
+  HIP_CHECK(hipGetDevice(&cur), "hipGetDevice");
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    HIP_CHECK(hipStreamGetDevice((hipStream_t)stream, &sdev), "hipStreamGetDevice");
+    if ((int)sdev != cur)
+      return fail(MOE_ERR_ARG, "stream belongs to device %d but device %d is current", (int)sdev, cur);
+  }
+  if (cur < 0 || cur >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d past %d", cur, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || ((uintptr_t)p & (kAlign - 1)) != 0) return fail(MOE_ERR_HIP, "bad static workspace address");
+    g_scratch_ptr[cur] = p;
+  }
+  *ws = g_scratch_ptr[cur];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -344,10 +383,13 @@ KernelEvents& kernel_events() {
 
 namespace {
 
+// checks_only: run every argument check, store the workspace the call needs there and
+// return without a HIP call.
 int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, const moe_fp8_bank* w2,
                  int T, int E, int H, int I, int top_k, void* out, int out_dtype, void* workspace,
                  size_t workspace_bytes, int32_t* ids_out, float* weights_out, const moe_opts* opts,
-                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds) {
+                 moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds,
+                 size_t* checks_only) {
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "H and I must be positive (got H=%d, I=%d)", H, I);
@@ -369,12 +411,19 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     info->slots = (int)(P < E ? P : E);
     info->kernels = 0;
   }
-  if (T == 0) return ok();
+  if (T == 0) {
+    if (checks_only) *checks_only = 0;
+    return ok();
+  }
   if (!hidden || !logits || !out) return fail(MOE_ERR_ARG, "hidden, logits and out must be non-NULL");
   if (!aligned16(hidden)) return fail(MOE_ERR_ALIGN, "hidden must be 16-byte aligned");
   if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out must be 16-byte aligned");
   const int act_mode = act_of(path, o);
   const Layout L = layout_for(path, act_mode, T, E, H, I, top_k);
+  if (checks_only) {
+    *checks_only = L.total;
+    return ok();
+  }
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -558,6 +607,27 @@ int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_b
   if (!aligned16(h) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h and out must be 16-byte aligned");
   st = mfma_down(R, h, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out, out_dtype == MOE_BF16);
   return st != MOE_OK ? st : ok();
+}
+
+int moe_fp8_block_forward_static(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
+                                 const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
+                                 int out_dtype, int32_t* ids_out, float* weights_out, const moe_opts* opts,
+                                 moe_run_info* info, void* stream) {
+  size_t need = 0;
+  int st = forward_impl(hidden, logits, w13, w2, T, E, H, I, top_k, out, out_dtype, nullptr, 0, ids_out, weights_out,
+                        opts, info, stream, nullptr, 0, nullptr, &need);
+  if (st != MOE_OK) return st;
+  if (need > (size_t)MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace; the static workspace holds %zu (use moe_fp8_block_forward "
+                "with a caller workspace)",
+                need, (size_t)MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES);
+  if (T == 0) return ok();
+  void* ws = nullptr;
+  if ((st = static_workspace(stream, &ws)) != MOE_OK) return st;
+  return forward_impl(hidden, logits, w13, w2, T, E, H, I, top_k, out, out_dtype, ws,
+                      (size_t)MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES, ids_out, weights_out, opts, info, stream, nullptr,
+                      0, nullptr);
 }
 
 int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales, void* stream) {

@@ -198,6 +198,25 @@ int moe_fp8_block_forward(const uint16_t* hidden, const float* logits, const moe
                           int out_dtype, void* workspace, size_t workspace_bytes, int32_t* ids_out,
                           float* weights_out, const moe_opts* opts, moe_run_info* info, void* stream);
 
+/*
+ * moe_fp8_block_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the workspace is a
+ * static device array of the library, MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES on each GPU it
+ * runs on, held until the process ends; the caller still passes inputs and outputs. A call
+ * whose workspace (moe_fp8_block_workspace_size) exceeds that size fails with
+ * MOE_ERR_WORKSPACE before any HIP call. The call allocates nothing. Its first call on a
+ * device looks the array's address up for that device, which must be the current device
+ * and the device of `stream` (MOE_ERR_ARG otherwise). Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (concurrent streams or host threads) race;
+ * no kernel needs the array zeroed, and each call overwrites what it uses. Everything else
+ * (arguments, errors, results) is as moe_fp8_block_forward.
+ */
+#define MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES (64u << 20)
+int moe_fp8_block_forward_static(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13,
+                                 const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
+                                 int out_dtype, int32_t* ids_out, float* weights_out, const moe_opts* opts,
+                                 moe_run_info* info, void* stream);
+
 /* Kernel kinds named by moe_fp8_block_forward_timed. */
 typedef enum {
   MOE_K_ROUTE = 1,    /* top-k and weights */
