@@ -154,8 +154,8 @@ Layout layout_for(int path, int act, int T, int E, int H, int I, int top_k) {
   L.h = c.take(P * (size_t)I * 4);  // h in float, [pair or sorted position, I]
   if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);  // y in float
   if (path == MOE_PATH_MFMA) {
-    L.y = c.take(P * (size_t)H * 2);  // y in fp16, one exponent per (pair, 64 outputs)
-    L.yexp = c.take(P * (size_t)(H / 64));
+    L.y = c.take(P * (size_t)H * 2);  // y in fp16, one exponent per (pair, kYGroup outputs)
+    L.yexp = c.take(P * (size_t)(H / moe::kYGroup));
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
     L.hq = c.take(P * (size_t)I);

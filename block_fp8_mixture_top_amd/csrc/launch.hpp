@@ -117,6 +117,7 @@ hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, v
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                   hipStream_t s);
 constexpr int kMfmaTileM = 128;  // sorted pairs per MFMA tile
+constexpr int kYGroup = 32;      // MFMA path: outputs of a pair's y that share one exponent
 size_t mfma_tiles_bound(int P, int E);
 // Shapes the MFMA kernels are built for: H a multiple of 128 up to 8192, I in {128, 256, 384, 512}.
 bool mfma_shape_ok(int H, int I);
@@ -126,11 +127,11 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
 // Per-row e4m3 codes and scales (amax/448) of hf, rows in sorted-position order.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s);
 // y[pair, H] = s_h * W2 h for every pair from the h codes hq and row scales hs, stored as
-// fp16 of y * 2^-e with one exponent e per (pair, 64 outputs) in yexp[pair, H/64] (no
+// fp16 of y * 2^-e with one exponent e per (pair, kYGroup outputs) in yexp[pair, H/kYGroup] (no
 // atomics; the combine applies the weights).
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
-// out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/64] + bias[ids[t*k + j], n]),
+// out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/kYGroup] + bias[ids[t*k + j], n]),
 // slots summed in order; bias may be nullptr (no w2 bias).
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
                               const float* bias, int T, int H, int k, void* out, int out_bf16, hipStream_t s);

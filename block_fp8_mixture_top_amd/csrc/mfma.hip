@@ -19,7 +19,7 @@
 // through LDS rings a few K blocks ahead of the multiply. GEMM1 (a 128-feature block of h
 // per workgroup) writes h = silu(gate)*up in float; a row quantiser turns it into e4m3
 // codes and one scale per (token, slot); GEMM2 copies the codes to LDS, multiplies, and
-// writes each pair's y row once, in fp16 with a power-of-two exponent per 64 outputs; the
+// writes each pair's y row once, in fp16 with a power-of-two exponent per 32 outputs; the
 // combine kernel sums the slots of a token in slot order with the router weights.
 #include "common.hpp"
 #include "launch.hpp"
@@ -150,7 +150,7 @@ __device__ __forceinline__ int y_exponent(uint32_t m) {
   return ey < -60 ? -60 : (ey > 100 ? 100 : ey);
 }
 
-// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/64], slots in order; eight
+// out[t, n] = sum_j w[t, j] * y[t*k + j, n] * 2^e[t*k + j, n/32], slots in order; eight
 // consecutive outputs (within one exponent group) per thread, read as one 16-byte load per
 // slot, the slots' reads unrolled so several are in flight.
 // BIAS: each pair's y also gets its expert's w2 bias (ids give the expert) before the router
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __rest
 #pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const size_t p = t * k + j;
-    const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / 64) + n / 64]) << 23);  // 2^e
+    const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / kYGroup) + n / kYGroup]) << 23);  // 2^e
     const float wj = w[p];
     const h8 v = *(const h8*)(y + p * H + n);
     if constexpr (BIAS) {
@@ -510,59 +510,66 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- GEMM2
 
-// One workgroup per (expert, 128-pair tile, half of 64 pairs), 4 waves; the two halves of a
-// tile are consecutive workgroups of one XCD, so the second reads the expert's w2 from L2.
-// A = h codes (pairs as rows; e4m3 per (token, slot) row, scale amax/448, from the row
-// quantiser), B = w2 rows (features). The half's h codes are copied to LDS once and then
-// read into registers, every K block of them (at most 128 VGPRs), which leaves the whole
-// LDS to the w2 stream. The H outputs go in chunks of 256; wave w owns features 64w ..
-// 64w+64 of each chunk (FT = 4 MFMA tiles; a last chunk of 128 has work for waves 0 and 1
-// only), so lane (r16, kq) of a result holds pairs 4kq..4kq+3 of feature r16. Each wave
-// streams its own w2 rows, (chunk, K block) after (chunk, K block), through a private
-// kRing2-deep LDS ring with kRing2 - 1 stages in flight and no barriers. Each pair's y row
-// = s_h * W2 h is written once, in fp16 with an exponent per 64 outputs; the combine kernel
-// applies the router weights. The fp16 values of 16 pairs x 64 features pass through a 2 KB
-// LDS area of the wave so that each lane stores 32 contiguous bytes: 8 store instructions
-// per chunk instead of 64 two-byte ones, all of which count against the w2 copies' wait. The
-// 64 exponents of a chunk go the same way, one byte store instead of 16.
+// One workgroup per (expert, 64-pair half of a 128-pair tile), 4 waves, one per SIMD; the
+// two halves of a tile are consecutive items on one XCD, so the second reads the expert's w2
+// from L2. A = w2 rows (features), B = the half's h codes (pairs as rows; e4m3 per (token,
+// slot) row, scale amax/448, from the row quantiser), so lane (r16, kq) of a 16x16 result
+// holds outputs 4kq..4kq+3 of pair r16: four consecutive outputs of one pair, written with
+// one 8-byte store. The H outputs go in chunks of 256; wave w multiplies outputs 64w ..
+// 64w+63 of each chunk (4 feature tiles) by the half's 64 pairs (4 pair tiles, whose h codes
+// stay in registers for every K block). Each wave streams its own w2 rows, (chunk, K block)
+// after (chunk, K block), through a private kRing2-deep LDS ring with kRing2 - 1 stages in
+// flight and no barriers. Each MFMA starts from zero and its block product is scaled into
+// the accumulator on the VALU while the next MFMA runs. Each pair's y row = s_h * W2 h is
+// written once, in fp16 with one power-of-two exponent per kYGroup (32) outputs; the combine
+// kernel applies the router weights. (Measured on gfx950: 128 pairs per workgroup, a ring
+// shared by the four waves, or two waves per SIMD were no faster; the w2 stream is held back
+// by the vector memory path's pending-miss stalls, not by the bytes per MFMA.)
 constexpr int kRing2 = 4;
+constexpr int kG2PairTiles = 4;  // pair tiles per workgroup (16 pairs each)
 
 // Wait for the copy of the stage issued `later` stages before the newest one: the loads of
-// the `later` younger stages (8 each) may stay outstanding. Loads complete in issue order,
+// the `later` younger stages (PER each) may stay outstanding. Loads complete in issue order,
 // so the count is exact for them; stores issued meanwhile (they may complete out of order)
 // can only make the wait longer, never shorter.
+template <int PER>  // loads per stage
 __device__ __forceinline__ void wait_stage(int later) {
-  if (later >= 3) wait_vm<24>();
-  else if (later == 2) wait_vm<16>();
-  else if (later == 1) wait_vm<8>();
+  if (later >= 3) wait_vm<3 * PER>();
+  else if (later == 2) wait_vm<2 * PER>();
+  else if (later == 1) wait_vm<PER>();
   else wait_vm<0>();
 }
 
-template <int KB>  // I / 128
+template <int KB, int NP>  // I / 128, pair tiles per workgroup (NP * 16 pairs)
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
                                                             int H, int I, int nblocks, _Float16* __restrict__ y,
                                                             int8_t* __restrict__ yexp) {
-  constexpr int HM = 64;           // pairs per half tile
-  constexpr int FT = 4;
-  constexpr int NCH = 4 * FT * 16;
-  constexpr int WB = 64 * kRowB;   // one wave's w2 rows of a stage
-  constexpr int HB = HM * kRowB;   // the h codes of one K block
-  static_assert(KB * HB <= 4 * kRing2 * WB, "the h codes are staged in the ring");
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  constexpr int TP = NP * 16;      // pairs per workgroup
+  constexpr int PARTS = kTM / TP;  // workgroups per 128-pair tile
+  constexpr int NW = 4;            // waves, one per SIMD
+  constexpr int NF = 4;            // feature tiles per wave (64 outputs)
+  constexpr int FW = NF * 16;      // outputs per wave and chunk
+  constexpr int NCH = NW * FW;     // outputs per chunk
+  constexpr int WB = FW * kRowB;   // one wave's w2 rows of a stage
+  constexpr int HB = TP * kRowB;   // the workgroup's h codes of one K block
+  static_assert(KB * HB <= NW * kRing2 * WB, "the h codes are staged in the ring");
   static_assert(kRing2 - 1 <= 3, "wait_stage covers up to three younger stages");
-  __shared__ __align__(16) uint8_t ring[4 * kRing2 * WB];
+  __shared__ __align__(16) uint8_t ring[NW * kRing2 * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
-  __shared__ __align__(16) _Float16 s_y[4][16 * 64];  // per wave: pairs 4kq+q x 64 features
-  __shared__ int8_t s_e[4][64];                       // per wave: the y exponents of a chunk
+  __shared__ float s_hs[TP];
+  __shared__ int s_prow[TP];
 
-  const int nitems = plan.tile_off[E] * 2;
-  const int L = xcd_item(blockIdx.x, nitems);
+  const int nitems = plan.tile_off[E] * PARTS;
+  const int L = xcd_item(blockIdx.x, nitems);  // consecutive items of an expert share its w2 in L2
   if (L >= nitems) return;
-  const int tile = L >> 1, half = L & 1;
+  const int tile = L / PARTS, part = L - tile * PARTS;
   const int e = find_expert(plan.tile_off, E, tile);
-  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM + half * HM;
+  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM + part * TP;
+  if (pos0 >= plan.offsets[e + 1]) return;
   const int pos_end = plan.offsets[e + 1];
-  if (pos0 >= pos_end) return;
+  const int nvalid = pos_end - pos0 < TP ? pos_end - pos0 : TP;
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -570,16 +577,47 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
 
-  // chunks holding features of this wave: those with c * NCH + 64 * wave < H (H is a
-  // multiple of 128, so a wave's 64 features are all in range or all out)
-  const int nch = (H - wave * 64 + NCH - 1) / NCH;
-  const int nst = nch * KB;
-  // w2 copy i covers rows 8i .. 8i+7 of the wave's 64; chunk c adds c * NCH rows
-  uint32_t woff[8];
+  stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
+  if (tid < TP) {
+    const bool ok = tid < nvalid;
+    s_hs[tid] = hs[pos0 + (ok ? tid : 0)];
+    s_prow[tid] = ok ? plan.sorted[pos0 + tid] : -1;
+  }
+  // the h codes into the ring space: (TP / 8) * KB copies of 8 rows x 128 bytes, a quarter
+  // per wave (rows past the expert's pairs copy the first row; their results are never stored)
+  constexpr int RG = TP / 8;  // 8-row groups
+  static_assert((RG * KB) % NW == 0, "every wave copies the same number of row groups");
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < RG * KB / NW; ++i) {
+    const int q = wave + NW * i;
+    const int kb = q / RG, r = (q % RG) * 8 + lr;
+    const int rr = r < nvalid ? r : 0;
+    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q % RG) * 1024);
+  }
+  wait_vm<0>();  // everyone's h codes, scales and pair rows are in after the barrier
+  __syncthreads();
+  // pair tiles with no valid pair (in a tile's last, partial tile) are multiplied anyway
+  // (rows past the expert's pairs hold the first row's codes) and their results dropped
+  const int npt = min(NP, (nvalid + 15) / 16);
+  i32x8 bh[KB][NP];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int pt = 0; pt < NP; ++pt) bh[kb][pt] = lds_operand(ring + kb * HB, pt * 16 + r16, kq);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's h reads are done
+  __syncthreads();                     // and everyone's, before the ring is refilled
+
+  // chunks holding outputs of this wave: those with c * NCH + FW * wave < H (H is a
+  // multiple of 128, so a wave's FW outputs are all in range or all out)
+  const int nch = (H - wave * FW + NCH - 1) / NCH;
+  const int nst = nch * KB;
+  // w2 copy i covers rows 8i .. 8i+7 of the wave's FW; chunk c adds c * NCH rows
+  constexpr int NCP = FW / 8;  // copies per wave and stage
+  uint32_t woff[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
     const int b = i * 8 + lr;
-    woff[i] = (uint32_t)(wave * 64 + b) * (uint32_t)I + (uint32_t)((lc ^ sw(b)) << 4);
+    woff[i] = (uint32_t)(wave * FW + b) * (uint32_t)I + (uint32_t)((lc ^ sw(b)) << 4);
   }
   uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
@@ -587,144 +625,99 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const uint8_t* src = wb + (size_t)c * NCH * I + kb * 128;
     uint8_t* slot = myring + (st % kRing2) * WB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g2lds(src + woff[i], slot + i * 1024);
+    for (int i = 0; i < NCP; ++i) g2lds(src + woff[i], slot + i * 1024);
   };
-  stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
-  const int nvalid = pos_end - pos0 < HM ? pos_end - pos0 : HM;
-  // the half's h codes into the ring space: 8 * KB copies of 8 rows x 128 bytes, 2 * KB per
-  // wave (rows past the expert's pairs copy the first row; their results are never stored)
 #pragma unroll
-  for (int i = 0; i < 2 * KB; ++i) {
-    const int q = wave * 2 * KB + i;
-    const int kb = q >> 3, r = (q & 7) * 8 + lr;
-    const int rr = r < nvalid ? r : 0;
-    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q & 7) * 1024);
-  }
-  float hsc[4][4];
-  int prow[4][4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = pt * 16 + kq * 4 + q;
-      const bool ok = r < nvalid;
-      hsc[pt][q] = hs[pos0 + (ok ? r : 0)];
-      prow[pt][q] = ok ? plan.sorted[pos0 + r] : -1;
-    }
-  // the y stores from LDS: lane (srow, sseg) writes features 16 sseg .. 16 sseg + 15 of pair
-  // pt * 16 + srow
-  const int srow = lane >> 2, sseg = lane & 3;
-  int prow_st[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    const int r = pt * 16 + srow;
-    prow_st[pt] = r < nvalid ? plan.sorted[pos0 + r] : -1;
-  }
-  const int prow_e = lane < nvalid ? plan.sorted[pos0 + lane] : -1;  // lane's pair for the exponents
-  wait_vm<0>();  // everyone's h codes and the block scales are in after the barrier
-  __syncthreads();
-  i32x8 a[KB][4];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) a[kb][pt] = lds_operand(ring + kb * HB, pt * 16 + r16, kq);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's h reads are done
-  __syncthreads();                     // and everyone's, before the ring is refilled
-
-#pragma unroll
-  for (int s = 0; s < kRing2 - 1; ++s)
-    if (s < nst) issue(s);
-  f32x4 acc[FT][4];
+  for (int st = 0; st < kRing2 - 1; ++st)
+    if (st < nst) issue(st);
+  f32x4 acc[NF][NP];
   // (chunk c, K block kb) is stage st = c * KB + kb; kb is unrolled so that the h operands
   // are indexed statically and stay in registers
   for (int c = 0; c < nch; ++c) {
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = c * KB + kb;
-    // stage st has landed once at most min(kRing2 - 2, nst - 1 - st) younger stages remain
-    wait_stage(min(kRing2 - 2, nst - 1 - st));
-    // the slot of stage st - 1 is refilled next, so this wave's reads of it must have
-    // completed: the compiler waits for them only where their values are used, which it may
-    // schedule after this refill, and nothing orders a pending LDS read before direct loads
-    // into the same bytes
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (st + kRing2 - 1 < nst) issue(st + kRing2 - 1);
-    if (kb == 0) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int st = c * KB + kb;
+      // stage st has landed once at most min(kRing2 - 2, nst - 1 - st) younger stages remain
+      wait_stage<NCP>(min(kRing2 - 2, nst - 1 - st));
+      // the slot of stage st - 1 is refilled next, so this wave's reads of it must have
+      // completed: the compiler waits for them only where their values are used, which it may
+      // schedule after this refill, and nothing orders a pending LDS read before direct loads
+      // into the same bytes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (st + kRing2 - 1 < nst) issue(st + kRing2 - 1);
+      if (kb == 0) {
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+        for (int ft = 0; ft < NF; ++ft)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const uint8_t* slot = myring + (st % kRing2) * WB;
-    i32x8 bw[FT];
+          for (int pt = 0; pt < NP; ++pt) acc[ft][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      const uint8_t* slot = myring + (st % kRing2) * WB;
+      i32x8 aw[NF];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) bw[ft] = lds_operand(slot, ft * 16 + r16, kq);
-    const int n0 = c * NCH + wave * 64;
-    // features n0 .. n0 + 63 share one 128-row scale block
-    const int nb = n0 / kScaleBlock;
-    // each MFMA starts from zero and its block product is scaled into the accumulator on
-    // the VALU while the next MFMA runs
-    const float sc = s_sc[nb * KB + kb];  // uniform
-    {
+      for (int ft = 0; ft < NF; ++ft) aw[ft] = lds_operand(slot, ft * 16 + r16, kq);
+      const int n0 = c * NCH + wave * FW;
+      // outputs n0 .. n0 + FW - 1 share one 128-row scale block
+      const float sc = s_sc[(n0 / kScaleBlock) * KB + kb];  // uniform
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      f32x4 pp = mfma_fp8(a[kb][0], bw[0], z);
+      {
+        f32x4 pp = mfma_fp8(aw[0], bh[kb][0], z);
 #pragma unroll
-      for (int j = 0; j < FT * 4; ++j) {
-        const int ft = j / 4, pt = j % 4;
-        f32x4 nx;
-        if (j + 1 < FT * 4) nx = mfma_fp8(a[kb][(j + 1) % 4], bw[(j + 1) / 4], z);
+        for (int j = 0; j < NF * NP; ++j) {
+          const int ft = j / NP, pt = j % NP;
+          f32x4 nx;
+          if (j + 1 < NF * NP) nx = mfma_fp8(aw[(j + 1) / NP], bh[kb][(j + 1) % NP], z);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
-        if (j + 1 < FT * 4) pp = nx;
+          for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
+          if (j + 1 < NF * NP) pp = nx;
+        }
       }
-    }
-    if (kb == KB - 1) {
-      // y of pair (pt, 4kq+q), features n0 .. n0+63, held by the 16 lanes of row kq (r16)
-      // times FT: stored in fp16 with one power-of-two exponent per (pair, 64 features)
-      _Float16* sy = s_y[wave];
+      if (kb == KB - 1) {
+        // y of pair 16pt + r16, outputs n0 + 16ft + 4kq .. +3, in fp16 with one exponent per
+        // kYGroup outputs of the pair (GT feature tiles, held by lanes r16 + 16 kq)
+        constexpr int GT = kYGroup / 16;
+        static_assert(NF % GT == 0, "a wave's outputs are whole exponent groups");
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+        for (int pt = 0; pt < NP; ++pt) {
+          if (pt < npt) {
+            const int rl = pt * 16 + r16;
+            const int prow = s_prow[rl];
+            const float hsc = s_hs[rl];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v[FT];
-          uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
+            for (int g = 0; g < NF / GT; ++g) {
+              float v[GT][4];
+              uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) {
-            v[ft] = acc[ft][pt][q] * hsc[pt][q];
-            m = max(m, __float_as_uint(__builtin_fabsf(v[ft])));
+              for (int f = 0; f < GT; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  v[f][q] = acc[g * GT + f][pt][q] * hsc;
+                  m = max(m, __float_as_uint(__builtin_fabsf(v[f][q])));
+                }
+              m = max(m, (uint32_t)__shfl_xor((int)m, 16, kWave));
+              m = max(m, (uint32_t)__shfl_xor((int)m, 32, kWave));
+              const int ey = y_exponent(m);
+              const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
+              if (prow >= 0) {
+#pragma unroll
+                for (int f = 0; f < GT; ++f) {
+                  const h4 o = {(_Float16)(v[f][0] * down), (_Float16)(v[f][1] * down),
+                                (_Float16)(v[f][2] * down), (_Float16)(v[f][3] * down)};
+                  *(h4*)(y + (size_t)prow * H + n0 + (g * GT + f) * 16 + kq * 4) = o;
+                }
+                if (kq == 0) yexp[(size_t)prow * (H / kYGroup) + n0 / kYGroup + g] = (int8_t)ey;
+              }
+            }
           }
-          m = max(m, dpp_u32<0xB1, 0xF, 0xF>(0u, m));   // quad_perm [1,0,3,2]
-          m = max(m, dpp_u32<0x4E, 0xF, 0xF>(0u, m));   // quad_perm [2,3,0,1]
-          m = max(m, dpp_u32<0x124, 0xF, 0xF>(0u, m));  // row_ror:4
-          m = max(m, dpp_u32<0x128, 0xF, 0xF>(0u, m));  // row_ror:8
-          const int ey = y_exponent(m);
-          const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft) sy[(kq * 4 + q) * 64 + ft * 16 + r16] = (_Float16)(v[ft] * down);
-          if (r16 == 0) s_e[wave][pt * 16 + kq * 4 + q] = (int8_t)ey;
         }
-        wave_lds_sync();
-        const u32x4 lo = *(const u32x4*)(sy + srow * 64 + sseg * 16);
-        const u32x4 hi = *(const u32x4*)(sy + srow * 64 + sseg * 16 + 8);
-        if (prow_st[pt] >= 0) {
-          u32x4* yr = (u32x4*)(y + (size_t)prow_st[pt] * H + n0 + sseg * 16);
-          yr[0] = lo;
-          yr[1] = hi;
-        }
-        wave_lds_sync();  // the reads are done before the next pair tile overwrites the area
       }
-      // one byte store for the chunk's 64 exponents instead of one per (pair tile, q)
-      const int8_t ee = s_e[wave][lane];
-      if (prow_e >= 0) yexp[(size_t)prow_e * (H / 64) + n0 / 64] = ee;
-      wave_lds_sync();
     }
-  }
   }
 }
-template <int KB>
+template <int KB, int NP>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
                int I, _Float16* y, int8_t* yexp, hipStream_t s) {
-  launch_kernel(gemm2_mfma_kernel<KB>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y, yexp);
+  launch_kernel(gemm2_mfma_kernel<KB, NP>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y,
+                yexp);
   return hipGetLastError();
 }
 
@@ -792,12 +785,12 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
-  const int nblocks = (int)mfma_tiles_bound(P, E) * 2;
+  const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
   switch (I / 128) {
-    case 1: return g2m<1>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    case 2: return g2m<2>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    case 3: return g2m<3>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    default: return g2m<4>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    case 1: return g2m<1, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    case 2: return g2m<2, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    case 3: return g2m<3, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+    default: return g2m<4, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
   }
 }
 

@@ -189,7 +189,7 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  * quantises x per token and h per (token, slot) row to e4m3 with scale amax/448 (float
  * division, 1 for a zero row; codes round to nearest even and saturate at 448) and
  * multiplies on the fp8 matrix cores; its per-(token, slot) down-projection results reach
- * the combine in fp16 with a power-of-two exponent per 64 outputs (at most 2^-11 relative
+ * the combine in fp16 with a power-of-two exponent per 32 outputs (at most 2^-11 relative
  * rounding each). Every path writes each (token, slot) result once and sums a token's
  * slots in slot order, so all of them are deterministic.
  */

@@ -497,7 +497,7 @@ def test_mfma_down_on_oracle_h_every_output(decode_banks, T):
     definition of the same, on every output of every token. The h codes then follow the
     same float32 inputs on both sides, so no rounding is ambiguous; the bound per output is
     the accumulation bound of the down GEMM (coarse), the fp16 storage of y (2^-11 of the
-    largest |y| of its 64-output group) and the float32 combine, weighted by |w|."""
+    largest |y| of its 32-output group) and the float32 combine, weighted by |w|."""
     c = W.make_case("prefill", T=T, seed=7, device=DEV, banks=decode_banks)
     say("mfma down", T)
     hid = bf16_bits(c.hidden)
@@ -518,8 +518,8 @@ def test_mfma_down_on_oracle_h_every_output(decode_banks, T):
     for e, pairs in OO._pairs_by_expert(ids).items():
         W2 = O.dequant_expert(w2, e)
         y = hd[pairs] @ W2.T
-        g64 = np.repeat(np.abs(y).reshape(len(pairs), -1, 64).max(axis=2), 64, axis=1)
-        per = O.acc_bound(W2, hd[pairs], coarse=True) + 2.0 ** -11 * 1.01 * g64 + 2.0 ** -21 * np.abs(y)
+        g32 = np.repeat(np.abs(y).reshape(len(pairs), -1, 32).max(axis=2), 32, axis=1)
+        per = O.acc_bound(W2, hd[pairs], coarse=True) + 2.0 ** -11 * 1.01 * g32 + 2.0 ** -21 * np.abs(y)
         bound[pairs // k] += np.abs(w.ravel()[pairs])[:, None] * per
     err = np.abs(o - ref)
     say("mfma down", T, f"max err/max|ref| {err.max() / np.abs(ref).max():.3e}, max err/bound {(err / bound).max():.3f}")
