@@ -110,7 +110,7 @@ int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* 
       return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 needs H %% 128 == 0 (got H=%d)", H);
   }
   if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
-    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H and I multiples of 128, H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
     p = MOE_PATH_STREAM;
   }
   if (p == MOE_PATH_GATHER && !moe::gemm2_gather_supported(top_k, I)) {
@@ -154,8 +154,10 @@ Layout layout_for(int path, int act, int T, int E, int H, int I, int top_k) {
   L.h = c.take(P * (size_t)I * 4);  // h in float, [pair or sorted position, I]
   if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);  // y in float
   if (path == MOE_PATH_MFMA) {
-    L.y = c.take(P * (size_t)H * 2);  // y in fp16, one exponent per (pair, kYGroup outputs)
-    L.yexp = c.take(P * (size_t)(H / moe::kYGroup));
+    // y in fp16, one exponent per (pair, kYGroup outputs), one plane per K part of GEMM2
+    const size_t parts = (size_t)moe::mfma_k_parts(I);
+    L.y = c.take(parts * P * (size_t)H * 2);
+    L.yexp = c.take(parts * P * (size_t)(H / moe::kYGroup));
     L.xq = c.take((size_t)T * H);
     L.xs = c.take((size_t)T * 4);
     L.hq = c.take(P * (size_t)I);
@@ -513,7 +515,8 @@ int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Pla
   _Float16* y16 = at<_Float16>(workspace, L.y);
   int8_t* yexp = at<int8_t>(workspace, L.yexp);
   RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
-  RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, plan.w, plan.ids, b2.bias, T, H, top_k, out, out_bf16, s),
+  RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, plan.w, plan.ids, b2.bias, T, H, top_k, moe::mfma_k_parts(I),
+                                             out, out_bf16, s),
       "combine launch");
   return MOE_OK;
 }
@@ -526,7 +529,7 @@ int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, co
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (!moe::mfma_shape_ok(H, I))
-    return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I in {128,256,384,512} (got H=%d, I=%d)", H, I);
+    return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H and I multiples of 128, H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
   if ((st = check_bank(bank, bank_name, E, N, K))) return st;
   if (T == 0) return ok();
   if (!logits) return fail(MOE_ERR_ARG, "logits must be non-NULL");

@@ -119,8 +119,13 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t
 constexpr int kMfmaTileM = 128;  // sorted pairs per MFMA tile
 constexpr int kYGroup = 32;      // MFMA path: outputs of a pair's y that share one exponent
 size_t mfma_tiles_bound(int P, int E);
-// Shapes the MFMA kernels are built for: H a multiple of 128 up to 8192, I in {128, 256, 384, 512}.
+// Shapes the MFMA kernels are built for: H a multiple of 128 up to 8192, I a multiple of 128
+// up to 4096.
 bool mfma_shape_ok(int H, int I);
+// GEMM2 on the matrix cores multiplies up to kMfmaPartBlocks 128-wide K blocks of h per launch;
+// I beyond that runs in mfma_k_parts(I) K parts, each writing its own y plane.
+constexpr int kMfmaPartBlocks = 4;
+int mfma_k_parts(int I);
 // hf[p, I] = silu(gate) * up in float for every sorted pair position p.
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
                              int P, int H, int I, int k, float* hf, hipStream_t s);
@@ -133,8 +138,10 @@ hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& 
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
 // out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/kYGroup] + bias[ids[t*k + j], n]),
 // slots summed in order; bias may be nullptr (no w2 bias).
+// parts: the number of y planes (K parts) of each pair, summed in plane order first.
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
-                              const float* bias, int T, int H, int k, void* out, int out_bf16, hipStream_t s);
+                              const float* bias, int T, int H, int k, int parts, void* out, int out_bf16,
+                              hipStream_t s);
 
 // Test exports.
 hipError_t launch_decode_e4m3(const uint8_t* codes, float* out, int64_t n, hipStream_t s);

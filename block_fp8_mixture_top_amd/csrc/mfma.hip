@@ -155,33 +155,45 @@ __device__ __forceinline__ int y_exponent(uint32_t m) {
 // slot, the slots' reads unrolled so several are in flight.
 // BIAS: each pair's y also gets its expert's w2 bias (ids give the expert) before the router
 // weight is applied.
+// With I > 512 a pair's y comes in `parts` planes (K parts), summed first, in plane order.
 template <bool BIAS>
 __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __restrict__ y,
                                                           const int8_t* __restrict__ yexp,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ ids,
                                                           const float* __restrict__ bias, int T, int H, int k,
-                                                          void* __restrict__ out, int out_bf16) {
+                                                          int parts, void* __restrict__ out, int out_bf16) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (idx >= (size_t)T * H) return;
   const size_t t = idx / H, n = idx % H;
+  const size_t yplane = (size_t)T * k * H, eplane = (size_t)T * k * (H / kYGroup);
   float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const size_t p = t * k + j;
-    const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / kYGroup) + n / kYGroup]) << 23);  // 2^e
     const float wj = w[p];
-    const h8 v = *(const h8*)(y + p * H + n);
+    float yv[8];
+    {
+      const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / kYGroup) + n / kYGroup]) << 23);  // 2^e
+      const h8 v = *(const h8*)(y + p * H + n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) yv[q] = (float)v[q] * up;
+    }
+    for (int part = 1; part < parts; ++part) {
+      const float up = __uint_as_float((uint32_t)(127 + yexp[part * eplane + p * (H / kYGroup) + n / kYGroup]) << 23);
+      const h8 v = *(const h8*)(y + part * yplane + p * H + n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) yv[q] = __builtin_fmaf((float)v[q], up, yv[q]);
+    }
     if constexpr (BIAS) {
       const float* b = bias + (size_t)ids[p] * H + n;
       const f32x4 b0 = *(const f32x4*)b, b1 = *(const f32x4*)(b + 4);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        s[q] = __builtin_fmaf(wj, __builtin_fmaf((float)v[q], up, q < 4 ? b0[q] : b1[q - 4]), s[q]);
+      for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, yv[q] + (q < 4 ? b0[q] : b1[q - 4]), s[q]);
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, (float)v[q] * up, s[q]);
+      for (int q = 0; q < 8; ++q) s[q] = __builtin_fmaf(wj, yv[q], s[q]);
     }
   }
   if (out_bf16) {
@@ -231,7 +243,8 @@ __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgc
 
 constexpr int kTM = kMfmaTileM;  // pairs per tile
 constexpr int kMaxH = 8192;      // bounds the block-scale slabs staged in LDS
-constexpr int kMaxI = 512;       // GEMM2 keeps a half tile of h codes (64 x I) in LDS
+constexpr int kMaxI = 512;       // GEMM2 holds the h codes of up to 4 K blocks (one K part) in registers
+constexpr int kMaxIParts = 4096; // I beyond 512 runs GEMM2 in K parts, one y plane each
 constexpr int kStages = 3;       // depth of the LDS rings
 constexpr int kRowB = 128;       // bytes of one row in one 128-wide K block
 
@@ -543,8 +556,10 @@ __device__ __forceinline__ void wait_stage(int later) {
 template <int KB, int NP>  // I / 128, pair tiles per workgroup (NP * 16 pairs)
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
-                                                            int H, int I, int nblocks, _Float16* __restrict__ y,
+                                                            int H, int I, int nblocks, int kb0, _Float16* __restrict__ y,
                                                             int8_t* __restrict__ yexp) {
+  // this launch multiplies K blocks kb0 .. kb0 + KB - 1 of h and w2 (a part of K when
+  // I > 512) and writes that part's y plane; y and yexp point at the plane
   typedef _Float16 h4 __attribute__((ext_vector_type(4)));
   constexpr int TP = NP * 16;      // pairs per workgroup
   constexpr int PARTS = kTM / TP;  // workgroups per 128-pair tile
@@ -577,7 +592,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
 
-  stage_scales(s_sc, w2, (int64_t)e * w2.sexp, H / 128, KB);
+  stage_scales(s_sc, w2, (int64_t)e * w2.sexp + kb0, H / 128, KB);
   if (tid < TP) {
     const bool ok = tid < nvalid;
     s_hs[tid] = hs[pos0 + (ok ? tid : 0)];
@@ -592,7 +607,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const int q = wave + NW * i;
     const int kb = q / RG, r = (q % RG) * 8 + lr;
     const int rr = r < nvalid ? r : 0;
-    g2lds(hq + (size_t)(pos0 + rr) * I + kb * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q % RG) * 1024);
+    g2lds(hq + (size_t)(pos0 + rr) * I + (kb0 + kb) * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q % RG) * 1024);
   }
   wait_vm<0>();  // everyone's h codes, scales and pair rows are in after the barrier
   __syncthreads();
@@ -622,7 +637,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
     const int c = st / KB, kb = st - c * KB;
-    const uint8_t* src = wb + (size_t)c * NCH * I + kb * 128;
+    const uint8_t* src = wb + (size_t)c * NCH * I + (kb0 + kb) * 128;
     uint8_t* slot = myring + (st % kRing2) * WB;
 #pragma unroll
     for (int i = 0; i < NCP; ++i) g2lds(src + woff[i], slot + i * 1024);
@@ -715,9 +730,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
 }
 template <int KB, int NP>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
-               int I, _Float16* y, int8_t* yexp, hipStream_t s) {
-  launch_kernel(gemm2_mfma_kernel<KB, NP>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, y,
-                yexp);
+               int I, int kb0, _Float16* y, int8_t* yexp, hipStream_t s) {
+  launch_kernel(gemm2_mfma_kernel<KB, NP>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, kb0,
+                y, yexp);
   return hipGetLastError();
 }
 
@@ -732,8 +747,10 @@ size_t mfma_tiles_bound(int P, int E) {
 }
 
 bool mfma_shape_ok(int H, int I) {
-  return H % 128 == 0 && H > 0 && H <= kMaxH && I % 128 == 0 && I >= 128 && I <= kMaxI;
+  return H % 128 == 0 && H > 0 && H <= kMaxH && I % 128 == 0 && I >= 128 && I <= kMaxIParts;
 }
+
+int mfma_k_parts(int I) { return (I / 128 + kMfmaPartBlocks - 1) / kMfmaPartBlocks; }
 
 // Pieces of 8 values per lane, 512 columns per wave and piece; rows of up to 8192 columns.
 #define MOE_QUANT_LAUNCH(KERNEL, T)                                                                          \
@@ -763,14 +780,15 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* co
 }
 
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
-                              const float* bias, int T, int H, int k, void* out, int out_bf16, hipStream_t s) {
+                              const float* bias, int T, int H, int k, int parts, void* out, int out_bf16,
+                              hipStream_t s) {
   const size_t n = (size_t)T * H / 8;
   if (bias != nullptr)
     launch_kernel(combine_f16_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, ids,
-                  bias, T, H, k, out, out_bf16);
+                  bias, T, H, k, parts, out, out_bf16);
   else
     launch_kernel(combine_f16_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, yexp, w, ids,
-                  bias, T, H, k, out, out_bf16);
+                  bias, T, H, k, parts, out, out_bf16);
   return hipGetLastError();
 }
 
@@ -786,12 +804,23 @@ hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& 
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
-  switch (I / 128) {
-    case 1: return g2m<1, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    case 2: return g2m<2, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    case 3: return g2m<3, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
-    default: return g2m<4, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, y, yexp, s);
+  // K parts of up to four 128-wide blocks, each into its own y plane
+  const int nkb = I / 128;
+  for (int part = 0; part < mfma_k_parts(I); ++part) {
+    const int kb0 = part * kMfmaPartBlocks;
+    const int kbn = nkb - kb0 < kMfmaPartBlocks ? nkb - kb0 : kMfmaPartBlocks;
+    _Float16* yp = y + (size_t)part * P * H;
+    int8_t* ep = yexp + (size_t)part * P * (H / kYGroup);
+    hipError_t err;
+    switch (kbn) {
+      case 1: err = g2m<1, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      case 2: err = g2m<2, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      case 3: err = g2m<3, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      default: err = g2m<4, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+    }
+    if (err != hipSuccess) return err;
   }
+  return hipSuccess;
 }
 
 }  // namespace moe

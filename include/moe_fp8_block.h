@@ -249,7 +249,7 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
  * Test exports: the two halves of the MFMA path (route + sort first in each), so that each
  * half can be checked against a reference on its own inputs. Both take the workspace of a
  * forward forced onto MFMA (moe_fp8_block_workspace_size with force_path MOE_PATH_MFMA)
- * and need H a multiple of 128 up to 8192 and I in {128, 256, 384, 512}
+ * and need H a multiple of 128 up to 8192 and I a multiple of 128 up to 4096
  * (MOE_ERR_UNSUPPORTED otherwise).
  *   mfma_up:   x quantised per token (as quantize_rows), GEMM1 on the fp8 matrix cores and
  *              h = silu(gate) * up written in float to h [T*top_k, I], row p holding the

@@ -185,11 +185,11 @@ def test_forward_forced_path_is_never_downgraded(lib):
     o = L.Opts()
     lib.moe_fp8_block_default_opts(ctypes.byref(o))
     o.force_path = 3
-    st, msg, _ = _forward(lib, T=4, H=256, I=1024, opts=o)
+    st, msg, _ = _forward(lib, T=4, H=256, I=4224, opts=o)
     assert st == -2 and "MFMA" in msg
     o.force_path = 0
     # the gate alone may move off an unsupported MFMA shape, and reports it
-    st, _, info = _forward(lib, T=4096, E=8, H=256, I=1024, ws_bytes=16, opts=o)
+    st, _, info = _forward(lib, T=4096, E=8, H=256, I=4224, ws_bytes=16, opts=o)
     assert st == -5 and info.path == 2
 
 

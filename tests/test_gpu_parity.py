@@ -528,6 +528,72 @@ def test_mfma_down_on_oracle_h_every_output(decode_banks, T):
     assert len(_tiles_of(offsets)) >= c.E
 
 
+def _staged_mfma_check(c, what):
+    """Both MFMA halves of case c on their own against the oracle, at every pair and output
+    (as test_mfma_up_h_within_drift_bound and test_mfma_down_on_oracle_h_every_output)."""
+    hid = bf16_bits(c.hidden)
+    ids, w, _ = O.route(c.logits.cpu().numpy(), c.top_k)
+    counts, offsets, sp = O.sort_pairs(ids, c.E)
+    w13, w2 = bank_numpy(c.w13), bank_numpy(c.w2)
+    h, d = O.up_w8a8(hid, ids, w13, coarse=True)
+    hg = M.mfma_up(c.hidden, c.logits, c.w13, c.top_k, c.I).cpu().numpy().astype(np.float64)
+    r = np.abs(hg - h[sp]) / d[sp]
+    say(what, f"up: max |h_gpu - h| / coarse bound {r.max():.3f}")
+    assert np.isfinite(hg).all() and r.max() <= 1.0
+    h32 = h.astype(np.float32)
+    out = M.mfma_down(torch.from_numpy(h32[sp]).to(DEV), c.logits, c.w2, c.top_k, c.H)
+    o = out.cpu().numpy().astype(np.float64)
+    ref = O.down_w8a8(h32, ids, w, w2)
+    q, sh = O.quantize_rows(h32)
+    hd = O.e4m3_lut()[q] * sh.astype(np.float64)[:, None]
+    bound = np.zeros_like(ref)
+    nparts = -(-c.I // 512)
+    for e, pairs in OO._pairs_by_expert(ids).items():
+        W2 = O.dequant_expert(w2, e)
+        per = np.zeros((len(pairs), c.H))
+        for part in range(nparts):  # each K part is stored in fp16 with its own exponents
+            ks = slice(512 * part, min(512 * (part + 1), c.I))
+            yp = hd[pairs][:, ks] @ W2[:, ks].T
+            g32 = np.repeat(np.abs(yp).reshape(len(pairs), -1, 32).max(axis=2), 32, axis=1)
+            per += (O.acc_bound(W2[:, ks], hd[pairs][:, ks], coarse=True) + 2.0 ** -11 * 1.01 * g32
+                    + 2.0 ** -21 * np.abs(yp))
+        bound[pairs // c.top_k] += np.abs(w.ravel()[pairs])[:, None] * per
+    err = np.abs(o - ref)
+    say(what, f"down: max err/max|ref| {err.max() / np.abs(ref).max():.3e}, max err/bound {(err / bound).max():.3f}")
+    assert np.isfinite(o).all() and np.all(err <= bound)
+    assert len(_tiles_of(offsets)) >= c.E
+
+
+@pytest.mark.parametrize("E,H,I,k,T", [(16, 1024, 640, 4, 256), (16, 512, 1536, 4, 600), (32, 7168, 2048, 4, 1024)])
+def test_mfma_k_parts_staged(E, H, I, k, T):
+    """I beyond 512: the down GEMM runs in K parts of up to four 128-wide blocks (640 = 4 + 1,
+    1536 = 4 + 4 + 4, and the large-expert shape's 2048 = 4 x 4 with H=7168 and fp32
+    scales), each part into its own y plane, summed by the combine. Both halves checked at
+    every pair and every output."""
+    name = "large" if H == 7168 else "decode"
+    c = W.make_case(name, T=T, seed=E + I, device=DEV, E=E, H=H, I=I, top_k=k)
+    say("mfma k parts", E, H, I, k, T)
+    _staged_mfma_check(c, f"k parts H={H} I={I}")
+
+
+def test_mfma_large_expert_forward():
+    """The large-expert workload (E=256, H=7168, I=2048, top_k=8) at T=1024, where the gate
+    now picks MFMA; the oracle checks sampled tokens (their experts only)."""
+    shp = W.SHAPES["large"]
+    T = 1024
+    banks = W.make_banks("large", seed=4, device=DEV)
+    c = W.make_case("large", T=T, seed=5, device=DEV, banks=banks)
+    say("large mfma", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, return_routing=True)
+    torch.cuda.synchronize()
+    assert info["path"] == "mfma"
+    rows = np.array([0, 511, 1023])
+    ids, _, _ = O.route(c.logits.cpu().numpy()[rows], shp["top_k"])
+    res = oracle_out(c, rows=rows, act_mode=1, experts=O.routed_experts(ids))
+    assert np.array_equal(info["ids"].cpu().numpy()[rows], res["ids"])
+    check_out(out[torch.from_numpy(rows).to(DEV)], res, 1, "large T=1024 mfma")
+
+
 @pytest.mark.parametrize("T", [40, 100])
 def test_mfma_small_sizes_forced(decode_banks, T):
     """Forced MFMA with ragged tiles (few tokens per expert) against all rows; T=40 sorts
