@@ -65,9 +65,12 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
 
 
 def make_opts(force_path: Optional[int] = None, gate_ratio: Optional[float] = None,
-              mfma_min_tokens_per_expert: Optional[int] = None, act_mode: Optional[int] = None) -> L.Opts:
+              mfma_min_tokens_per_expert: Optional[int] = None, act_mode: Optional[int] = None,
+              use_measured_gate: Optional[bool] = None) -> L.Opts:
     o = L.Opts()
     L.check(lib().moe_fp8_block_default_opts(ctypes.byref(o)))
+    if use_measured_gate is not None:
+        o.use_measured_gate = int(bool(use_measured_gate))
     if act_mode is not None:
         o.act_mode = int(act_mode)
     if force_path is not None:
@@ -84,11 +87,11 @@ def _info_dict(info: L.RunInfo) -> dict:
                 kernels=info.kernels)
 
 
-def select_path(T: int, E: int, top_k: int, **opts) -> dict:
-    """The gate's decision for these sizes (host only)."""
+def select_path(T: int, E: int, H: int, I: int, top_k: int, **opts) -> dict:
+    """The path forward would take for these sizes (host only)."""
     info = L.RunInfo()
     o = make_opts(**opts)
-    L.check(lib().moe_fp8_block_select_path(T, E, top_k, ctypes.byref(o), ctypes.byref(info)))
+    L.check(lib().moe_fp8_block_select_path(T, E, H, I, top_k, ctypes.byref(o), ctypes.byref(info)))
     return _info_dict(info)
 
 

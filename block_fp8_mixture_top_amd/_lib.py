@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8_block.so")
 
 STATIC_WORKSPACE_BYTES = 64 << 20  # MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES
-ABI_VERSION = 3  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 4  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
 
 MOE_OK = 0
 STATUS_NAMES = {
@@ -65,6 +65,7 @@ class Opts(ctypes.Structure):
         ("force_path", ctypes.c_int32),
         ("mfma_min_tokens_per_expert", ctypes.c_int32),
         ("act_mode", ctypes.c_int32),
+        ("use_measured_gate", ctypes.c_int32),
     ]
 
 
@@ -91,7 +92,7 @@ _SIGS = {
     "moe_fp8_block_abi_version": (_I, []),
     "moe_fp8_block_last_error": (ctypes.c_char_p, []),
     "moe_fp8_block_default_opts": (_I, [ctypes.POINTER(Opts)]),
-    "moe_fp8_block_select_path": (_I, [_I, _I, _I, ctypes.POINTER(Opts), ctypes.POINTER(RunInfo)]),
+    "moe_fp8_block_select_path": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(Opts), ctypes.POINTER(RunInfo)]),
     "moe_fp8_block_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_fp8_block_route": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_fp8_block_workspace_size": (_SZ, [_I, _I, _I, _I, _I, ctypes.POINTER(Opts)]),

@@ -57,7 +57,23 @@ moe_opts defaults() {
   o.force_path = MOE_PATH_AUTO;
   o.mfma_min_tokens_per_expert = 2;
   o.act_mode = MOE_ACT_PATH;
+  o.use_measured_gate = 1;
   return o;
+}
+
+// One expert shape's measured gate: path[i] is the fastest path for T <= t_max[i] (the last
+// t_max is INT32_MAX). Generated from the committed sweeps by tune_gate.py.
+struct GateEntry {
+  int E, H, I, k, n;
+  int t_max[24];
+  int path[24];
+};
+#include "gate_table.inc"
+
+const GateEntry* gate_entry(int E, int H, int I, int k) {
+  for (const GateEntry& g : kGateTable)
+    if (g.E == E && g.H == H && g.I == I && g.k == k) return &g;
+  return nullptr;
 }
 
 int check_sizes(int T, int E, int top_k) {
@@ -78,14 +94,22 @@ int check_opts(const moe_opts* o) {
   if (o->mfma_min_tokens_per_expert < 1) return fail(MOE_ERR_ARG, "mfma_min_tokens_per_expert must be >= 1");
   if (o->act_mode != MOE_ACT_PATH && o->act_mode != MOE_ACT_GROUP_FP8)
     return fail(MOE_ERR_ARG, "act_mode %d is not MOE_ACT_PATH or MOE_ACT_GROUP_FP8", o->act_mode);
+  if (o->use_measured_gate != 0 && o->use_measured_gate != 1)
+    return fail(MOE_ERR_ARG, "use_measured_gate must be 0 or 1");
   return MOE_OK;
 }
 
-// The gate (gaudi-cookbook "fp8-moe-gather", The fix): gather while T*top_k <= ratio*E.
-// Group-wise e4m3 activations run on GATHER and STREAM only, so the gate never picks MFMA
-// for them.
-int gate(int T, int E, int top_k, const moe_opts& o) {
+// The gate (gaudi-cookbook "fp8-moe-gather", The fix): gather while T*top_k <= ratio*E, or,
+// for a shape with a measured table, the path measured fastest at this T. Group-wise e4m3
+// activations run on GATHER and STREAM only, so the gate never picks MFMA for them.
+int gate(int T, int E, int H, int I, int top_k, const moe_opts& o) {
   if (o.force_path != MOE_PATH_AUTO) return o.force_path;
+  if (o.use_measured_gate && o.act_mode == MOE_ACT_PATH) {
+    if (const GateEntry* g = gate_entry(E, H, I, top_k)) {
+      for (int i = 0; i < g->n; ++i)
+        if (T <= g->t_max[i]) return g->path[i];
+    }
+  }
   const double P = (double)T * top_k;
   if (P <= (double)o.gate_ratio * E) return MOE_PATH_GATHER;
   if (P >= (double)o.mfma_min_tokens_per_expert * E && o.act_mode != MOE_ACT_GROUP_FP8) return MOE_PATH_MFMA;
@@ -101,7 +125,7 @@ int act_of(int path, const moe_opts& o) {
 // Path actually run: the gate's choice, moved off a path the shapes do not fit only when
 // the caller left the choice to the gate.
 int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* path) {
-  int p = gate(T, E, top_k, o);
+  int p = gate(T, E, H, I, top_k, o);
   const bool forced = o.force_path != MOE_PATH_AUTO;
   if (o.act_mode == MOE_ACT_GROUP_FP8) {
     if (p == MOE_PATH_MFMA)
@@ -306,13 +330,15 @@ int moe_fp8_block_default_opts(moe_opts* opts) {
   return ok();
 }
 
-int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe_run_info* info) {
+int moe_fp8_block_select_path(int T, int E, int H, int I, int top_k, const moe_opts* opts, moe_run_info* info) {
   if (!info) return fail(MOE_ERR_ARG, "info is NULL");
   int st = check_sizes(T, E, top_k);
   if (st) return st;
+  if (H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "H and I must be positive (got H=%d, I=%d)", H, I);
   const moe_opts o = opts ? *opts : defaults();
   if ((st = check_opts(&o))) return st;
-  const int p = gate(T, E, top_k, o);
+  int p = 0;
+  if ((st = resolve_path(T, E, H, I, top_k, o, &p))) return st;
   info->path = p;
   info->act_mode = act_of(p, o);
   const int64_t P = (int64_t)T * top_k;

@@ -45,7 +45,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a struct, an enum or an entry point's meaning. */
-#define MOE_FP8_BLOCK_ABI_VERSION 3
+#define MOE_FP8_BLOCK_ABI_VERSION 4
 
 /* Limits checked on every call. */
 #define MOE_FP8_BLOCK_MAX_EXPERTS 1024
@@ -112,6 +112,9 @@ typedef struct {
   int32_t force_path;                /* moe_path; anything but AUTO is taken as asked or fails */
   int32_t mfma_min_tokens_per_expert;/* grouped work uses MFMA iff T*top_k >= this*E (default 2, measured) */
   int32_t act_mode;                  /* MOE_ACT_PATH (default) or MOE_ACT_GROUP_FP8 */
+  int32_t use_measured_gate;         /* 1 (default): for an (E, H, I, top_k) the library has a measured
+                                        table for, the path measured fastest at this T (see
+                                        moe_fp8_block_select_path); 0: the two thresholds above */
 } moe_opts;
 
 /* Filled by forward (host struct): what actually ran. */
@@ -137,14 +140,17 @@ int moe_fp8_block_default_opts(moe_opts* opts);
 /*
  * The gather/grouped gate, host only (gaudi-cookbook "fp8-moe-gather", The fix and the
  * VLLM_HPU_MOE_GATHER_RATIO row of its table): GATHER iff T*top_k <= gate_ratio*E,
- * else MFMA iff T*top_k >= mfma_min_tokens_per_expert*E, else STREAM. The defaults are the
- * crossovers measured on MI355X by block_fp8_mixture_top_amd/tune_gate.py (the page's
- * ratio 0.4 was chosen for another device). With act_mode MOE_ACT_GROUP_FP8 the gate
- * never picks MFMA (STREAM instead). A forced path is reported unchanged; forward runs
- * STREAM where the gate says MFMA for a shape the MFMA kernels do not take. Writes path,
- * act_mode and slots into *info; no HIP call.
+ * else MFMA iff T*top_k >= mfma_min_tokens_per_expert*E, else STREAM. The page's ratio
+ * 0.4 was chosen for another device; with use_measured_gate, a shape (E, H, I, top_k) the
+ * library carries a table for takes the path measured fastest on MI355X at the nearest
+ * swept T instead (the table is generated by block_fp8_mixture_top_amd/tune_gate.py from
+ * the committed sweeps under profiles/; FreeToken PR #662 likewise picks its backend from
+ * measured bandwidth). With act_mode MOE_ACT_GROUP_FP8 the gate never picks MFMA (STREAM
+ * instead) and uses the thresholds. A forced path is reported unchanged; a gate choice the
+ * shape does not support moves to STREAM, as forward does. Writes path, act_mode and slots
+ * into *info; no HIP call.
  */
-int moe_fp8_block_select_path(int T, int E, int top_k, const moe_opts* opts, moe_run_info* info);
+int moe_fp8_block_select_path(int T, int E, int H, int I, int top_k, const moe_opts* opts, moe_run_info* info);
 
 /* Bytes of workspace moe_fp8_block_route needs for these sizes (0 if sizes are invalid). */
 size_t moe_fp8_block_route_workspace_size(int T, int E, int top_k);

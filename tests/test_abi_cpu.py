@@ -43,18 +43,19 @@ def test_default_opts(lib):
     o = L.Opts()
     assert lib.moe_fp8_block_default_opts(ctypes.byref(o)) == 0
     assert o.gate_ratio == pytest.approx(2.0)
-    assert (o.force_path, o.mfma_min_tokens_per_expert, o.act_mode) == (0, 2, 0)
+    assert (o.force_path, o.mfma_min_tokens_per_expert, o.act_mode, o.use_measured_gate) == (0, 2, 0, 1)
     assert lib.moe_fp8_block_default_opts(None) == -1
     assert b"NULL" in lib.moe_fp8_block_last_error()
 
 
-def _path(lib, T, E, k, **kw):
+def _path(lib, T, E, k, H=2048, I=512, **kw):
     o = L.Opts()
     lib.moe_fp8_block_default_opts(ctypes.byref(o))
+    o.use_measured_gate = 0  # the two thresholds (the measured table is tested on its own)
     for a, v in kw.items():
         setattr(o, a, v)
     info = L.RunInfo()
-    st = lib.moe_fp8_block_select_path(T, E, k, ctypes.byref(o), ctypes.byref(info))
+    st = lib.moe_fp8_block_select_path(T, E, H, I, k, ctypes.byref(o), ctypes.byref(info))
     return st, info
 
 
@@ -249,3 +250,41 @@ def test_group_fp8_activations_gate_and_checks(lib):
     assert st == -2 and "128" in msg
     st, msg, _ = _forward(lib, opts=o, ws_bytes=16)
     assert st == -5
+
+
+def test_measured_gate_table_is_generated_from_the_profiles():
+    """csrc/gate_table.inc is exactly what tune_gate.py --emit makes from the committed sweeps
+    (nobody edited it by hand, and no sweep was left out)."""
+    from block_fp8_mixture_top_amd import tune_gate as TG
+
+    inc, _ = TG.emit_text()
+    with open(TG.TABLE) as f:
+        assert f.read() == inc
+
+
+def test_measured_gate_follows_its_table(lib):
+    """For every measured shape, select_path with use_measured_gate picks, at each swept T,
+    the path the table gives there, and at the geometric-mean boundaries the right side."""
+    import glob
+    import json
+
+    from block_fp8_mixture_top_amd import tune_gate as TG
+
+    for path in glob.glob(os.path.join(TG.PROFILES, "gate_sweep_E*_H*_I*_k*.json")):
+        with open(path) as f:
+            prof = json.load(f)
+        s = prof["shape"]
+        iv = TG.intervals(TG.best_paths(list(prof["rows"].values())))
+        for r in prof["rows"].values():
+            T = r["T"]
+            want = next(p for t, p in iv if T <= t)
+            st, info = _path(lib, T, s["E"], s["top_k"], H=s["H"], I=s["I"], use_measured_gate=1)
+            assert st == 0 and info.path == TG.PATH_IDS[want], (path, T, info.path, want)
+        for (t, p), (_, q) in zip(iv, iv[1:]):
+            assert _path(lib, t, s["E"], s["top_k"], H=s["H"], I=s["I"], use_measured_gate=1)[1].path == TG.PATH_IDS[p]
+            assert _path(lib, t + 1, s["E"], s["top_k"], H=s["H"], I=s["I"], use_measured_gate=1)[1].path == TG.PATH_IDS[q]
+
+
+def test_use_measured_gate_must_be_a_flag(lib):
+    st, _ = _path(lib, 4, 256, 8, use_measured_gate=2)
+    assert st == -1 and b"use_measured_gate" in lib.moe_fp8_block_last_error()
