@@ -134,7 +134,7 @@ int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* 
       return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 needs H %% 128 == 0 (got H=%d)", H);
   }
   if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
-    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H and I multiples of 128, H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
+    if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
     p = MOE_PATH_STREAM;
   }
   if (p == MOE_PATH_GATHER && !moe::gemm2_gather_supported(top_k, I)) {
@@ -181,10 +181,11 @@ Layout layout_for(int path, int act, int T, int E, int H, int I, int top_k) {
     // y in fp16, one exponent per (pair, kYGroup outputs), one plane per K part of GEMM2
     const size_t parts = (size_t)moe::mfma_k_parts(I);
     L.y = c.take(parts * P * (size_t)H * 2);
-    L.yexp = c.take(parts * P * (size_t)(H / moe::kYGroup));
-    L.xq = c.take((size_t)T * H);
+    L.yexp = c.take(parts * P * (size_t)moe::mfma_y_groups(H));
+    // x and h code rows padded to whole 128-wide blocks (zero past H, I)
+    L.xq = c.take((size_t)T * moe::mfma_pad(H));
     L.xs = c.take((size_t)T * 4);
-    L.hq = c.take(P * (size_t)I);
+    L.hq = c.take(P * (size_t)moe::mfma_pad(I));
     L.hs = c.take(P * 4);
   }
   if (act == MOE_ACT_GROUP_FP8) {
@@ -495,7 +496,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
       // one quantisation row per (token, 128 columns)
       g1.xq = at<uint8_t>(workspace, L.xq);
       g1.xs = at<float>(workspace, L.xs);
-      RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T * (H / 128), 128, at<uint8_t>(workspace, L.xq),
+      RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T * (H / 128), 128, 128, at<uint8_t>(workspace, L.xq),
                                                    at<float>(workspace, L.xs), s),
           "quant launch");
     }
@@ -525,7 +526,7 @@ int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const mo
   const int64_t P = (int64_t)T * top_k;
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
   float* xs = at<float>(workspace, L.xs);
-  RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, xq, xs, s), "quant launch");
+  RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, moe::mfma_pad(H), xq, xs, s), "quant launch");
   RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s), "gemm1 mfma launch");
   return MOE_OK;
 }
@@ -537,7 +538,7 @@ int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Pla
   const int64_t P = (int64_t)T * top_k;
   uint8_t* hq = at<uint8_t>(workspace, L.hq);
   float* hs = at<float>(workspace, L.hs);
-  RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, hq, hs, s), "h quant launch");
+  RUN(MOE_K_HQUANT, moe::launch_quant_rows_f32(hf, (int)P, I, moe::mfma_pad(I), hq, hs, s), "h quant launch");
   _Float16* y16 = at<_Float16>(workspace, L.y);
   int8_t* yexp = at<int8_t>(workspace, L.yexp);
   RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s), "gemm2 mfma launch");
@@ -555,7 +556,7 @@ int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, co
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (!moe::mfma_shape_ok(H, I))
-    return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H and I multiples of 128, H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
+    return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
   if ((st = check_bank(bank, bank_name, E, N, K))) return st;
   if (T == 0) return ok();
   if (!logits) return fail(MOE_ERR_ARG, "logits must be non-NULL");
@@ -666,7 +667,7 @@ int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* 
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(MOE_ERR_ARG, "x, codes and scales must be non-NULL");
   if (!aligned16(x) || !aligned16(codes)) return fail(MOE_ERR_ALIGN, "x and codes must be 16-byte aligned");
-  HIP_CHECK(moe::launch_quant_rows_bf16(x, rows, cols, codes, scales, (hipStream_t)stream), "quant launch");
+  HIP_CHECK(moe::launch_quant_rows_bf16(x, rows, cols, cols, codes, scales, (hipStream_t)stream), "quant launch");
   return ok();
 }
 

@@ -114,26 +114,34 @@ hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, v
                           hipStream_t s);
 
 // W8A8 path.
-hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+// Per-row e4m3 codes (row stride ostride bytes, columns cols .. ostride - 1 zero; ostride - cols
+// < 512) and scales amax/448 of rows of bf16 x.
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
                                   hipStream_t s);
 constexpr int kMfmaTileM = 128;  // sorted pairs per MFMA tile
 constexpr int kYGroup = 32;      // MFMA path: outputs of a pair's y that share one exponent
 size_t mfma_tiles_bound(int P, int E);
-// Shapes the MFMA kernels are built for: H a multiple of 128 up to 8192, I a multiple of 128
-// up to 4096.
+// Shapes the MFMA kernels are built for: H and I multiples of 16, H up to 8192, I up to 4096.
+// A last 128-wide block that is partial multiplies zero activation codes past the row end
+// (the code rows of x and h are padded to mfma_pad(H), mfma_pad(I) bytes).
 bool mfma_shape_ok(int H, int I);
+__host__ __device__ inline int mfma_pad(int n) { return (n + 127) / 128 * 128; }
+// exponent groups of a pair's y row
+__host__ __device__ inline int mfma_y_groups(int H) { return (H + kYGroup - 1) / kYGroup; }
 // GEMM2 on the matrix cores multiplies up to kMfmaPartBlocks 128-wide K blocks of h per launch;
 // I beyond that runs in mfma_k_parts(I) K parts, each writing its own y plane.
 constexpr int kMfmaPartBlocks = 4;
 int mfma_k_parts(int I);
-// hf[p, I] = silu(gate) * up in float for every sorted pair position p.
+// hf[p, I] = silu(gate) * up in float for every sorted pair position p, from the x codes
+// xq[T, mfma_pad(H)] and scales xs[T].
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
                              int P, int H, int I, int k, float* hf, hipStream_t s);
-// Per-row e4m3 codes and scales (amax/448) of hf, rows in sorted-position order.
-hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s);
-// y[pair, H] = s_h * W2 h for every pair from the h codes hq and row scales hs, stored as
-// fp16 of y * 2^-e with one exponent e per (pair, kYGroup outputs) in yexp[pair, H/kYGroup] (no
-// atomics; the combine applies the weights).
+// The same quantisation for rows of float (hf, rows in sorted-position order).
+hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
+                                 hipStream_t s);
+// y[pair, H] = s_h * W2 h for every pair from the h codes hq[P, mfma_pad(I)] and row scales
+// hs, stored as fp16 of y * 2^-e with one exponent e per (pair, kYGroup outputs) in
+// yexp[pair, mfma_y_groups(H)] (no atomics; the combine applies the weights).
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
 // out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/kYGroup] + bias[ids[t*k + j], n]),

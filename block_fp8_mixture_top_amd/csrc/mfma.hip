@@ -47,13 +47,21 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
 // enough to be float subnormals round to the e4m3 zero either way.
 __device__ __forceinline__ float quot(float x, double rs) { return (float)((double)x * rs); }
 
+// Zero codes for columns cols .. ostride - 1 of a code row (ostride - cols < 512, both
+// multiples of 8): the padding that makes a partial last 128-wide K block multiply zeros.
+__device__ __forceinline__ void zero_tail(uint8_t* row, int cols, int ostride, int lane) {
+  const int c = cols + lane * 8;
+  if (c < ostride) *(uint2*)(row + c) = make_uint2(0u, 0u);
+}
+
 // One wave per row of bf16: amax, scale = amax/448 (1 if zero), codes = e4m3(x/scale).
 // Lane l holds the 8-value pieces l, l + 64, ... of the row: IT of them, all read up front
 // (pieces past the row end read its last piece and are ignored), so the row is read from
-// memory once and every read is in flight together.
+// memory once and every read is in flight together. Code rows are ostride bytes apart, the
+// columns past cols zero.
 template <int IT>
 __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int rows, int cols,
-                                                              uint8_t* __restrict__ codes,
+                                                              int ostride, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
   const int row = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
   if (row >= rows) return;
@@ -91,8 +99,9 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
       const uint32_t b = enc2(quot(bf16_lo(w[2 * q + 1]), rs), quot(bf16_hi(w[2 * q + 1]), rs));
       out[q] = a | (b << 16);
     }
-    *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(out[0], out[1]);
+    *(uint2*)(codes + (size_t)row * ostride + c) = make_uint2(out[0], out[1]);
   }
+  zero_tail(codes + (size_t)row * ostride, cols, ostride, lane);
   if (lane == 0) scales[row] = s;
 }
 
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
 // 4-float reads per piece.
 template <int IT>
 __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __restrict__ x, int rows, int cols,
-                                                             uint8_t* __restrict__ codes,
+                                                             int ostride, uint8_t* __restrict__ codes,
                                                              float* __restrict__ scales) {
   const int row = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
   if (row >= rows) return;
@@ -132,8 +141,9 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
     const f32x4 a = va[it], b = vb[it];
     const uint32_t lo = enc2(quot(a[0], rs), quot(a[1], rs)) | (enc2(quot(a[2], rs), quot(a[3], rs)) << 16);
     const uint32_t hi = enc2(quot(b[0], rs), quot(b[1], rs)) | (enc2(quot(b[2], rs), quot(b[3], rs)) << 16);
-    *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(lo, hi);
+    *(uint2*)(codes + (size_t)row * ostride + c) = make_uint2(lo, hi);
   }
+  zero_tail(codes + (size_t)row * ostride, cols, ostride, lane);
   if (lane == 0) scales[row] = s;
 }
 
@@ -167,7 +177,8 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __rest
   const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (idx >= (size_t)T * H) return;
   const size_t t = idx / H, n = idx % H;
-  const size_t yplane = (size_t)T * k * H, eplane = (size_t)T * k * (H / kYGroup);
+  const int EG = mfma_y_groups(H);
+  const size_t yplane = (size_t)T * k * H, eplane = (size_t)T * k * EG;
   float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
   for (int j = 0; j < k; ++j) {
@@ -175,13 +186,13 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const _Float16* __rest
     const float wj = w[p];
     float yv[8];
     {
-      const float up = __uint_as_float((uint32_t)(127 + yexp[p * (H / kYGroup) + n / kYGroup]) << 23);  // 2^e
+      const float up = __uint_as_float((uint32_t)(127 + yexp[p * EG + n / kYGroup]) << 23);  // 2^e
       const h8 v = *(const h8*)(y + p * H + n);
 #pragma unroll
       for (int q = 0; q < 8; ++q) yv[q] = (float)v[q] * up;
     }
     for (int part = 1; part < parts; ++part) {
-      const float up = __uint_as_float((uint32_t)(127 + yexp[part * eplane + p * (H / kYGroup) + n / kYGroup]) << 23);
+      const float up = __uint_as_float((uint32_t)(127 + yexp[part * eplane + p * EG + n / kYGroup]) << 23);
       const h8 v = *(const h8*)(y + part * yplane + p * H + n);
 #pragma unroll
       for (int q = 0; q < 8; ++q) yv[q] = __builtin_fmaf((float)v[q], up, yv[q]);
@@ -342,12 +353,14 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
   constexpr int SB = 4 * QB + XB;         // one stage
   constexpr int LPW = 4 + 2;              // direct loads per wave per stage
   __shared__ __align__(16) uint8_t ring[kStages * SB];
-  __shared__ float s_sc[2 * (kMaxH / 128)];
-  __shared__ float s_rt[2 * (kMaxH / 128)];
-  __shared__ float s_last[2];
+  // block scales, their ratios and last values of three row blocks: the gate rows' block and
+  // the (up to) two blocks the up rows fall in (one unless I % 128 != 0)
+  __shared__ float s_sc[3 * (kMaxH / 128)];
+  __shared__ float s_rt[3 * (kMaxH / 128)];
+  __shared__ float s_last[3];
   __shared__ int s_tok[TM];
 
-  const int nfb = I / 128;
+  const int nfb = mfma_pad(I) / 128;
   const int nitems = plan.tile_off[E] * nfb;
   const int L = xcd_item(blockIdx.x, nitems);  // consecutive L share an expert's rows and a tile's x
   if (L >= nitems) return;
@@ -363,43 +376,58 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
   const int r16 = lane & 15, kq = lane >> 4;
   const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
-  const int nkb = H / 128;
+  const int Hp = mfma_pad(H);  // x code rows, zero past H
+  const int nkb = Hp / 128;
+  // scale row blocks: the gate rows' (fb) and the up rows' first and last (rows past 2I in
+  // the last feature block are clamped, so the block index is too)
+  const int bu0 = (I + fb * 128) / 128;
+  const int bumax = (2 * I - 1) / 128;
 
   // token of each tile row (rows past the expert's pairs repeat the first token; their
   // results are never stored) and the gate / up block scales of this feature block
   if (tid < TM) s_tok[tid] = plan.sorted[pos0 + (tid < nvalid ? tid : 0)] / k;
-  if (tid < 2 * nkb) {
-    const int up = tid >= nkb;
-    const int kb = tid - up * nkb;
-    s_sc[tid] = load_scale(w13.scales, w13.scale_bf16, (int64_t)e * w13.sexp + (int64_t)(fb + up * nfb) * w13.srow + kb);
+  if (tid < 3 * nkb) {
+    const int sq = tid / nkb, kb = tid - sq * nkb;
+    const int rb = sq == 0 ? fb : min(bu0 + sq - 1, bumax);
+    s_sc[tid] = load_scale(w13.scales, w13.scale_bf16, (int64_t)e * w13.sexp + (int64_t)rb * w13.srow + kb);
   }
   __syncthreads();
-  if (tid < 2 * nkb) {
-    const int up = tid >= nkb;
-    scale_ratio(s_sc + up * nkb, nkb, tid - up * nkb, s_rt + up * nkb, s_last + up);
+  if (tid < 3 * nkb) {
+    const int sq = tid / nkb;
+    scale_ratio(s_sc + sq * nkb, nkb, tid - sq * nkb, s_rt + sq * nkb, s_last + sq);
   }
   __syncthreads();
 
   // direct-load sources. Quarter fq's 64 weight rows (0..31 gate, 32..63 up) are copied 8 rows
   // at a time: this wave takes copies 4th .. 4th+3. x copies: this wave takes tile rows
   // 16w .. 16w+15. K block kb adds kb*128 bytes.
-  uint32_t woff[4];
+  // rows past I (gate) or 2I (up) in the last feature block read the last valid row; their
+  // results are never stored
+  uint32_t wrow[4], wch[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = (th * 4 + j) * 8 + lr;
-    const int row = (b < 32 ? 0 : I - 32) + fb * 128 + fq * 32 + b;
-    woff[j] = (uint32_t)row * (uint32_t)H + (uint32_t)((lc ^ sw(b)) << 4);
+    const int row = b < 32 ? min(fb * 128 + fq * 32 + b, I - 1) : min(I + fb * 128 + fq * 32 + b - 32, 2 * I - 1);
+    wrow[j] = (uint32_t)row * (uint32_t)H;
+    wch[j] = (uint32_t)((lc ^ sw(b)) << 4);
   }
+  // a partial last K block: chunks past the row end read the row's last chunk (finite codes,
+  // multiplied by the zero x codes there)
+  const uint32_t ktail = (uint32_t)(H - (nkb - 1) * 128);  // bytes of the last K block
   const uint8_t* xsrc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = wave * 16 + j * 8 + lr;
-    xsrc[j] = xq + (size_t)s_tok[r] * H + ((lc ^ sw(r)) << 4);
+    xsrc[j] = xq + (size_t)s_tok[r] * Hp + ((lc ^ sw(r)) << 4);
   }
   auto copy = [&](int kb, int j) {  // this wave's copy j (0..5) of stage kb
     uint8_t* slot = ring + (kb % kStages) * SB;
-    if (j < 4) g2lds(wb + kb * 128 + woff[j], slot + fq * QB + (th * 4 + j) * 1024);
-    else g2lds(xsrc[j - 4] + kb * 128, slot + 4 * QB + (wave * 16 + (j - 4) * 8) * kRowB);
+    if (j < 4) {
+      const uint32_t ch = kb == nkb - 1 && wch[j] >= ktail ? ktail - 16 : wch[j];
+      g2lds(wb + kb * 128 + wrow[j] + ch, slot + fq * QB + (th * 4 + j) * 1024);
+    } else {
+      g2lds(xsrc[j - 4] + kb * 128, slot + 4 * QB + (wave * 16 + (j - 4) * 8) * kRowB);
+    }
   };
   float xsc[NTT];  // x scale of token 64th + tt*16 + r16
 #pragma unroll
@@ -419,9 +447,14 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
   // copies of stage kb + 1 are in, the barrier makes everyone's visible and shows every wave
   // has read stage kb into registers (its LDS reads waited for), so stage kb's slot is
   // refilled with stage kb + 3. Copies, reads and MFMAs go in two interleaved groups.
+  // the scale sequence of each up tile (the gate tiles use sequence 0): rows I + fb*128 +
+  // 32fq + 16(f-2) .. +15 lie in one 128-row block (I is a multiple of 16)
+  int squ[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) squ[f] = 1 + min((I + fb * 128 + fq * 32 + f * 16) / 128, bumax) - bu0;
   auto step = [&](int kb, const Ops& cur, Ops& nxt) {
     // the scale ratios first, so that the explicit LDS wait below covers them too
-    const float rg = s_rt[kb], ru = s_rt[nkb + kb];
+    const float rs[4] = {s_rt[kb], s_rt[kb], s_rt[squ[0] * nkb + kb], s_rt[squ[1] * nkb + kb]};
     if (kb + 1 < nkb) {
       if (kb + 2 < nkb) wait_vm<LPW>();
       else wait_vm<0>();
@@ -444,10 +477,10 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
         nxt.wa[t] = lds_operand(rslot + fq * QB, t * 16 + r16, kq);
       }
       // gate tiles in group 0, up tiles in group 1
-      const float r = g == 0 ? rg : ru;  // uniform
-      if (r != 0.0f) {                   // a zero block scale adds nothing
 #pragma unroll
-        for (int f = 2 * g; f < 2 * g + 2; ++f) {
+      for (int f = 2 * g; f < 2 * g + 2; ++f) {
+        const float r = rs[f];  // uniform
+        if (r != 0.0f) {        // a zero block scale adds nothing
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -487,13 +520,14 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     if (kb + 1 < nkb) step(kb + 1, o1, o0);
   }
   // the MLP bias of this lane's gate and up features (w13's bias: gate half, then up half);
-  // without a bias the reads go to an in-bounds address and are dropped
+  // without a bias the reads go to an in-bounds address and are dropped, as are those of
+  // features past I (read at the last valid ones)
   const bool hb = w13.bias != nullptr;
   const float* bb = hb ? w13.bias + (size_t)e * 2 * I : (const float*)w13.codes;
   f32x4 bgv[2], buv[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
-    const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;
+    const int i = min(fb * 128 + fq * 32 + f * 16 + kq * 4, I - 4);
     bgv[f] = *(const f32x4*)(bb + (hb ? i : 0));
     buv[f] = *(const f32x4*)(bb + (hb ? I + i : 0));
   }
@@ -504,8 +538,10 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     if (pos >= pos_end) continue;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
+      const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;  // features i .. i+3, all < I or none
+      if (i >= I) continue;
       f32x4 h;
-      const float gs = s_last[0] * xsc[tt], us = s_last[1] * xsc[tt];
+      const float gs = s_last[0] * xsc[tt], us = s_last[squ[f]] * xsc[tt];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float g = acc[f][tt][q] * gs;
@@ -516,7 +552,7 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
         }
         h[q] = silu_fast(g) * u;
       }
-      *(f32x4*)(hf + (size_t)pos * I + fb * 128 + fq * 32 + f * 16 + kq * 4) = h;
+      *(f32x4*)(hf + (size_t)pos * I + i) = h;
     }
   }
 }
@@ -592,7 +628,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w2.codes + (size_t)e * w2.expert_stride;
 
-  stage_scales(s_sc, w2, (int64_t)e * w2.sexp + kb0, H / 128, KB);
+  const int Ip = mfma_pad(I);  // h code rows, zero past I
+  stage_scales(s_sc, w2, (int64_t)e * w2.sexp + kb0, (H + 127) / 128, KB);
   if (tid < TP) {
     const bool ok = tid < nvalid;
     s_hs[tid] = hs[pos0 + (ok ? tid : 0)];
@@ -607,7 +644,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     const int q = wave + NW * i;
     const int kb = q / RG, r = (q % RG) * 8 + lr;
     const int rr = r < nvalid ? r : 0;
-    g2lds(hq + (size_t)(pos0 + rr) * I + (kb0 + kb) * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q % RG) * 1024);
+    g2lds(hq + (size_t)(pos0 + rr) * Ip + (kb0 + kb) * 128 + ((lc ^ sw(r)) << 4), ring + kb * HB + (q % RG) * 1024);
   }
   wait_vm<0>();  // everyone's h codes, scales and pair rows are in after the barrier
   __syncthreads();
@@ -622,25 +659,39 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's h reads are done
   __syncthreads();                     // and everyone's, before the ring is refilled
 
-  // chunks holding outputs of this wave: those with c * NCH + FW * wave < H (H is a
-  // multiple of 128, so a wave's FW outputs are all in range or all out)
+  // chunks holding outputs of this wave: those with c * NCH + FW * wave < H (the last one
+  // may hold fewer than FW: H is a multiple of 16, so each feature tile is in range or out)
   const int nch = (H - wave * FW + NCH - 1) / NCH;
   const int nst = nch * KB;
-  // w2 copy i covers rows 8i .. 8i+7 of the wave's FW; chunk c adds c * NCH rows
+  // w2 copy i covers rows 8i .. 8i+7 of the wave's FW; chunk c adds c * NCH rows. Rows past H
+  // read the last row and chunks past a partial last K block the row's last chunk (finite
+  // codes, multiplied by the zero h codes there); neither result is stored.
   constexpr int NCP = FW / 8;  // copies per wave and stage
-  uint32_t woff[NCP];
+  uint32_t wch[NCP], woff[NCP];
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
-    const int b = i * 8 + lr;
-    woff[i] = (uint32_t)(wave * FW + b) * (uint32_t)I + (uint32_t)((lc ^ sw(b)) << 4);
+    wch[i] = (uint32_t)((lc ^ sw(i * 8 + lr)) << 4);
+    woff[i] = (uint32_t)(wave * FW + i * 8 + lr) * (uint32_t)I + wch[i];
   }
+  const int nkb_all = Ip / 128;
+  const uint32_t ktail = (uint32_t)(I - (nkb_all - 1) * 128);  // bytes of the last K block
   uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
     const int c = st / KB, kb = st - c * KB;
-    const uint8_t* src = wb + (size_t)c * NCH * I + (kb0 + kb) * 128;
     uint8_t* slot = myring + (st % kRing2) * WB;
+    const bool ptail = kb0 + kb == nkb_all - 1 && ktail < 128;  // uniform
+    if (!ptail && c * NCH + wave * FW + FW <= H) {
+      const uint8_t* src = wb + (size_t)c * NCH * I + (kb0 + kb) * 128;
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) g2lds(src + woff[i], slot + i * 1024);
+      for (int i = 0; i < NCP; ++i) g2lds(src + woff[i], slot + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        const int row = min(c * NCH + wave * FW + i * 8 + lr, H - 1);
+        const uint32_t ch = ptail && wch[i] >= ktail ? ktail - 16 : wch[i];
+        g2lds(wb + (size_t)row * I + (kb0 + kb) * 128 + ch, slot + i * 1024);
+      }
+    }
   };
 #pragma unroll
   for (int st = 0; st < kRing2 - 1; ++st)
@@ -688,9 +739,11 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
       }
       if (kb == KB - 1) {
         // y of pair 16pt + r16, outputs n0 + 16ft + 4kq .. +3, in fp16 with one exponent per
-        // kYGroup outputs of the pair (GT feature tiles, held by lanes r16 + 16 kq)
+        // kYGroup outputs of the pair (GT feature tiles, held by lanes r16 + 16 kq); feature
+        // tiles past H are left out of the exponent and not stored
         constexpr int GT = kYGroup / 16;
         static_assert(NF % GT == 0, "a wave's outputs are whole exponent groups");
+        const int EG = mfma_y_groups(H);
 #pragma unroll
         for (int pt = 0; pt < NP; ++pt) {
           if (pt < npt) {
@@ -702,24 +755,27 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
               float v[GT][4];
               uint32_t m = 0u;  // bits of the largest |v| (non-negative floats order as integers)
 #pragma unroll
-              for (int f = 0; f < GT; ++f)
+              for (int f = 0; f < GT; ++f) {
+                const bool in = n0 + (g * GT + f) * 16 < H;  // uniform
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   v[f][q] = acc[g * GT + f][pt][q] * hsc;
-                  m = max(m, __float_as_uint(__builtin_fabsf(v[f][q])));
+                  if (in) m = max(m, __float_as_uint(__builtin_fabsf(v[f][q])));
                 }
+              }
               m = max(m, (uint32_t)__shfl_xor((int)m, 16, kWave));
               m = max(m, (uint32_t)__shfl_xor((int)m, 32, kWave));
               const int ey = y_exponent(m);
               const float down = __uint_as_float((uint32_t)(127 - ey) << 23);  // 2^-ey, exact
-              if (prow >= 0) {
+              if (prow >= 0 && n0 + g * kYGroup < H) {
 #pragma unroll
                 for (int f = 0; f < GT; ++f) {
+                  if (n0 + (g * GT + f) * 16 >= H) continue;
                   const h4 o = {(_Float16)(v[f][0] * down), (_Float16)(v[f][1] * down),
                                 (_Float16)(v[f][2] * down), (_Float16)(v[f][3] * down)};
                   *(h4*)(y + (size_t)prow * H + n0 + (g * GT + f) * 16 + kq * 4) = o;
                 }
-                if (kq == 0) yexp[(size_t)prow * (H / kYGroup) + n0 / kYGroup + g] = (int8_t)ey;
+                if (kq == 0) yexp[(size_t)prow * EG + n0 / kYGroup + g] = (int8_t)ey;
               }
             }
           }
@@ -747,22 +803,23 @@ size_t mfma_tiles_bound(int P, int E) {
 }
 
 bool mfma_shape_ok(int H, int I) {
-  return H % 128 == 0 && H > 0 && H <= kMaxH && I % 128 == 0 && I >= 128 && I <= kMaxIParts;
+  return H % 16 == 0 && H > 0 && H <= kMaxH && I % 16 == 0 && I > 0 && I <= kMaxIParts;
 }
 
-int mfma_k_parts(int I) { return (I / 128 + kMfmaPartBlocks - 1) / kMfmaPartBlocks; }
+int mfma_k_parts(int I) { return (mfma_pad(I) / 128 + kMfmaPartBlocks - 1) / kMfmaPartBlocks; }
 
 // Pieces of 8 values per lane, 512 columns per wave and piece; rows of up to 8192 columns.
 #define MOE_QUANT_LAUNCH(KERNEL, T)                                                                          \
-  static hipError_t launch_##KERNEL(const T* x, int rows, int cols, uint8_t* codes, float* scales,          \
-                                    hipStream_t s) {                                                         \
+  static hipError_t launch_##KERNEL(const T* x, int rows, int cols, int ostride, uint8_t* codes,            \
+                                    float* scales, hipStream_t s) {                                          \
     const dim3 grid((rows + 3) / 4), block(256);                                                             \
     const int it = (cols + kWave * 8 - 1) / (kWave * 8);                                                     \
-    if (it <= 1) launch_kernel(KERNEL<1>, grid, block, 0, s, x, rows, cols, codes, scales);                   \
-    else if (it <= 2) launch_kernel(KERNEL<2>, grid, block, 0, s, x, rows, cols, codes, scales);              \
-    else if (it <= 4) launch_kernel(KERNEL<4>, grid, block, 0, s, x, rows, cols, codes, scales);              \
-    else if (it <= 8) launch_kernel(KERNEL<8>, grid, block, 0, s, x, rows, cols, codes, scales);              \
-    else if (it <= 16) launch_kernel(KERNEL<16>, grid, block, 0, s, x, rows, cols, codes, scales);            \
+    if (ostride < cols || ostride - cols >= kWave * 8 || ostride % 8 != 0) return hipErrorInvalidValue;      \
+    if (it <= 1) launch_kernel(KERNEL<1>, grid, block, 0, s, x, rows, cols, ostride, codes, scales);          \
+    else if (it <= 2) launch_kernel(KERNEL<2>, grid, block, 0, s, x, rows, cols, ostride, codes, scales);     \
+    else if (it <= 4) launch_kernel(KERNEL<4>, grid, block, 0, s, x, rows, cols, ostride, codes, scales);     \
+    else if (it <= 8) launch_kernel(KERNEL<8>, grid, block, 0, s, x, rows, cols, ostride, codes, scales);     \
+    else if (it <= 16) launch_kernel(KERNEL<16>, grid, block, 0, s, x, rows, cols, ostride, codes, scales);   \
     else return hipErrorInvalidValue;                                                                        \
     return hipGetLastError();                                                                                \
   }
@@ -770,13 +827,14 @@ MOE_QUANT_LAUNCH(quant_rows_bf16_kernel, uint16_t)
 MOE_QUANT_LAUNCH(quant_rows_f32_kernel, float)
 #undef MOE_QUANT_LAUNCH
 
-hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
                                   hipStream_t s) {
-  return launch_quant_rows_bf16_kernel(x, rows, cols, codes, scales, s);
+  return launch_quant_rows_bf16_kernel(x, rows, cols, ostride, codes, scales, s);
 }
 
-hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, uint8_t* codes, float* scales, hipStream_t s) {
-  return launch_quant_rows_f32_kernel(x, rows, cols, codes, scales, s);
+hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
+                                 hipStream_t s) {
+  return launch_quant_rows_f32_kernel(x, rows, cols, ostride, codes, scales, s);
 }
 
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
@@ -795,7 +853,7 @@ hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E, int P,
                              int H, int I, int k, float* hf, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
-  const int nblocks = (int)mfma_tiles_bound(P, E) * (I / 128);
+  const int nblocks = (int)mfma_tiles_bound(P, E) * (mfma_pad(I) / 128);
   launch_kernel(gemm1_mfma_kernel, dim3(nblocks), dim3(512), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks, hf);
   return hipGetLastError();
 }
@@ -805,12 +863,12 @@ hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& 
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
   // K parts of up to four 128-wide blocks, each into its own y plane
-  const int nkb = I / 128;
+  const int nkb = mfma_pad(I) / 128;
   for (int part = 0; part < mfma_k_parts(I); ++part) {
     const int kb0 = part * kMfmaPartBlocks;
     const int kbn = nkb - kb0 < kMfmaPartBlocks ? nkb - kb0 : kMfmaPartBlocks;
     _Float16* yp = y + (size_t)part * P * H;
-    int8_t* ep = yexp + (size_t)part * P * (H / kYGroup);
+    int8_t* ep = yexp + (size_t)part * P * mfma_y_groups(H);
     hipError_t err;
     switch (kbn) {
       case 1: err = g2m<1, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;

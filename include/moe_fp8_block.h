@@ -189,7 +189,8 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  *   opts    host, NULL = defaults; info host, NULL = not reported.
  * H and I must be multiples of 16 (MOE_ERR_UNSUPPORTED otherwise); a last 128-wide scale
  * block may be partial. Scale blocks tile the stored rows, so w13's up row I+i takes block
- * (I+i)/128. The MFMA path needs multiples of 128 and is not chosen otherwise. Every pointer the
+ * (I+i)/128. On MFMA a partial last 128-wide K block multiplies zero activation codes past the
+ * row end (the x and h code rows are padded in the workspace). Every pointer the
  * chosen path reads must be non-NULL. T = 0 is a no-op (info still filled).
  * The W8A16 paths (GATHER, STREAM) decode weights exactly and accumulate in float. MFMA
  * quantises x per token and h per (token, slot) row to e4m3 with scale amax/448 (float
@@ -255,8 +256,8 @@ int moe_fp8_block_forward_timed(const uint16_t* hidden, const float* logits, con
  * Test exports: the two halves of the MFMA path (route + sort first in each), so that each
  * half can be checked against a reference on its own inputs. Both take the workspace of a
  * forward forced onto MFMA (moe_fp8_block_workspace_size with force_path MOE_PATH_MFMA)
- * and need H a multiple of 128 up to 8192 and I a multiple of 128 up to 4096
- * (MOE_ERR_UNSUPPORTED otherwise).
+ * and need H and I multiples of 16, H up to 8192 and I up to 4096 (MOE_ERR_UNSUPPORTED
+ * otherwise).
  *   mfma_up:   x quantised per token (as quantize_rows), GEMM1 on the fp8 matrix cores and
  *              h = silu(gate) * up written in float to h [T*top_k, I], row p holding the
  *              pair at sorted position p (the sorted_pairs order of moe_fp8_block_route).

@@ -165,14 +165,24 @@ def test_forward_rejects_misalignment(lib):
 
 
 def test_partial_scale_blocks_are_accepted(lib):
-    """H and I need only be multiples of 16 (a last 128-wide scale block may be partial); the
-    call then gets as far as the workspace check."""
+    """H and I need only be multiples of 16 (a last 128-wide scale block may be partial) on
+    every path, MFMA included; the call then gets as far as the workspace check. The MFMA
+    workspace holds the x and h code rows padded to whole 128-wide blocks."""
     st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), ws_bytes=16)
     assert st == -5 and "workspace" in msg
     o = L.Opts()
     lib.moe_fp8_block_default_opts(ctypes.byref(o))
-    o.force_path = 3  # MFMA needs whole 128-wide blocks
-    st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), opts=o)
+    o.force_path = 3
+    st, msg, info = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), opts=o, ws_bytes=16)
+    assert st == -5 and "workspace" in msg and info.path == 3
+    ragged = lib.moe_fp8_block_workspace_size(64, 256, 2064, 528, 8, ctypes.byref(o))
+    whole = lib.moe_fp8_block_workspace_size(64, 256, 2048, 512, 8, ctypes.byref(o))
+    assert ragged > whole > 0
+    # the gate keeps MFMA for ragged grouped work
+    st, info = _path(lib, 4096, 256, 8, H=2064, I=528)
+    assert st == 0 and info.path == 3
+    # sizes past the kernels' limits are refused on a forced MFMA
+    st, msg, _ = _forward(lib, H=8208, I=80, w13=_bank(160, 8208), w2=_bank(8208, 80), opts=o)
     assert st == -2 and "MFMA" in msg
 
 

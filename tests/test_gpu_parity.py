@@ -294,18 +294,20 @@ def test_odd_shapes_forced(path, H, I):
     check_out(out, oracle_out(c, act_mode=act), act, f"{path} H={H} I={I}")
 
 
-@pytest.mark.parametrize("path", [None, "gather", "stream"])
-@pytest.mark.parametrize("H,I,T", [(144, 80, 1), (144, 80, 3), (2064, 528, 1), (2064, 528, 40)])
+@pytest.mark.parametrize("path", [None, "gather", "stream", "mfma"])
+@pytest.mark.parametrize("H,I,T", [(144, 80, 1), (144, 80, 3), (2064, 528, 1), (2064, 528, 40), (2064, 528, 300)])
 def test_partial_scale_blocks(path, H, I, T):
     """H and I that are multiples of 16 but not of 128: every row ends in a partial scale
-    block, and w13's up rows start inside a block (blocks tile the stored rows). The gate
-    never picks MFMA for them."""
+    block, and w13's up rows start inside a block (blocks tile the stored rows). On MFMA the
+    partial last K blocks multiply zero activation codes, rows past I or H are never stored,
+    and the up tiles of a feature block take the scales of the block each lies in."""
     c = W.make_case("decode", T=T, seed=31, device=DEV, E=16, H=H, I=I, top_k=4)
     say("partial blocks", path, H, I, T)
     kw = {} if path is None else {"force_path": PATHS[path]}
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32, **kw)
-    assert info["path"] == (path or info["path"]) and info["path"] != "mfma"
-    check_out(out, oracle_out(c), 0, f"{info['path']} H={H} I={I} T={T}")
+    assert info["path"] == (path or info["path"])
+    act = 1 if info["path"] == "mfma" else 0
+    check_out(out, oracle_out(c, act_mode=act), act, f"{info['path']} H={H} I={I} T={T}")
 
 
 @pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
@@ -557,7 +559,10 @@ def _staged_mfma_check(c, what):
         for part in range(nparts):  # each K part is stored in fp16 with its own exponents
             ks = slice(512 * part, min(512 * (part + 1), c.I))
             yp = hd[pairs][:, ks] @ W2[:, ks].T
-            g32 = np.repeat(np.abs(yp).reshape(len(pairs), -1, 32).max(axis=2), 32, axis=1)
+            eg = -(-c.H // 32)  # exponent groups; a last one may be partial
+            ap = np.zeros((len(pairs), eg * 32))
+            ap[:, :c.H] = np.abs(yp)
+            g32 = np.repeat(ap.reshape(len(pairs), eg, 32).max(axis=2), 32, axis=1)[:, :c.H]
             per += (O.acc_bound(W2[:, ks], hd[pairs][:, ks], coarse=True) + 2.0 ** -11 * 1.01 * g32
                     + 2.0 ** -21 * np.abs(yp))
         bound[pairs // c.top_k] += np.abs(w.ravel()[pairs])[:, None] * per
@@ -567,12 +572,15 @@ def _staged_mfma_check(c, what):
     assert len(_tiles_of(offsets)) >= c.E
 
 
-@pytest.mark.parametrize("E,H,I,k,T", [(16, 1024, 640, 4, 256), (16, 512, 1536, 4, 600), (32, 7168, 2048, 4, 1024)])
+@pytest.mark.parametrize("E,H,I,k,T", [(16, 1024, 640, 4, 256), (16, 512, 1536, 4, 600), (32, 7168, 2048, 4, 1024),
+                                       (16, 2064, 528, 4, 300), (8, 144, 80, 2, 60), (16, 1040, 2064, 4, 200)])
 def test_mfma_k_parts_staged(E, H, I, k, T):
     """I beyond 512: the down GEMM runs in K parts of up to four 128-wide blocks (640 = 4 + 1,
     1536 = 4 + 4 + 4, and the large-expert shape's 2048 = 4 x 4 with H=7168 and fp32
-    scales), each part into its own y plane, summed by the combine. Both halves checked at
-    every pair and every output."""
+    scales), each part into its own y plane, summed by the combine; and ragged H and I
+    (2064/528, 144/80, 1040/2064: partial last K blocks of both GEMMs, up rows straddling
+    scale blocks, a partial last exponent group). Both halves checked at every pair and every
+    output."""
     name = "large" if H == 7168 else "decode"
     c = W.make_case(name, T=T, seed=E + I, device=DEV, E=E, H=H, I=I, top_k=k)
     say("mfma k parts", E, H, I, k, T)
