@@ -34,14 +34,18 @@ Pins (tests/test_oracle_*.py, run without a GPU):
                     and with MLP biases); dense == gathered; unrouted experts contribute
                     exactly zero; E=1,k=1 is a textbook SwiGLU FFN (torch), with and
                     without biases; expert permutation and token independence invariants;
-                    act_mode 2 against scalar loops over group-dequantised activations.
+                    act_mode 2 against scalar loops over group-dequantised activations;
+                    act_modes 1 and 3 against torch's e4m3 cast with fp32 scales, every
+                    x and h code and scale compared.
   e4m3_midpoint_distance
                     a linear walk over every finite value at every value, midpoint and
                     its float32 neighbours, and at random magnitudes.
   h_drift / flags   GEMM1 evaluated on the CPU with float32 sums in several orders and
                     with a truncating aligned accumulator: every h stays within the bound
-                    and every code that changes is flagged; on the GPU, the MFMA path's h
-                    lies within the bound at every element. The constants are a reading
+                    and every code that changes is flagged, for h scaled per row and per
+                    128-feature group; on the GPU, the MFMA path's h lies within the bound
+                    at every element. The allowance equals the output moved by rounding
+                    each flagged element the other way. The constants are a reading
                     (the pages fix no accumulation precision), documented at ACC_MMA.
 """
 
@@ -359,34 +363,49 @@ def _expert_up(W13, X, b13=None):
     return g, u, silu(g) * u
 
 
-def _requantize_h(W13, X, g, u, h):
-    """act_mode 1: h re-quantised per (token, slot) row to e4m3 (scale amax/448, in float32
-    emulation) before the down GEMM, and the elements whose rounding an implementation may
-    decide either way flagged: |v - midpoint| <= drift(h_i)/s + |v| * drift(h_r)/amax,
-    with r the row's argmax (the second term is the scale moving with amax)."""
+def _h_group(act_mode: int, I: int) -> int:
+    """Columns of h that share one re-quantisation scale: the whole row (I) for act_mode 1,
+    128 for act_mode 3 (one scale per (pair, 128-feature group), the granularity of the
+    weight blocks along the down GEMM's K)."""
+    return BLOCK if act_mode == 3 else I
+
+
+def _requantize_h(W13, X, g, u, h, group=None):
+    """act_modes 1 and 3: h re-quantised to e4m3 before the down GEMM, one scale per group
+    of `group` consecutive columns of a (token, slot) row (the whole row by default; scale
+    group amax/448 in float32 emulation, quantize_groups), and the elements whose rounding
+    an implementation may decide either way flagged: |v - midpoint| <= drift(h_i)/s +
+    |v| * drift(h_r)/amax, with r the argmax of the element's group and s, amax that
+    group's scale and maximum (the second term is the scale moving with amax)."""
     h32 = h.astype(np.float32)
-    q, s = quantize_rows(h32)
-    h_deq = _LUT[q] * s.astype(np.float64)[:, None]
+    n, I = h32.shape
+    group = I if group is None else group
+    q, s = quantize_groups(h32, group)
+    s_el = np.repeat(s.astype(np.float64), group, axis=1)  # each element's scale
+    h_deq = _LUT[q] * s_el
     d = h_drift(W13, X, g, u, h)
-    amax = np.max(np.abs(h32), axis=1).astype(np.float64)
-    r = np.argmax(np.abs(h32), axis=1)
-    v = (h32 / s[:, None]).astype(np.float32).astype(np.float64)
+    a = np.abs(h32).reshape(n, I // group, group)
+    amax = a.max(axis=2).astype(np.float64)  # [n, groups]
+    r = a.argmax(axis=2)
+    dr = np.take_along_axis(d.reshape(n, I // group, group), r[:, :, None], axis=2)[:, :, 0]
+    v = (h32 / s_el.astype(np.float32)).astype(np.float32).astype(np.float64)
     dist, step = e4m3_midpoint_distance(v)
-    dr = d[np.arange(len(r)), r]
     with np.errstate(divide="ignore", invalid="ignore"):
-        scale_term = np.where(amax[:, None] > 0, np.abs(v) * (dr / amax)[:, None], 0.0)
-    flags = dist <= d / s.astype(np.float64)[:, None] + scale_term
-    return h_deq, dict(h_codes=q, h_scale=s, flags=flags, step=step, drift=d)
+        rel = np.where(amax > 0, dr / amax, 0.0)
+    flags = dist <= d / s_el + np.abs(v) * np.repeat(rel, group, axis=1)
+    return h_deq, dict(h_codes=q, h_scale=s if group != I else s[:, 0], flags=flags, step=step, drift=d,
+                       h_scale_el=s_el)
 
 
 def _expert_mlp(W13, W2, X, act_mode: int, b13=None, b2=None):
     """The tokens X [n, H] routed to one expert: a = W13 x + b13, h = silu(a[:I]) * a[I:],
-    y = W2 h + b2, for each row. act_mode 1 re-quantises h first (_requantize_h). Returns
-    Y [n, H] and, for act_mode 1, the per-row h codes, scales, flags and steps."""
+    y = W2 h + b2, for each row. act_modes 1 and 3 re-quantise h first (_requantize_h, per
+    row or per 128-feature group). Returns Y [n, H] and, for those modes, the h codes,
+    scales, flags and steps."""
     g, u, h = _expert_up(W13, X, b13)
     extra = None
-    if act_mode == 1:
-        h, extra = _requantize_h(W13, np.atleast_2d(X), g, u, h)
+    if act_mode in (1, 3):
+        h, extra = _requantize_h(W13, np.atleast_2d(X), g, u, h, _h_group(act_mode, h.shape[1]))
     Y = h @ W2.T
     if b2 is not None:
         Y = Y + b2[None, :]
@@ -395,14 +414,14 @@ def _expert_mlp(W13, W2, X, act_mode: int, b13=None, b2=None):
 
 def _x_used(x, act_mode: int, res: dict):
     """The activations the up/gate GEMM multiplies: x itself (act_mode 0), x quantised per
-    token (1) or per (token, 128-column group) (2), dequantised in float64."""
+    token (1) or per (token, 128-column group) (2 and 3), dequantised in float64."""
     if act_mode == 0:
         return x
     if act_mode == 1:
         xq, xs = quantize_rows(x.astype(np.float32))
         res.update(x_codes=xq, x_scales=xs)
         return _LUT[xq] * xs.astype(np.float64)[:, None]
-    if act_mode == 2:
+    if act_mode in (2, 3):
         xq, xs = quantize_groups(x.astype(np.float32))
         res.update(x_codes=xq, x_scales=xs)
         return dequant_groups(xq, xs)
@@ -424,12 +443,15 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     and h per pair, both in fp32 emulation ([gather] The fix: the routed experts are
     gathered, up/gate run as one GEMM and the down projection follows); act_mode 2 is
     the gather variant of [gather] The fix: the up/gate GEMM on e4m3 activations quantised
-    per (token, 128-column group) and the down projection on h in full precision.
+    per (token, 128-column group) and the down projection on h in full precision;
+    act_mode 3 is W8A8 with both GEMMs on groups: x per (token, 128-column group) as in
+    act_mode 2 and h per (pair, 128-feature group).
     Only the routed experts are read; each is evaluated once on all the tokens routed to
     it (one matrix product per expert), and its contribution w_tj * y is added to each of
     those tokens. Returns a dict with out (float64 [T, H]), routing, the x quantisation for
-    act_modes 1 and 2, and for act_mode 1 the h quantisation (per pair p = t*k + j) and the
-    per-output allowance for ambiguous h roundings.
+    act_modes 1 to 3, and for act_modes 1 and 3 the h quantisation (per pair p = t*k + j:
+    codes and the row's scale, or its [I/128] group scales) and the per-output allowance
+    for ambiguous h roundings.
     """
     x = bf16_to_f64(hidden_bf16)
     T, H = x.shape
@@ -438,7 +460,7 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
     counts, offsets, sorted_pairs = sort_pairs(ids, E)
     res = dict(ids=ids, w=w, w32=w32, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs)
     x_used = _x_used(x, act_mode, res)
-    h_mode = 1 if act_mode == 1 else 0  # only act_mode 1 re-quantises h
+    h_mode = act_mode if act_mode in (1, 3) else 0  # act_modes 1 and 3 re-quantise h
     get = _expert_cache(w13, w2)
     out = np.zeros((T, H), dtype=np.float64)
     allowance = np.zeros((T, H), dtype=np.float64)
@@ -455,24 +477,26 @@ def forward(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int 
             if extra is not None:
                 f = extra["flags"]
                 n_flag += int(f.sum())
-                amt = np.where(f, extra["step"] * extra["h_scale"].astype(np.float64)[:, None], 0.0)
+                amt = np.where(f, extra["step"] * extra["h_scale_el"], 0.0)
                 allowance[toks[sl]] += np.abs(wf[pairs[sl], None]) * (amt @ np.abs(W2).T)
                 for r, p in enumerate(pairs[sl]):
                     h_codes[int(p)] = extra["h_codes"][r]
                     h_scales[int(p)] = extra["h_scale"][r]
     res["out"] = out
-    if act_mode == 1:
+    if act_mode in (1, 3):
         res.update(allowance=allowance, n_flagged=n_flag, n_h=T * top_k * (w13["N"] // 2),
                    h_codes=h_codes, h_scales=h_scales)
     return res
 
 
-def up_w8a8(hidden_bf16, ids, w13: dict, pairs=None, coarse: bool = False):
-    """The first half of act_mode 1 on its own: h = silu(gate) * up for every pair
+def up_w8a8(hidden_bf16, ids, w13: dict, pairs=None, coarse: bool = False, act_mode: int = 1):
+    """The first half of act_mode 1 (or 3) on its own: h = silu(gate) * up for every pair
     p = t*k + j (or the listed pairs), float64 [len(pairs), I] in the order given, from x
-    quantised per token. Also returns the drift bound of each h (h_drift, coarse or not)."""
+    quantised per token (per (token, 128-column group)). Also returns the drift bound of
+    each h (h_drift, coarse or not)."""
+    assert act_mode in (1, 3)
     x = bf16_to_f64(hidden_bf16)
-    xu = _x_used(x, 1, {})
+    xu = _x_used(x, act_mode, {})
     ids = np.asarray(ids)
     k = ids.shape[1]
     pairs = np.arange(ids.size) if pairs is None else np.asarray(pairs)
@@ -508,6 +532,23 @@ def down_w8a8(h32_pairs, ids, w, w2: dict):
     return out
 
 
+def down_w8a8_groups(h_codes, h_scales, ids, w, w2: dict):
+    """The second half of act_mode 3 on given h codes: each pair's e4m3 codes [T*k, I] with
+    one scale per (pair, 128-feature group) [T*k, I/128] (pair p = t*k + j) are dequantised,
+    multiplied by the expert's w2 and added to out[t] with the router weight w[t, j].
+    Returns out float64 [T, H]."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    hd = dequant_groups(h_codes, h_scales)
+    out = np.zeros((T, w2["N"]))
+    wf = np.asarray(w, dtype=np.float64).ravel()
+    for e, pairs in _pairs_by_expert(ids).items():
+        W2 = dequant_expert(w2, e)
+        b2 = expert_bias(w2, e)
+        out[pairs // k] += wf[pairs, None] * (hd[pairs] @ W2.T + b2[None, :])
+    return out
+
+
 def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode: int = 0):
     """Dense all-experts formulation: out[t] = sum_e C[t, e] * expert_e(x_t).
 
@@ -528,7 +569,7 @@ def forward_dense(hidden_bf16, logits, w13: dict, w2: dict, top_k: int, act_mode
     for e in range(E):
         W13, W2 = dequant_expert(w13, e), dequant_expert(w2, e)
         b13, b2 = expert_bias(w13, e), expert_bias(w2, e)
-        Y, _ = _expert_mlp(W13, W2, x_used, 1 if act_mode == 1 else 0, b13, b2)
+        Y, _ = _expert_mlp(W13, W2, x_used, act_mode if act_mode in (1, 3) else 0, b13, b2)
         out += C[:, e:e + 1] * Y
     return out
 

@@ -178,7 +178,7 @@ def test_forward_matches_scalar_loops_partial_blocks(scale_dtype):
     assert np.max(np.abs(res["out"] - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("act_mode", [0, 1])
+@pytest.mark.parametrize("act_mode", [0, 1, 2, 3])
 def test_dense_equals_gathered(act_mode):
     c = W.make_case("tiny", T=5, seed=7)
     n = case_numpy(c)
@@ -299,13 +299,61 @@ def test_w8a8_matches_torch_quantised_reference():
     assert np.max(np.abs(res["out"] - out.numpy())) <= 1e-12 * float(out.abs().max())
 
 
+def test_group_w8a8_matches_torch_quantised_reference():
+    """act_mode 3 against torch: x per (token, 128-column group) and h per (pair,
+    128-feature group), scales amax/448 by fp32 division, codes by torch's e4m3 cast; I=256
+    gives each h row two groups."""
+    c = W.make_case("decode", T=3, seed=3, E=4, H=256, I=256, top_k=2)
+    n = case_numpy(c)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=3)
+
+    def deq(bank, e):
+        codes = bank.codes.view(bank.E, -1)[e, : bank.N * bank.K].view(bank.N, bank.K)
+        vals = codes.view(torch.float8_e4m3fn).to(torch.float64)
+        s = bank.scales.view(bank.E, -1)[e].view(-1, bank.scale_row_stride)[:, : bank.scale_cols]
+        s = s.to(torch.float64).repeat_interleave(128, 0)[: bank.N].repeat_interleave(128, 1)[:, : bank.K]
+        return vals * s
+
+    def qg(x32):  # [C] float32 -> codes [C], scales [C/128]
+        g = x32.view(-1, 128)
+        s = g.abs().amax(dim=-1, keepdim=True) / torch.tensor(448.0)
+        s = torch.where(s == 0, torch.ones_like(s), s)
+        return (g / s).to(torch.float8_e4m3fn).view(-1), s.view(-1)
+
+    def dq(codes, s):
+        return (codes.to(torch.float64).view(-1, 128) * s.to(torch.float64)[:, None]).view(-1)
+
+    out = torch.zeros((c.T, c.H), dtype=torch.float64)
+    ids = torch.from_numpy(res["ids"].astype(np.int64))
+    w = torch.from_numpy(res["w"])
+    I = c.I
+    for t in range(c.T):
+        xq, xs = qg(c.hidden[t].to(torch.float32))
+        assert np.array_equal(xq.view(torch.uint8).numpy(), res["x_codes"][t])
+        assert np.array_equal(xs.numpy(), res["x_scales"][t])
+        for j in range(c.top_k):
+            e = int(ids[t, j])
+            W13, W2 = deq(c.w13, e), deq(c.w2, e)
+            a = W13 @ dq(xq, xs)
+            h = torch.nn.functional.silu(a[:I]) * a[I:]
+            hq, hs = qg(h.to(torch.float32))
+            p = t * c.top_k + j
+            assert np.array_equal(hq.view(torch.uint8).numpy(), res["h_codes"][p])
+            assert np.array_equal(hs.numpy(), res["h_scales"][p])
+            out[t] += w[t, j] * (W2 @ dq(hq, hs))
+    assert np.max(np.abs(res["out"] - out.numpy())) <= 1e-12 * float(out.abs().max())
+    # the two h groups of a row do take different scales
+    assert any(len(set(np.atleast_1d(v).tolist())) > 1 for v in res["h_scales"].values())
+
+
 def _gemm1_h_variants(codes_w, S, xq, xs, lut):
     """GEMM1 + silu*up of one expert evaluated three ways the exact arithmetic does not fix:
     float32 sums of the exact code products per 128-wide K block taken sequentially or
     pairwise, and a truncating aligned accumulator (each block's products cut toward zero to
     a multiple of 2^(e-17), e the binade of the block's largest |product|, summed exactly,
     rounded to float32). Block sums are scaled and added in float32, as are the SiLU and
-    product. Returns {name: h float32 [n, I]}."""
+    product. xs holds one scale per token [n] (applied to the sum) or per (token, K block)
+    [n, nkb] (applied to each block sum). Returns {name: h float32 [n, I]}."""
     f32 = np.float32
     n, H = xq.shape
     I = codes_w.shape[0] // 2
@@ -329,21 +377,27 @@ def _gemm1_h_variants(codes_w, S, xq, xs, lut):
     out = {}
     for name, P in sums.items():
         terms = (P * sc[None]).astype(f32)
+        if xs.ndim == 2:
+            terms = (terms * xs.astype(f32)[:, None, :]).astype(f32)
         a = np.zeros((n, 2 * I), f32)
         for kb in range(nkb):
             a = (a + terms[:, :, kb]).astype(f32)
-        a = (a * xs.astype(f32)[:, None]).astype(f32)
+        if xs.ndim == 1:
+            a = (a * xs.astype(f32)[:, None]).astype(f32)
         g, u = a[:, :I], a[:, I:]
         out[name] = ((g / (f32(1) + np.exp(-g).astype(f32))).astype(f32) * u).astype(f32)
     return out
 
 
-def test_h_drift_covers_other_evaluations():
+@pytest.mark.parametrize("act_mode", [1, 3])
+def test_h_drift_covers_other_evaluations(act_mode):
     """Pin of the W8A8 drift bound: at the prefill shape (decode banks, uniform logits, 64
-    tokens, 512 pairs), GEMM1 evaluated with float32 block sums in two orders and with a
+    tokens and 512 pairs, or 32 and 256), GEMM1 evaluated with float32 block sums in two orders and with a
     truncating aligned accumulator stays within h_drift of the exact h at every element,
-    and every h code that such an evaluation changes is one the oracle flags."""
-    T, k = 64, 8
+    and every h code that such an evaluation changes is one the oracle flags; with x and h
+    quantised per row (act_mode 1) or per 128-column group (act_mode 3)."""
+    T, k = (64, 8) if act_mode == 1 else (32, 8)
+    group = 128 if act_mode == 3 else None
     lg = W.make_logits(T, 256, "uniform", seed=41)
     ids, _, _ = O.route(lg.numpy(), k)
     used = O.routed_experts(ids)
@@ -351,9 +405,13 @@ def test_h_drift_covers_other_evaluations():
     n13 = w13.numpy()
     hid = bf16_bits(W.make_hidden(T, 2048, seed=42))
     x = O.bf16_to_f64(hid)
-    xq, xs = O.quantize_rows(x.astype(np.float32))
     lut = O.e4m3_lut()
-    xu = lut[xq] * xs.astype(np.float64)[:, None]
+    if act_mode == 3:
+        xq, xs = O.quantize_groups(x.astype(np.float32))
+        xu = O.dequant_groups(xq, xs)
+    else:
+        xq, xs = O.quantize_rows(x.astype(np.float32))
+        xu = lut[xq] * xs.astype(np.float64)[:, None]
     st = n13["expert_stride_bytes"]
     worst, changed, flagged, total = 0.0, 0, 0, 0
     for e in used:
@@ -361,7 +419,7 @@ def test_h_drift_covers_other_evaluations():
         toks = np.nonzero((ids == e).any(axis=1))[0]
         W13 = O.dequant_expert(n13, e)
         g, u, h = OO._expert_up(W13, xu[toks])
-        _, extra = OO._requantize_h(W13, xu[toks], g, u, h)
+        _, extra = OO._requantize_h(W13, xu[toks], g, u, h, group)
         d = extra["drift"]
         assert np.all(O.h_drift(W13, xu[toks], g, u, h, coarse=True) >= d)
         codes = n13["codes"][e * st:e * st + 1024 * 2048].reshape(1024, 2048)
@@ -369,7 +427,7 @@ def test_h_drift_covers_other_evaluations():
             r = np.abs(hv.astype(np.float64) - h) / d
             worst = max(worst, float(r.max()))
             assert r.max() <= 1.0, (name, e, float(r.max()))
-            qv, _ = O.quantize_rows(hv)
+            qv, _ = O.quantize_groups(hv, group or hv.shape[1])
             diff = qv != extra["h_codes"]
             changed += int(diff.sum())
             assert not (diff & ~extra["flags"]).any(), (name, e)
@@ -379,13 +437,16 @@ def test_h_drift_covers_other_evaluations():
     assert changed > 0  # the evaluations do round some codes the other way
 
 
-def test_allowance_is_the_effect_of_the_flagged_roundings():
+@pytest.mark.parametrize("act_mode", [1, 3])
+def test_allowance_is_the_effect_of_the_flagged_roundings(act_mode):
     """The allowance of every output is the sum, over the flagged h elements, of what
     rounding that element to its other neighbour moves the output by, found here by
-    recomputing the output with that one code changed."""
-    c = W.make_case("decode", T=2, seed=44, E=4, H=256, I=128, top_k=2)
+    recomputing the output with that one code changed (h scaled per row, or per
+    128-feature group with two groups per row)."""
+    c = W.make_case("decode", T=2, seed=44, E=4, H=256, I=128 if act_mode == 1 else 256, top_k=2)
     n = case_numpy(c)
-    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=1)
+    res = O.forward(n["hidden"], n["logits"], n["w13"], n["w2"], c.top_k, act_mode=act_mode)
+    group = 128 if act_mode == 3 else None
     lut = O.e4m3_lut()
     pos = lut[:0x7F]
     moved = np.zeros_like(res["out"])
@@ -395,16 +456,23 @@ def test_allowance_is_the_effect_of_the_flagged_roundings():
             p = t * c.top_k + j
             e = int(res["ids"][t, j])
             W2 = O.dequant_expert(n["w2"], e)
-            q, s = res["h_codes"][p], float(res["h_scales"][p])
+            q = res["h_codes"][p]
+            sg = np.atleast_1d(res["h_scales"][p]).astype(np.float32)
+            s_el = np.repeat(sg, c.I // len(sg))  # each element's scale
             x = O.bf16_to_f64(n["hidden"][t:t + 1]).astype(np.float32)
-            xq, xs = O.quantize_rows(x)
+            if act_mode == 3:
+                xq, xs = O.quantize_groups(x)
+                X = O.dequant_groups(xq, xs)
+            else:
+                xq, xs = O.quantize_rows(x)
+                X = lut[xq] * xs.astype(np.float64)[:, None]
             W13 = O.dequant_expert(n["w13"], e)
-            X = lut[xq] * xs.astype(np.float64)[:, None]
             g, u, h = OO._expert_up(W13, X)
-            _, extra = OO._requantize_h(W13, X, g, u, h)
-            v = (h[0].astype(np.float32) / np.float32(s)).astype(np.float64)
+            _, extra = OO._requantize_h(W13, X, g, u, h, group)
+            v = (h[0].astype(np.float32) / s_el).astype(np.float64)
             for i in np.nonzero(extra["flags"][0])[0]:
                 nflag += 1
+                s = float(s_el[i])
                 a = abs(v[i])
                 lo = pos[pos <= a].max() if a < 448 else 448.0
                 hi = pos[pos > a].min() if a < 448 else 448.0

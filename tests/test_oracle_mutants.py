@@ -30,6 +30,7 @@ PINS = [
     lambda: PF.test_single_expert_is_swiglu(0.5),
     PF.test_w8a8_matches_torch_quantised_reference,
     PF.test_group_quantisation_matches_scalar_search,
+    PF.test_group_w8a8_matches_torch_quantised_reference,
 ]
 
 
@@ -134,6 +135,16 @@ def _groups_of_64(x32, group=128):
     return q.reshape(R, C), np.repeat(s.reshape(R, C // 64)[:, ::2], 1, axis=1)
 
 
+def _h_group_whole_row(act_mode, I):
+    """act_mode 3 re-quantising h with one scale per row instead of per 128-feature group."""
+    return I
+
+
+def _h_group_of_64(act_mode, I):
+    """h groups half as wide as the weight blocks along the down GEMM's K."""
+    return 64 if act_mode == 3 else I
+
+
 MUTANTS = {
     "gate_up_swapped": ("_expert_mlp", _mlp_swapped),
     "silu_dropped": ("_expert_mlp", _mlp_no_silu),
@@ -147,6 +158,8 @@ MUTANTS = {
     "bias_dropped": ("expert_bias", _bias_dropped),
     "group_scales_tiled": ("dequant_groups", _groups_tiled),
     "groups_of_64": ("quantize_groups", _groups_of_64),
+    "h_group_whole_row": ("_h_group", _h_group_whole_row),
+    "h_group_of_64": ("_h_group", _h_group_of_64),
 }
 
 
