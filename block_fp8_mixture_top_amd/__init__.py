@@ -16,6 +16,7 @@ import torch
 from . import _lib as L
 from ._lib import (  # noqa: F401
     ACT_GROUP_FP8,
+    ACT_GROUP_FP8_W8A8,
     ACT_PATH,
     ACT_ROW_FP8,
     MOE_BF16,
@@ -30,8 +31,9 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "abi_version", "lib", "make_opts", "bank_struct", "check_bank_extents", "select_path", "route_workspace_size", "route", "workspace_size",
-    "forward", "forward_static", "mfma_up", "mfma_down", "quantize_rows", "decode_e4m3", "decode_e4m3_paths", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
+    "forward", "forward_static", "mfma_up", "mfma_down", "mfma_up_groups", "mfma_down_groups", "quantize_rows", "quantize_groups", "decode_e4m3", "decode_e4m3_paths", "encode_e4m3", "MoeError", "PATH_AUTO", "PATH_GATHER",
     "PATH_STREAM", "PATH_MFMA", "PATH_NAMES", "ACT_PATH", "ACT_ROW_FP8", "ACT_GROUP_FP8",
+    "ACT_GROUP_FP8_W8A8",
 ]
 
 
@@ -300,6 +302,47 @@ def mfma_down(h: torch.Tensor, logits: torch.Tensor, w2, top_k: int, H: int, out
     return out
 
 
+def mfma_up_groups(hidden: torch.Tensor, logits: torch.Tensor, w13, top_k: int, I: int):
+    """Test export: the first half of the group-scaled MFMA path. Returns (h codes [T*top_k,
+    I] uint8, h scales [T*top_k, I/128] float32), row p for the pair at sorted position p."""
+    _need(hidden, "hidden", torch.bfloat16)
+    dev = hidden.device
+    _need(logits, "logits", torch.float32, dev)
+    T, H = hidden.shape
+    E = logits.shape[1]
+    b13 = bank_struct(w13, E, 2 * I, H, dev)
+    ws = torch.empty(max(workspace_size(T, E, H, I, top_k, force_path=PATH_MFMA, act_mode=ACT_GROUP_FP8), 1),
+                     dtype=torch.uint8, device=dev)
+    codes = torch.empty((T * top_k, I), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T * top_k, max(I // 128, 1)), dtype=torch.float32, device=dev)
+    L.check(lib().moe_fp8_block_mfma_up_groups(_ptr(hidden), _ptr(logits), ctypes.byref(b13), T, E, H, I, top_k,
+                                               _ptr(codes), _ptr(scales), _ptr(ws), ws.numel(), _stream(hidden)))
+    return codes, scales
+
+
+def mfma_down_groups(codes: torch.Tensor, scales: torch.Tensor, logits: torch.Tensor, w2, top_k: int, H: int,
+                     out_dtype=torch.float32) -> torch.Tensor:
+    """Test export: the second half of the group-scaled MFMA path on h codes [T*top_k, I]
+    uint8 and scales [T*top_k, I/128] float32 in sorted-position order. Returns out [T, H]."""
+    _need(codes, "codes", torch.uint8)
+    dev = codes.device
+    _need(scales, "scales", torch.float32, dev)
+    _need(logits, "logits", torch.float32, dev)
+    T, E = logits.shape
+    I = codes.shape[1]
+    if codes.shape[0] != T * top_k or tuple(scales.shape) != (T * top_k, I // 128) or I % 128 != 0:
+        raise ValueError("codes must be [T*top_k, I] with I % 128 == 0 and scales [T*top_k, I/128]")
+    b2 = bank_struct(w2, E, H, I, dev)
+    ws = torch.empty(max(workspace_size(T, E, H, I, top_k, force_path=PATH_MFMA, act_mode=ACT_GROUP_FP8), 1),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    L.check(lib().moe_fp8_block_mfma_down_groups(_ptr(codes), _ptr(scales), _ptr(logits), ctypes.byref(b2), T, E, H,
+                                                 I, top_k, _ptr(out),
+                                                 L.MOE_BF16 if out_dtype == torch.bfloat16 else L.MOE_F32, _ptr(ws),
+                                                 ws.numel(), _stream(codes)))
+    return out
+
+
 def quantize_rows(x: torch.Tensor):
     """Per-row dynamic e4m3 of a bf16 [rows, cols] tensor -> (codes uint8, scales float32)."""
     _need(x, "x", torch.bfloat16)
@@ -307,6 +350,17 @@ def quantize_rows(x: torch.Tensor):
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     scales = torch.empty(rows, dtype=torch.float32, device=x.device)
     L.check(lib().moe_fp8_block_quantize_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def quantize_groups(x: torch.Tensor):
+    """Dynamic e4m3 per (row, 128-column group) of a bf16 [rows, cols] tensor -> (codes
+    uint8 [rows, cols], scales float32 [rows, cols/128])."""
+    _need(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(cols // 128, 1)), dtype=torch.float32, device=x.device)
+    L.check(lib().moe_fp8_block_quantize_groups(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
 
 

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_fp8_block.so")
 
 STATIC_WORKSPACE_BYTES = 64 << 20  # MOE_FP8_BLOCK_STATIC_WORKSPACE_BYTES
-ABI_VERSION = 4  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 5  # MOE_FP8_BLOCK_ABI_VERSION of the header this binding mirrors
 
 MOE_OK = 0
 STATUS_NAMES = {
@@ -24,7 +24,7 @@ STATUS_NAMES = {
 MOE_F32, MOE_BF16 = 0, 1
 PATH_AUTO, PATH_GATHER, PATH_STREAM, PATH_MFMA = 0, 1, 2, 3
 PATH_NAMES = {PATH_AUTO: "auto", PATH_GATHER: "gather", PATH_STREAM: "stream", PATH_MFMA: "mfma"}
-ACT_PATH, ACT_ROW_FP8, ACT_GROUP_FP8 = 0, 1, 2
+ACT_PATH, ACT_ROW_FP8, ACT_GROUP_FP8, ACT_GROUP_FP8_W8A8 = 0, 1, 2, 3
 KERNEL_NAMES = {1: "route", 2: "sort", 3: "quant", 4: "hquant", 5: "gemm1", 6: "gemm2", 7: "combine"}
 EXPORTS = [
     "moe_fp8_block_abi_version",
@@ -39,7 +39,10 @@ EXPORTS = [
     "moe_fp8_block_forward_static",
     "moe_fp8_block_mfma_up",
     "moe_fp8_block_mfma_down",
+    "moe_fp8_block_mfma_up_groups",
+    "moe_fp8_block_mfma_down_groups",
     "moe_fp8_block_quantize_rows",
+    "moe_fp8_block_quantize_groups",
     "moe_fp8_block_decode_e4m3",
     "moe_fp8_block_decode_e4m3_paths",
     "moe_fp8_block_encode_e4m3",
@@ -114,7 +117,11 @@ _SIGS = {
     ),
     "moe_fp8_block_mfma_up": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "moe_fp8_block_mfma_down": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P]),
+    "moe_fp8_block_mfma_up_groups": (_I, [_P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "moe_fp8_block_mfma_down_groups": (
+        _I, [_P, _P, _P, ctypes.POINTER(Bank), _I, _I, _I, _I, _I, _P, _I, _P, _SZ, _P]),
     "moe_fp8_block_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P]),
+    "moe_fp8_block_quantize_groups": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_fp8_block_decode_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),
     "moe_fp8_block_decode_e4m3_paths": (_I, [_P, _P, ctypes.c_int64, _P]),
     "moe_fp8_block_encode_e4m3": (_I, [_P, _P, ctypes.c_int64, _P]),

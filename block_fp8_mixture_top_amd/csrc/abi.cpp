@@ -100,8 +100,8 @@ int check_opts(const moe_opts* o) {
 }
 
 // The gate (gaudi-cookbook "fp8-moe-gather", The fix): gather while T*top_k <= ratio*E, or,
-// for a shape with a measured table, the path measured fastest at this T. Group-wise e4m3
-// activations run on GATHER and STREAM only, so the gate never picks MFMA for them.
+// for a shape with a measured table, the path measured fastest at this T (the tables were
+// measured with the paths' own activations; group-wise e4m3 takes the thresholds).
 int gate(int T, int E, int H, int I, int top_k, const moe_opts& o) {
   if (o.force_path != MOE_PATH_AUTO) return o.force_path;
   if (o.use_measured_gate && o.act_mode == MOE_ACT_PATH) {
@@ -112,13 +112,13 @@ int gate(int T, int E, int H, int I, int top_k, const moe_opts& o) {
   }
   const double P = (double)T * top_k;
   if (P <= (double)o.gate_ratio * E) return MOE_PATH_GATHER;
-  if (P >= (double)o.mfma_min_tokens_per_expert * E && o.act_mode != MOE_ACT_GROUP_FP8) return MOE_PATH_MFMA;
+  if (P >= (double)o.mfma_min_tokens_per_expert * E) return MOE_PATH_MFMA;
   return MOE_PATH_STREAM;
 }
 
 // Activation precision a path runs with (moe_run_info.act_mode).
 int act_of(int path, const moe_opts& o) {
-  if (path == MOE_PATH_MFMA) return MOE_ACT_ROW_FP8;
+  if (path == MOE_PATH_MFMA) return o.act_mode == MOE_ACT_GROUP_FP8 ? MOE_ACT_GROUP_FP8_W8A8 : MOE_ACT_ROW_FP8;
   return o.act_mode == MOE_ACT_GROUP_FP8 ? MOE_ACT_GROUP_FP8 : MOE_ACT_PATH;
 }
 
@@ -128,10 +128,13 @@ int resolve_path(int T, int E, int H, int I, int top_k, const moe_opts& o, int* 
   int p = gate(T, E, H, I, top_k, o);
   const bool forced = o.force_path != MOE_PATH_AUTO;
   if (o.act_mode == MOE_ACT_GROUP_FP8) {
-    if (p == MOE_PATH_MFMA)
-      return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 runs on GATHER and STREAM only, not on a forced MFMA");
     if (H % 128 != 0)
       return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 needs H %% 128 == 0 (got H=%d)", H);
+    if (p == MOE_PATH_MFMA && I % 128 != 0) {
+      if (forced)
+        return fail(MOE_ERR_UNSUPPORTED, "MOE_ACT_GROUP_FP8 on MFMA needs I %% 128 == 0 (got I=%d)", I);
+      p = MOE_PATH_STREAM;
+    }
   }
   if (p == MOE_PATH_MFMA && !moe::mfma_shape_ok(H, I)) {
     if (forced) return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
@@ -175,18 +178,28 @@ Layout layout_for(int path, int act, int T, int E, int H, int I, int top_k) {
   L.n_act = c.take(4);
   L.tile_off = c.take((size_t)(E + 1) * 4);
   L.scratch = c.take(moe::sort_scratch_bytes((int)P, E));
-  L.h = c.take(P * (size_t)I * 4);  // h in float, [pair or sorted position, I]
+  // h in float, [pair or sorted position, I] (the group-scaled MFMA path writes codes only)
+  if (act != MOE_ACT_GROUP_FP8_W8A8) L.h = c.take(P * (size_t)I * 4);
   if (path == MOE_PATH_STREAM) L.y = c.take(P * (size_t)H * 4);  // y in float
   if (path == MOE_PATH_MFMA) {
     // y in fp16, one exponent per (pair, kYGroup outputs), one plane per K part of GEMM2
     const size_t parts = (size_t)moe::mfma_k_parts(I);
     L.y = c.take(parts * P * (size_t)H * 2);
     L.yexp = c.take(parts * P * (size_t)moe::mfma_y_groups(H));
-    // x and h code rows padded to whole 128-wide blocks (zero past H, I)
-    L.xq = c.take((size_t)T * moe::mfma_pad(H));
-    L.xs = c.take((size_t)T * 4);
-    L.hq = c.take(P * (size_t)moe::mfma_pad(I));
-    L.hs = c.take(P * 4);
+    if (act == MOE_ACT_GROUP_FP8_W8A8) {
+      // x codes and one scale per (token, 128 columns); h codes and one scale per (sorted
+      // pair, 128 features) (H and I multiples of 128)
+      L.xq = c.take((size_t)T * H);
+      L.xs = c.take((size_t)T * (H / 128) * 4);
+      L.hq = c.take(P * (size_t)I);
+      L.hs = c.take(P * (size_t)(I / 128) * 4);
+    } else {
+      // x and h code rows padded to whole 128-wide blocks (zero past H, I)
+      L.xq = c.take((size_t)T * moe::mfma_pad(H));
+      L.xs = c.take((size_t)T * 4);
+      L.hq = c.take(P * (size_t)moe::mfma_pad(I));
+      L.hs = c.take(P * 4);
+    }
   }
   if (act == MOE_ACT_GROUP_FP8) {
     L.xq = c.take((size_t)T * H);  // x codes and one scale per (token, 128 columns)
@@ -276,9 +289,13 @@ int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const mo
             const Layout& L, int T, int E, int H, int I, int top_k, float* hf);
 int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Plan& plan, void* workspace,
               const Layout& L, int T, int E, int H, int I, int top_k, void* out, int out_bf16);
+int mfma_up_groups(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
+                   const Layout& L, int T, int E, int H, int I, int top_k, uint8_t* hq, float* hs);
+int mfma_down_groups(Runner& R, const uint8_t* hq, const float* hs, const moe::BankArg& b2, const moe::Plan& plan,
+                     void* workspace, const Layout& L, int T, int E, int H, int I, int top_k, void* out, int out_bf16);
 int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, const char* bank_name, int64_t N,
-                    int64_t K, int T, int E, int H, int I, int top_k, void* workspace, size_t workspace_bytes,
-                    Layout* Lout, moe::Plan* plan);
+                    int64_t K, int T, int E, int H, int I, int top_k, int act_mode, void* workspace,
+                    size_t workspace_bytes, Layout* Lout, moe::Plan* plan);
 
 }  // namespace
 
@@ -422,8 +439,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "H and I must be positive (got H=%d, I=%d)", H, I);
-  // rows of 16-byte code chunks; a last 128-wide scale block may be partial (the MFMA path
-  // needs whole blocks and is never chosen otherwise)
+  // rows of 16-byte code chunks; a last 128-wide scale block may be partial on every path
   if (H % 16 != 0 || I % 16 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 16 (got H=%d, I=%d)", H, I);
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
@@ -496,8 +512,8 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
       // one quantisation row per (token, 128 columns)
       g1.xq = at<uint8_t>(workspace, L.xq);
       g1.xs = at<float>(workspace, L.xs);
-      RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T * (H / 128), 128, 128, at<uint8_t>(workspace, L.xq),
-                                                   at<float>(workspace, L.xs), s),
+      RUN(MOE_K_QUANT, moe::launch_quant_groups_bf16(hidden, T, H, at<uint8_t>(workspace, L.xq),
+                                                     at<float>(workspace, L.xs), s),
           "quant launch");
     }
     RUN(MOE_K_GEMM1, moe::launch_gemm1_w8a16(g1, s), "gemm1 launch");
@@ -508,6 +524,12 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
       RUN(MOE_K_GEMM2, moe::launch_gemm2_expert(h, b2, plan, slots, H, I, top_k, y, s), "gemm2 launch");
       RUN(MOE_K_COMBINE, moe::launch_combine(y, w, T, H, top_k, out, out_bf16, s), "combine launch");
     }
+  } else if (act_mode == MOE_ACT_GROUP_FP8_W8A8) {
+    uint8_t* hq = at<uint8_t>(workspace, L.hq);
+    float* hs = at<float>(workspace, L.hs);
+    int st2 = mfma_up_groups(R, hidden, b13, plan, workspace, L, T, E, H, I, top_k, hq, hs);
+    if (st2 == MOE_OK) st2 = mfma_down_groups(R, hq, hs, b2, plan, workspace, L, T, E, H, I, top_k, out, out_bf16);
+    if (st2 != MOE_OK) return st2;
   } else {
     float* hf = at<float>(workspace, L.h);
     int st2 = mfma_up(R, hidden, b13, plan, workspace, L, T, E, H, I, top_k, hf);
@@ -548,19 +570,52 @@ int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Pla
   return MOE_OK;
 }
 
-// Checks and routing shared by the two test exports of the MFMA halves: the sizes, the
-// bank, the workspace of a forward forced onto MFMA, then route + sort into the workspace.
+// The group-scaled variant: x quantised per (token, 128 columns), then GEMM1 with h
+// quantised per (sorted pair, 128 features) in its epilogue into hq / hs.
+int mfma_up_groups(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
+                   const Layout& L, int T, int E, int H, int I, int top_k, uint8_t* hq, float* hs) {
+  hipStream_t s = R.s;
+  const int64_t P = (int64_t)T * top_k;
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* xs = at<float>(workspace, L.xs);
+  RUN(MOE_K_QUANT, moe::launch_quant_groups_bf16(hidden, T, H, xq, xs, s), "quant launch");
+  RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma_groups(xq, xs, b13, plan, E, (int)P, H, I, top_k, hq, hs, s),
+      "gemm1 mfma launch");
+  return MOE_OK;
+}
+
+// Its second half: the down GEMM on the group-scaled h codes, and the combine.
+int mfma_down_groups(Runner& R, const uint8_t* hq, const float* hs, const moe::BankArg& b2, const moe::Plan& plan,
+                     void* workspace, const Layout& L, int T, int E, int H, int I, int top_k, void* out,
+                     int out_bf16) {
+  hipStream_t s = R.s;
+  const int64_t P = (int64_t)T * top_k;
+  _Float16* y16 = at<_Float16>(workspace, L.y);
+  int8_t* yexp = at<int8_t>(workspace, L.yexp);
+  RUN(MOE_K_GEMM2, moe::launch_gemm2_mfma_groups(hq, hs, b2, plan, E, (int)P, H, I, y16, yexp, s),
+      "gemm2 mfma launch");
+  RUN(MOE_K_COMBINE, moe::launch_combine_f16(y16, yexp, plan.w, plan.ids, b2.bias, T, H, top_k, moe::mfma_k_parts(I),
+                                             out, out_bf16, s),
+      "combine launch");
+  return MOE_OK;
+}
+
+// Checks and routing shared by the test exports of the MFMA halves: the sizes, the bank,
+// the workspace of a forward forced onto MFMA with activations act_mode (MOE_ACT_ROW_FP8 or
+// MOE_ACT_GROUP_FP8_W8A8), then route + sort into the workspace.
 int mfma_half_setup(Runner& R, const float* logits, const moe_fp8_bank* bank, const char* bank_name, int64_t N,
-                    int64_t K, int T, int E, int H, int I, int top_k, void* workspace, size_t workspace_bytes,
-                    Layout* Lout, moe::Plan* plan) {
+                    int64_t K, int T, int E, int H, int I, int top_k, int act_mode, void* workspace,
+                    size_t workspace_bytes, Layout* Lout, moe::Plan* plan) {
   int st = check_sizes(T, E, top_k);
   if (st) return st;
   if (!moe::mfma_shape_ok(H, I))
     return fail(MOE_ERR_UNSUPPORTED, "MFMA path needs H <= 8192 and I <= 4096 (got H=%d, I=%d)", H, I);
+  if (act_mode == MOE_ACT_GROUP_FP8_W8A8 && !moe::mfma_groups_shape_ok(H, I))
+    return fail(MOE_ERR_UNSUPPORTED, "group-scaled MFMA needs H and I multiples of 128 (got H=%d, I=%d)", H, I);
   if ((st = check_bank(bank, bank_name, E, N, K))) return st;
   if (T == 0) return ok();
   if (!logits) return fail(MOE_ERR_ARG, "logits must be non-NULL");
-  const Layout L = layout_for(MOE_PATH_MFMA, MOE_ACT_ROW_FP8, T, E, H, I, top_k);
+  const Layout L = layout_for(MOE_PATH_MFMA, act_mode, T, E, H, I, top_k);
   if (!workspace || workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -615,8 +670,8 @@ int moe_fp8_block_mfma_up(const uint16_t* hidden, const float* logits, const moe
   Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
   Layout L{};
   moe::Plan plan{};
-  int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, workspace, workspace_bytes,
-                           &L, &plan);
+  int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, MOE_ACT_ROW_FP8, workspace,
+                           workspace_bytes, &L, &plan);
   if (st != MOE_OK || T == 0) return st;
   if (!hidden || !h) return fail(MOE_ERR_ARG, "hidden and h must be non-NULL");
   if (!aligned16(hidden) || !aligned16(h)) return fail(MOE_ERR_ALIGN, "hidden and h must be 16-byte aligned");
@@ -631,11 +686,44 @@ int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_b
   Layout L{};
   moe::Plan plan{};
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
-  int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, workspace, workspace_bytes, &L, &plan);
+  int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, MOE_ACT_ROW_FP8, workspace, workspace_bytes,
+                           &L, &plan);
   if (st != MOE_OK || T == 0) return st;
   if (!h || !out) return fail(MOE_ERR_ARG, "h and out must be non-NULL");
   if (!aligned16(h) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h and out must be 16-byte aligned");
   st = mfma_down(R, h, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out, out_dtype == MOE_BF16);
+  return st != MOE_OK ? st : ok();
+}
+
+int moe_fp8_block_mfma_up_groups(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, int T, int E,
+                                 int H, int I, int top_k, uint8_t* h_codes, float* h_scales, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
+  Layout L{};
+  moe::Plan plan{};
+  int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, MOE_ACT_GROUP_FP8_W8A8,
+                           workspace, workspace_bytes, &L, &plan);
+  if (st != MOE_OK || T == 0) return st;
+  if (!hidden || !h_codes || !h_scales) return fail(MOE_ERR_ARG, "hidden, h_codes and h_scales must be non-NULL");
+  if (!aligned16(hidden) || !aligned16(h_codes)) return fail(MOE_ERR_ALIGN, "hidden and h_codes must be 16-byte aligned");
+  st = mfma_up_groups(R, hidden, bank_arg(w13), plan, workspace, L, T, E, H, I, top_k, h_codes, h_scales);
+  return st != MOE_OK ? st : ok();
+}
+
+int moe_fp8_block_mfma_down_groups(const uint8_t* h_codes, const float* h_scales, const float* logits,
+                                   const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
+                                   int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
+  Layout L{};
+  moe::Plan plan{};
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
+  int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, MOE_ACT_GROUP_FP8_W8A8, workspace,
+                           workspace_bytes, &L, &plan);
+  if (st != MOE_OK || T == 0) return st;
+  if (!h_codes || !h_scales || !out) return fail(MOE_ERR_ARG, "h_codes, h_scales and out must be non-NULL");
+  if (!aligned16(h_codes) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h_codes and out must be 16-byte aligned");
+  st = mfma_down_groups(R, h_codes, h_scales, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out,
+                        out_dtype == MOE_BF16);
   return st != MOE_OK ? st : ok();
 }
 
@@ -668,6 +756,18 @@ int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* 
   if (!x || !codes || !scales) return fail(MOE_ERR_ARG, "x, codes and scales must be non-NULL");
   if (!aligned16(x) || !aligned16(codes)) return fail(MOE_ERR_ALIGN, "x and codes must be 16-byte aligned");
   HIP_CHECK(moe::launch_quant_rows_bf16(x, rows, cols, cols, codes, scales, (hipStream_t)stream), "quant launch");
+  return ok();
+}
+
+int moe_fp8_block_quantize_groups(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                                  void* stream) {
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_ARG, "rows must be >= 0 and cols > 0");
+  if (cols % 128 != 0 || cols > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 128 and at most 8192 (got %d)", cols);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(MOE_ERR_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes)) return fail(MOE_ERR_ALIGN, "x and codes must be 16-byte aligned");
+  HIP_CHECK(moe::launch_quant_groups_bf16(x, rows, cols, codes, scales, (hipStream_t)stream), "quant launch");
   return ok();
 }
 

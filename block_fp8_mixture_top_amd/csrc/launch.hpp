@@ -118,6 +118,10 @@ hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, v
 // < 512) and scales amax/448 of rows of bf16 x.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
                                   hipStream_t s);
+// e4m3 codes [rows, cols] and one scale per (row, 128-column group) [rows, cols/128] of rows
+// of bf16 x (cols a multiple of 128, at most 8192).
+hipError_t launch_quant_groups_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                                   hipStream_t s);
 constexpr int kMfmaTileM = 128;  // sorted pairs per MFMA tile
 constexpr int kYGroup = 32;      // MFMA path: outputs of a pair's y that share one exponent
 size_t mfma_tiles_bound(int P, int E);
@@ -125,6 +129,9 @@ size_t mfma_tiles_bound(int P, int E);
 // A last 128-wide block that is partial multiplies zero activation codes past the row end
 // (the code rows of x and h are padded to mfma_pad(H), mfma_pad(I) bytes).
 bool mfma_shape_ok(int H, int I);
+// The group-scaled variant (x per (token, 128 columns), h per (pair, 128 features)) needs
+// whole groups: H and I multiples of 128 as well.
+bool mfma_groups_shape_ok(int H, int I);
 __host__ __device__ inline int mfma_pad(int n) { return (n + 127) / 128 * 128; }
 // exponent groups of a pair's y row
 __host__ __device__ inline int mfma_y_groups(int H) { return (H + kYGroup - 1) / kYGroup; }
@@ -136,6 +143,11 @@ int mfma_k_parts(int I);
 // xq[T, mfma_pad(H)] and scales xs[T].
 hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
                              int P, int H, int I, int k, float* hf, hipStream_t s);
+// GEMM1 on x codes xq[T, H] with one scale per (token, 128-column group) xs[T, H/128]; h is
+// quantised in the epilogue per (sorted pair position, 128-feature group): codes hq[P, I] and
+// scales hs[P, I/128] (scale = group amax / 448, 1 for a zero group).
+hipError_t launch_gemm1_mfma_groups(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
+                                    int P, int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s);
 // The same quantisation for rows of float (hf, rows in sorted-position order).
 hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, int ostride, uint8_t* codes, float* scales,
                                  hipStream_t s);
@@ -144,6 +156,9 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, int ostride
 // yexp[pair, mfma_y_groups(H)] (no atomics; the combine applies the weights).
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
+// The same from h codes hq[P, I] with one scale per (pair, 128-feature group) hs[P, I/128].
+hipError_t launch_gemm2_mfma_groups(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E,
+                                    int P, int H, int I, _Float16* y, int8_t* yexp, hipStream_t s);
 // out[t, n] = sum_j w[t, j] * (y[t*k + j, n] * 2^yexp[t*k + j, n/kYGroup] + bias[ids[t*k + j], n]),
 // slots summed in order; bias may be nullptr (no w2 bias).
 // parts: the number of y planes (K parts) of each pair, summed in plane order first.

@@ -1,10 +1,12 @@
 // W8A8 grouped GEMMs on gfx950's fp8 matrix cores, for expert batches large enough to be
 // a dense contraction (prefill).
 //
-// Activations are quantised per row to e4m3 with a dynamic scale, as the gathered FP8 path
-// of gaudi-cookbook "fp8-moe-gather" does for checkpoints with dynamic activation scales
+// Activations are quantised to e4m3 with a dynamic scale, as the gathered FP8 path of
+// gaudi-cookbook "fp8-moe-gather" does for checkpoints with dynamic activation scales
 // (section Who is affected): scale = amax/448 (1 for an all-zero row), code = e4m3(x/scale),
-// rows being tokens for GEMM1 and (token, slot) pairs for GEMM2.
+// one scale per row (tokens for GEMM1, (token, slot) pairs for GEMM2) or, in the group
+// variant, one per 128-column group of a row (the K blocks of the weight scales), h then
+// being quantised inside GEMM1.
 //
 // One v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 scales) covers exactly one 128-wide
 // K block, so every MFMA result is one block's partial sum and takes that block's bank
@@ -103,6 +105,51 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
   }
   zero_tail(codes + (size_t)row * ostride, cols, ostride, lane);
   if (lane == 0) scales[row] = s;
+}
+
+// The same with one scale per 128-column group (cols a multiple of 128): a 512-column piece
+// holds four groups, lanes 16q .. 16q+15 holding group q's 128 values, so a group's amax is
+// a maximum over 16 neighbouring lanes. Codes [rows, cols], scales [rows, cols/128].
+template <int IT>
+__global__ __launch_bounds__(256) void quant_groups_bf16_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales) {
+  const int row = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+  if (row >= rows) return;
+  const int lane = lane_id();
+  const uint16_t* xr = x + (size_t)row * cols;
+  u32x4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    v[it] = *(const u32x4*)(xr + (c < cols ? c : cols - 8));
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = lane * 8 + it * kWave * 8;
+    const bool in = c < cols;  // whole groups of 16 lanes are in or out (cols % 128 == 0)
+    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_lo(w[q])) : 0.0f);
+      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_hi(w[q])) : 0.0f);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, kWave));
+    const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+    const double rs = 1.0 / (double)s;
+    if (!in) continue;
+    uint32_t out[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t a = enc2(quot(bf16_lo(w[2 * q]), rs), quot(bf16_hi(w[2 * q]), rs));
+      const uint32_t b = enc2(quot(bf16_lo(w[2 * q + 1]), rs), quot(bf16_hi(w[2 * q + 1]), rs));
+      out[q] = a | (b << 16);
+    }
+    *(uint2*)(codes + (size_t)row * cols + c) = make_uint2(out[0], out[1]);
+    if ((lane & 15) == 0) scales[(size_t)row * (cols / 128) + c / 128] = s;
+  }
 }
 
 // The same for rows of float (h before the down GEMM, in sorted-position order), two
@@ -280,6 +327,13 @@ __device__ __forceinline__ void g2lds(const void* g, const uint8_t* lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
 }
 
+// The same with 4 bytes per lane (lane j: lds + 4 j).
+__device__ __forceinline__ void g2lds4(const void* g, const uint8_t* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(a) : "memory");
+}
+
 // Wait until at most N of this wave's vector memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -342,17 +396,33 @@ __device__ __forceinline__ void scale_ratio(const float* sc, int n, int kb, floa
 // read into registers while the current one is multiplied. A = weight rows (features),
 // B = token rows, so lane (r16, kq) of a 16x16 result holds features 4kq..4kq+3 of token
 // r16. h = silu(g)*u is written in float, [sorted pair, I]; GEMM2 quantises it per row.
+//
+// GROUP: x carries one scale per (token, 128-column group) xs[T, H/128], the group of each
+// K block, so the scale of a block product differs per token: every MFMA starts from zero
+// and its product is scaled into the accumulator by (weight block scale) x (the token's
+// group scale) on the VALU. The stage's group scales of the tile's tokens travel with the
+// stage in the ring (one 4-byte direct load per wave). h is then quantised in the epilogue,
+// one scale per (pair, 128-feature group) = this workgroup's feature block: the group's amax
+// is a maximum over the four waves holding its features (through LDS), scale = amax/448
+// (float division, 1 if zero), codes = e4m3(h / scale); codes go to hq [sorted pair, I] and
+// scales to hs [sorted pair, I/128]. Needs H and I multiples of 128.
+template <bool GROUP>
 __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                                                             BankArg w13, Plan plan, int E, int H, int I, int k,
-                                                            int nblocks, float* __restrict__ hf) {
+                                                            int nblocks, float* __restrict__ hf,
+                                                            uint8_t* __restrict__ hq, float* __restrict__ hs) {
   constexpr int TM = kTM;                 // pairs per tile
   constexpr int NTT = 4;                  // token tiles per wave (64 tokens)
   constexpr int NF = 4;                   // weight tiles per wave: 2 gate + 2 up
   constexpr int QB = 64 * kRowB;          // one feature quarter's weight rows of a stage
   constexpr int XB = TM * kRowB;          // the tile's x rows of a stage
-  constexpr int SB = 4 * QB + XB;         // one stage
-  constexpr int LPW = 4 + 2;              // direct loads per wave per stage
+  // GROUP: the group scales of the tile's 128 token rows for the stage's K block; wave w's
+  // load puts rows 16w .. 16w+15 at 256w (lane j copies row 16w + j%16 to 256w + 4j)
+  constexpr int XSB = GROUP ? 8 * 256 : 0;
+  constexpr int SB = 4 * QB + XB + XSB;   // one stage
+  constexpr int LPW = GROUP ? 7 : 6;      // direct loads per wave per stage
   __shared__ __align__(16) uint8_t ring[kStages * SB];
+  __shared__ float s_am[GROUP ? 4 * TM : 1];  // GROUP: per (feature quarter, tile row) h maxima
   // block scales, their ratios and last values of three row blocks: the gate rows' block and
   // the (up to) two blocks the up rows fall in (one unless I % 128 != 0)
   __shared__ float s_sc[3 * (kMaxH / 128)];
@@ -420,23 +490,33 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     const int r = wave * 16 + j * 8 + lr;
     xsrc[j] = xq + (size_t)s_tok[r] * Hp + ((lc ^ sw(r)) << 4);
   }
-  auto copy = [&](int kb, int j) {  // this wave's copy j (0..5) of stage kb
+  // GROUP: this lane's token row's group scales (row 16w + lane%16)
+  const float* xsrow = GROUP ? xs + (size_t)s_tok[wave * 16 + r16] * nkb : xs;
+  auto copy = [&](int kb, int j) {  // this wave's copy j (0 .. LPW-1) of stage kb
     uint8_t* slot = ring + (kb % kStages) * SB;
     if (j < 4) {
       const uint32_t ch = kb == nkb - 1 && wch[j] >= ktail ? ktail - 16 : wch[j];
       g2lds(wb + kb * 128 + wrow[j] + ch, slot + fq * QB + (th * 4 + j) * 1024);
-    } else {
+    } else if (j < 6) {
       g2lds(xsrc[j - 4] + kb * 128, slot + 4 * QB + (wave * 16 + (j - 4) * 8) * kRowB);
+    } else {
+      g2lds4(xsrow + kb, slot + 4 * QB + XB + wave * 256);
     }
   };
-  float xsc[NTT];  // x scale of token 64th + tt*16 + r16
+  float xsc[NTT];  // x scale of token 64th + tt*16 + r16 (per-row x only)
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) xsc[tt] = xs[s_tok[th * 64 + tt * 16 + r16]];
+  for (int tt = 0; tt < NTT; ++tt) xsc[tt] = GROUP ? 1.0f : xs[s_tok[th * 64 + tt * 16 + r16]];
 
-  // Operands of one K block in registers: this wave's token rows (B) and weight rows (A).
+  // Operands of one K block in registers: this wave's token rows (B) and weight rows (A),
+  // and with GROUP the group scales of its tokens for that block.
   struct Ops {
     i32x8 bx[NTT];
     i32x8 wa[NF];
+    float sx[GROUP ? NTT : 1];
+  };
+  // the group scale of tile row th*64 + t*16 + r16 in a stage slot
+  auto read_sx = [&](const uint8_t* slot, int t) {
+    return *(const float*)(slot + 4 * QB + XB + (th * 4 + t) * 256 + r16 * 4);
   };
   f32x4 acc[NF][NTT];
 #pragma unroll
@@ -453,8 +533,10 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 #pragma unroll
   for (int f = 0; f < 2; ++f) squ[f] = 1 + min((I + fb * 128 + fq * 32 + f * 16) / 128, bumax) - bu0;
   auto step = [&](int kb, const Ops& cur, Ops& nxt) {
-    // the scale ratios first, so that the explicit LDS wait below covers them too
-    const float rs[4] = {s_rt[kb], s_rt[kb], s_rt[squ[0] * nkb + kb], s_rt[squ[1] * nkb + kb]};
+    // the scale ratios (GROUP: the block scales) first, so that the explicit LDS wait below
+    // covers them too
+    const float* sq = GROUP ? s_sc : s_rt;
+    const float rs[4] = {sq[kb], sq[kb], sq[squ[0] * nkb + kb], sq[squ[1] * nkb + kb]};
     if (kb + 1 < nkb) {
       if (kb + 2 < nkb) wait_vm<LPW>();
       else wait_vm<0>();
@@ -470,23 +552,43 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
       if (refill) {
 #pragma unroll
         for (int j = 3 * g; j < 3 * g + 3; ++j) copy(kb + 3, j);
+        if (GROUP && g == 1) copy(kb + 3, 6);
       }
 #pragma unroll
       for (int t = 2 * g; t < 2 * g + 2; ++t) {
         nxt.bx[t] = lds_operand(rslot + 4 * QB, th * 64 + t * 16 + r16, kq);
         nxt.wa[t] = lds_operand(rslot + fq * QB, t * 16 + r16, kq);
+        if constexpr (GROUP) nxt.sx[t] = read_sx(rslot, t);
       }
       // gate tiles in group 0, up tiles in group 1
+      if constexpr (GROUP) {
+        // the group's 8 products, each MFMA issued before the previous one's result is
+        // scaled in (a zero block scale gives a zero factor: finite products add nothing)
+        constexpr int NJ = 2 * NTT;
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 pp = mfma_fp8(cur.wa[2 * g], cur.bx[0], z);
 #pragma unroll
-      for (int f = 2 * g; f < 2 * g + 2; ++f) {
-        const float r = rs[f];  // uniform
-        if (r != 0.0f) {        // a zero block scale adds nothing
+        for (int j = 0; j < NJ; ++j) {
+          const int f = 2 * g + j / NTT, tt = j % NTT;
+          f32x4 nx;
+          if (j + 1 < NJ) nx = mfma_fp8(cur.wa[2 * g + (j + 1) / NTT], cur.bx[(j + 1) % NTT], z);
+          const float c = rs[f] * cur.sx[tt];
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt)
+          for (int q = 0; q < 4; ++q) acc[f][tt][q] = __builtin_fmaf(c, pp[q], acc[f][tt][q]);
+          if (j + 1 < NJ) pp = nx;
+        }
+      } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[f][tt][q] *= r;
+        for (int f = 2 * g; f < 2 * g + 2; ++f) {
+          const float r = rs[f];  // uniform
+          if (r != 0.0f) {        // a zero block scale adds nothing
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) acc[f][tt] = mfma_fp8(cur.wa[f], cur.bx[tt], acc[f][tt]);
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[f][tt][q] *= r;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) acc[f][tt] = mfma_fp8(cur.wa[f], cur.bx[tt], acc[f][tt]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -513,6 +615,7 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     for (int t = 0; t < 4; ++t) {
       o0.bx[t] = lds_operand(rslot + 4 * QB, th * 64 + t * 16 + r16, kq);
       o0.wa[t] = lds_operand(rslot + fq * QB, t * 16 + r16, kq);
+      if constexpr (GROUP) o0.sx[t] = read_sx(rslot, t);
     }
   }
   for (int kb = 0; kb < nkb; kb += 2) {
@@ -532,27 +635,74 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
     buv[f] = *(const f32x4*)(bb + (hb ? I + i : 0));
   }
   // h of gate tile f (features fb*128 + 32fq + 16f + 4kq .. +3) for token 64th + 16tt + r16
+  if constexpr (GROUP) {
+    // the accumulators hold the scaled sums; h of every row (rows past the expert's pairs
+    // too: every lane takes part in the maxima and the barrier; their stores are skipped)
+    f32x4 hv[NTT][2];
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int pos = pos0 + th * 64 + tt * 16 + r16;
-    if (pos >= pos_end) continue;
+    for (int tt = 0; tt < NTT; ++tt) {
+      float m = 0.0f;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;  // features i .. i+3, all < I or none
-      if (i >= I) continue;
-      f32x4 h;
-      const float gs = s_last[0] * xsc[tt], us = s_last[squ[f]] * xsc[tt];
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g = acc[f][tt][q] * gs;
-        float u = acc[f + 2][tt][q] * us;
-        if (hb) {
-          g += bgv[f][q];
-          u += buv[f][q];
+        for (int q = 0; q < 4; ++q) {
+          float g = acc[f][tt][q];
+          float u = acc[f + 2][tt][q];
+          if (hb) {
+            g += bgv[f][q];
+            u += buv[f][q];
+          }
+          hv[tt][f][q] = silu_fast(g) * u;
+          m = __builtin_fmaxf(m, __builtin_fabsf(hv[tt][f][q]));
         }
-        h[q] = silu_fast(g) * u;
+      // over the four K-quarter lanes of the token: the wave's 32 features
+      m = __builtin_fmaxf(m, __shfl_xor(m, 16, kWave));
+      m = __builtin_fmaxf(m, __shfl_xor(m, 32, kWave));
+      if (kq == 0) s_am[fq * TM + th * 64 + tt * 16 + r16] = m;
+    }
+    __syncthreads();
+    const int ng = I / 128;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int row = th * 64 + tt * 16 + r16;
+      const int pos = pos0 + row;
+      const float amax = __builtin_fmaxf(__builtin_fmaxf(s_am[row], s_am[TM + row]),
+                                         __builtin_fmaxf(s_am[2 * TM + row], s_am[3 * TM + row]));
+      const float sc = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+      const double rsc = 1.0 / (double)sc;
+      if (pos >= pos_end) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;
+        const f32x4 v = hv[tt][f];
+        const uint32_t c4 = enc2(quot(v[0], rsc), quot(v[1], rsc)) | (enc2(quot(v[2], rsc), quot(v[3], rsc)) << 16);
+        *(uint32_t*)(hq + (size_t)pos * I + i) = c4;
       }
-      *(f32x4*)(hf + (size_t)pos * I + i) = h;
+      if (fq == 0 && kq == 0) hs[(size_t)pos * ng + fb] = sc;
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int pos = pos0 + th * 64 + tt * 16 + r16;
+      if (pos >= pos_end) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int i = fb * 128 + fq * 32 + f * 16 + kq * 4;  // features i .. i+3, all < I or none
+        if (i >= I) continue;
+        f32x4 h;
+        const float gs = s_last[0] * xsc[tt], us = s_last[squ[f]] * xsc[tt];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float g = acc[f][tt][q] * gs;
+          float u = acc[f + 2][tt][q] * us;
+          if (hb) {
+            g += bgv[f][q];
+            u += buv[f][q];
+          }
+          h[q] = silu_fast(g) * u;
+        }
+        *(f32x4*)(hf + (size_t)pos * I + i) = h;
+      }
     }
   }
 }
@@ -568,7 +718,8 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 // 64w+63 of each chunk (4 feature tiles) by the half's 64 pairs (4 pair tiles, whose h codes
 // stay in registers for every K block). Each wave streams its own w2 rows, (chunk, K block)
 // after (chunk, K block), through a private kRing2-deep LDS ring with kRing2 - 1 stages in
-// flight and no barriers. Each MFMA starts from zero and its block product is scaled into
+// flight and no barriers; the workgroups of one expert start at different chunks, so that
+// they do not all read the same rows at once. Each MFMA starts from zero and its block product is scaled into
 // the accumulator on the VALU while the next MFMA runs. Each pair's y row = s_h * W2 h is
 // written once, in fp16 with one power-of-two exponent per kYGroup (32) outputs; the combine
 // kernel applies the router weights. (Measured on gfx950: 128 pairs per workgroup, a ring
@@ -589,7 +740,10 @@ __device__ __forceinline__ void wait_stage(int later) {
   else wait_vm<0>();
 }
 
-template <int KB, int NP>  // I / 128, pair tiles per workgroup (NP * 16 pairs)
+// GROUP: h carries one scale per (pair, 128-feature group) hs[P, I/128] (from GEMM1's
+// epilogue), so the factor a block product takes is (w2 block scale) x (the pair's group
+// scale for that block), per lane; the pair's y needs no final scale.
+template <int KB, int NP, bool GROUP>  // K blocks of this part, pair tiles per workgroup (NP * 16 pairs)
 __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __restrict__ hq, const float* __restrict__ hs,
                                                             BankArg w2, Plan plan, int E,
                                                             int H, int I, int nblocks, int kb0, _Float16* __restrict__ y,
@@ -609,7 +763,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   static_assert(kRing2 - 1 <= 3, "wait_stage covers up to three younger stages");
   __shared__ __align__(16) uint8_t ring[NW * kRing2 * WB];
   __shared__ float s_sc[(kMaxH / 128) * (kMaxI / 128)];
-  __shared__ float s_hs[TP];
+  __shared__ float s_hs[GROUP ? TP * KB : TP];  // GROUP: [pair][K block of this part]
   __shared__ int s_prow[TP];
 
   const int nitems = plan.tile_off[E] * PARTS;
@@ -632,8 +786,15 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   stage_scales(s_sc, w2, (int64_t)e * w2.sexp + kb0, (H + 127) / 128, KB);
   if (tid < TP) {
     const bool ok = tid < nvalid;
-    s_hs[tid] = hs[pos0 + (ok ? tid : 0)];
+    if constexpr (!GROUP) s_hs[tid] = hs[pos0 + (ok ? tid : 0)];
     s_prow[tid] = ok ? plan.sorted[pos0 + tid] : -1;
+  }
+  if constexpr (GROUP) {
+    const int ng = Ip / 128;  // h groups per pair
+    for (int q = tid; q < TP * KB; q += 256) {
+      const int r = q / KB, kb = q - r * KB;
+      s_hs[q] = hs[(size_t)(pos0 + (r < nvalid ? r : 0)) * ng + kb0 + kb];
+    }
   }
   // the h codes into the ring space: (TP / 8) * KB copies of 8 rows x 128 bytes, a quarter
   // per wave (rows past the expert's pairs copy the first row; their results are never stored)
@@ -663,6 +824,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   // may hold fewer than FW: H is a multiple of 16, so each feature tile is in range or out)
   const int nch = (H - wave * FW + NCH - 1) / NCH;
   const int nst = nch * KB;
+  // workgroups of one expert start at different chunks so that they do not read the same w2
+  // rows at the same time
+  const int rot = ((tile - plan.tile_off[e]) * PARTS + part) % nch;
   // w2 copy i covers rows 8i .. 8i+7 of the wave's FW; chunk c adds c * NCH rows. Rows past H
   // read the last row and chunks past a partial last K block the row's last chunk (finite
   // codes, multiplied by the zero h codes there); neither result is stored.
@@ -677,7 +841,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   const uint32_t ktail = (uint32_t)(I - (nkb_all - 1) * 128);  // bytes of the last K block
   uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
-    const int c = st / KB, kb = st - c * KB;
+    const int c0 = st / KB, kb = st - c0 * KB;
+    const int c = c0 + rot < nch ? c0 + rot : c0 + rot - nch;
     uint8_t* slot = myring + (st % kRing2) * WB;
     const bool ptail = kb0 + kb == nkb_all - 1 && ktail < 128;  // uniform
     if (!ptail && c * NCH + wave * FW + FW <= H) {
@@ -721,9 +886,13 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
       i32x8 aw[NF];
 #pragma unroll
       for (int ft = 0; ft < NF; ++ft) aw[ft] = lds_operand(slot, ft * 16 + r16, kq);
-      const int n0 = c * NCH + wave * FW;
+      const int n0 = (c + rot < nch ? c + rot : c + rot - nch) * NCH + wave * FW;
       // outputs n0 .. n0 + FW - 1 share one 128-row scale block
       const float sc = s_sc[(n0 / kScaleBlock) * KB + kb];  // uniform
+      // the factor of each pair tile's products (GROUP: times the lane's pair's group scale)
+      float cp[NP];
+#pragma unroll
+      for (int pt = 0; pt < NP; ++pt) cp[pt] = GROUP ? sc * s_hs[(pt * 16 + r16) * KB + kb] : sc;
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
       {
         f32x4 pp = mfma_fp8(aw[0], bh[kb][0], z);
@@ -733,7 +902,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
           f32x4 nx;
           if (j + 1 < NF * NP) nx = mfma_fp8(aw[(j + 1) / NP], bh[kb][(j + 1) % NP], z);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(sc, pp[q], acc[ft][pt][q]);
+          for (int q = 0; q < 4; ++q) acc[ft][pt][q] = __builtin_fmaf(cp[pt], pp[q], acc[ft][pt][q]);
           if (j + 1 < NF * NP) pp = nx;
         }
       }
@@ -749,7 +918,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
           if (pt < npt) {
             const int rl = pt * 16 + r16;
             const int prow = s_prow[rl];
-            const float hsc = s_hs[rl];
+            const float hsc = GROUP ? 1.0f : s_hs[rl];
 #pragma unroll
             for (int g = 0; g < NF / GT; ++g) {
               float v[GT][4];
@@ -784,12 +953,35 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
     }
   }
 }
-template <int KB, int NP>
+template <int KB, int NP, bool GROUP>
 hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int nblocks, int H,
                int I, int kb0, _Float16* y, int8_t* yexp, hipStream_t s) {
-  launch_kernel(gemm2_mfma_kernel<KB, NP>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks, kb0,
-                y, yexp);
+  launch_kernel(gemm2_mfma_kernel<KB, NP, GROUP>, dim3(nblocks), dim3(256), 0, s, hq, hs, w2, plan, E, H, I, nblocks,
+                kb0, y, yexp);
   return hipGetLastError();
+}
+
+// GEMM2 over its K parts of up to four 128-wide blocks, each into its own y plane.
+template <bool GROUP>
+hipError_t gemm2_parts(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P, int H,
+                       int I, _Float16* y, int8_t* yexp, hipStream_t s) {
+  const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
+  const int nkb = mfma_pad(I) / 128;
+  for (int part = 0; part < mfma_k_parts(I); ++part) {
+    const int kb0 = part * kMfmaPartBlocks;
+    const int kbn = nkb - kb0 < kMfmaPartBlocks ? nkb - kb0 : kMfmaPartBlocks;
+    _Float16* yp = y + (size_t)part * P * H;
+    int8_t* ep = yexp + (size_t)part * P * mfma_y_groups(H);
+    hipError_t err;
+    switch (kbn) {
+      case 1: err = g2m<1, kG2PairTiles, GROUP>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      case 2: err = g2m<2, kG2PairTiles, GROUP>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      case 3: err = g2m<3, kG2PairTiles, GROUP>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+      default: err = g2m<4, kG2PairTiles, GROUP>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
+    }
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -805,6 +997,8 @@ size_t mfma_tiles_bound(int P, int E) {
 bool mfma_shape_ok(int H, int I) {
   return H % 16 == 0 && H > 0 && H <= kMaxH && I % 16 == 0 && I > 0 && I <= kMaxIParts;
 }
+
+bool mfma_groups_shape_ok(int H, int I) { return mfma_shape_ok(H, I) && H % 128 == 0 && I % 128 == 0; }
 
 int mfma_k_parts(int I) { return (mfma_pad(I) / 128 + kMfmaPartBlocks - 1) / kMfmaPartBlocks; }
 
@@ -837,6 +1031,20 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int cols, int ostride
   return launch_quant_rows_f32_kernel(x, rows, cols, ostride, codes, scales, s);
 }
 
+hipError_t launch_quant_groups_bf16(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                                   hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  const int it = (cols + kWave * 8 - 1) / (kWave * 8);
+  if (cols <= 0 || cols % 128 != 0) return hipErrorInvalidValue;
+  if (it <= 1) launch_kernel(quant_groups_bf16_kernel<1>, grid, block, 0, s, x, rows, cols, codes, scales);
+  else if (it <= 2) launch_kernel(quant_groups_bf16_kernel<2>, grid, block, 0, s, x, rows, cols, codes, scales);
+  else if (it <= 4) launch_kernel(quant_groups_bf16_kernel<4>, grid, block, 0, s, x, rows, cols, codes, scales);
+  else if (it <= 8) launch_kernel(quant_groups_bf16_kernel<8>, grid, block, 0, s, x, rows, cols, codes, scales);
+  else if (it <= 16) launch_kernel(quant_groups_bf16_kernel<16>, grid, block, 0, s, x, rows, cols, codes, scales);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_combine_f16(const _Float16* y, const int8_t* yexp, const float* w, const int32_t* ids,
                               const float* bias, int T, int H, int k, int parts, void* out, int out_bf16,
                               hipStream_t s) {
@@ -854,31 +1062,30 @@ hipError_t launch_gemm1_mfma(const uint8_t* xq, const float* xs, const BankArg& 
                              int H, int I, int k, float* hf, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
   const int nblocks = (int)mfma_tiles_bound(P, E) * (mfma_pad(I) / 128);
-  launch_kernel(gemm1_mfma_kernel, dim3(nblocks), dim3(512), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks, hf);
+  launch_kernel(gemm1_mfma_kernel<false>, dim3(nblocks), dim3(512), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks, hf,
+                nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm1_mfma_groups(const uint8_t* xq, const float* xs, const BankArg& w13, const Plan& plan, int E,
+                                    int P, int H, int I, int k, uint8_t* hq, float* hs, hipStream_t s) {
+  if (!mfma_groups_shape_ok(H, I)) return hipErrorInvalidValue;
+  const int nblocks = (int)mfma_tiles_bound(P, E) * (I / 128);
+  launch_kernel(gemm1_mfma_kernel<true>, dim3(nblocks), dim3(512), 0, s, xq, xs, w13, plan, E, H, I, k, nblocks,
+                nullptr, hq, hs);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_mfma(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P,
                              int H, int I, _Float16* y, int8_t* yexp, hipStream_t s) {
   if (!mfma_shape_ok(H, I)) return hipErrorInvalidValue;
-  const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
-  // K parts of up to four 128-wide blocks, each into its own y plane
-  const int nkb = mfma_pad(I) / 128;
-  for (int part = 0; part < mfma_k_parts(I); ++part) {
-    const int kb0 = part * kMfmaPartBlocks;
-    const int kbn = nkb - kb0 < kMfmaPartBlocks ? nkb - kb0 : kMfmaPartBlocks;
-    _Float16* yp = y + (size_t)part * P * H;
-    int8_t* ep = yexp + (size_t)part * P * mfma_y_groups(H);
-    hipError_t err;
-    switch (kbn) {
-      case 1: err = g2m<1, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
-      case 2: err = g2m<2, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
-      case 3: err = g2m<3, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
-      default: err = g2m<4, kG2PairTiles>(hq, hs, w2, plan, E, nblocks, H, I, kb0, yp, ep, s); break;
-    }
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
+  return gemm2_parts<false>(hq, hs, w2, plan, E, P, H, I, y, yexp, s);
+}
+
+hipError_t launch_gemm2_mfma_groups(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E,
+                                    int P, int H, int I, _Float16* y, int8_t* yexp, hipStream_t s) {
+  if (!mfma_groups_shape_ok(H, I)) return hipErrorInvalidValue;
+  return gemm2_parts<true>(hq, hs, w2, plan, E, P, H, I, y, yexp, s);
 }
 
 }  // namespace moe

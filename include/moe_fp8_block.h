@@ -45,7 +45,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a struct, an enum or an entry point's meaning. */
-#define MOE_FP8_BLOCK_ABI_VERSION 4
+#define MOE_FP8_BLOCK_ABI_VERSION 5
 
 /* Limits checked on every call. */
 #define MOE_FP8_BLOCK_MAX_EXPERTS 1024
@@ -101,9 +101,14 @@ typedef enum {
   MOE_ACT_PATH = 0,      /* the path's own: bf16 activations (exact W8A16) on GATHER and
                             STREAM; e4m3 per token and per (token, slot) on MFMA */
   MOE_ACT_ROW_FP8 = 1,   /* reported only: MFMA's per-row dynamic e4m3 on both GEMMs */
-  MOE_ACT_GROUP_FP8 = 2  /* GATHER / STREAM: GEMM1 on dynamic e4m3 activations with one scale
-                            per (token, 128-column group), scale = group amax/448; GEMM2 on
-                            float h. Needs H % 128 == 0; the gate then never picks MFMA. */
+  MOE_ACT_GROUP_FP8 = 2, /* dynamic e4m3 activations with one scale per 128-column group,
+                            scale = group amax/448. GATHER / STREAM: GEMM1 on x quantised per
+                            (token, 128 columns), GEMM2 on float h. MFMA: both GEMMs, x per
+                            (token, 128 columns) and h per ((token, slot), 128 features),
+                            reported as MOE_ACT_GROUP_FP8_W8A8. Needs H % 128 == 0, and on
+                            MFMA also I % 128 == 0 (a gate choice of MFMA moves to STREAM
+                            otherwise, a forced MFMA fails). */
+  MOE_ACT_GROUP_FP8_W8A8 = 3 /* reported only: MOE_ACT_GROUP_FP8 on MFMA */
 } moe_act;
 
 /* Host-side options; NULL means the defaults below. */
@@ -121,7 +126,8 @@ typedef struct {
 typedef struct {
   int32_t path;     /* moe_path taken (never AUTO) */
   int32_t act_mode; /* 0: bf16 activations, exact W8A16; 1: per-row dynamic e4m3 on both GEMMs
-                       (MFMA); 2: per-(token, 128-column) dynamic e4m3 on GEMM1, float GEMM2 */
+                       (MFMA); 2: per-(token, 128-column) dynamic e4m3 on GEMM1, float GEMM2;
+                       3: per-128-column-group dynamic e4m3 on both GEMMs (MFMA) */
   int32_t slots;    /* expert slots launched: min(E, T*top_k) */
   int32_t kernels;  /* kernel launches enqueued */
 } moe_run_info;
@@ -145,8 +151,8 @@ int moe_fp8_block_default_opts(moe_opts* opts);
  * library carries a table for takes the path measured fastest on MI355X at the nearest
  * swept T instead (the table is generated by block_fp8_mixture_top_amd/tune_gate.py from
  * the committed sweeps under profiles/; FreeToken PR #662 likewise picks its backend from
- * measured bandwidth). With act_mode MOE_ACT_GROUP_FP8 the gate never picks MFMA (STREAM
- * instead) and uses the thresholds. A forced path is reported unchanged; a gate choice the
+ * measured bandwidth). With act_mode MOE_ACT_GROUP_FP8 the gate uses the two thresholds
+ * (the tables were measured with MOE_ACT_PATH). A forced path is reported unchanged; a gate choice the
  * shape does not support moves to STREAM, as forward does. Writes path, act_mode and slots
  * into *info; no HIP call.
  */
@@ -193,8 +199,10 @@ size_t moe_fp8_block_workspace_size(int T, int E, int H, int I, int top_k, const
  * row end (the x and h code rows are padded in the workspace). Every pointer the
  * chosen path reads must be non-NULL. T = 0 is a no-op (info still filled).
  * The W8A16 paths (GATHER, STREAM) decode weights exactly and accumulate in float. MFMA
- * quantises x per token and h per (token, slot) row to e4m3 with scale amax/448 (float
- * division, 1 for a zero row; codes round to nearest even and saturate at 448) and
+ * quantises x per token and h per (token, slot) row (with MOE_ACT_GROUP_FP8: x per (token,
+ * 128 columns) and h per ((token, slot), 128 features), h inside the up/gate GEMM) to e4m3
+ * with scale amax/448 (float division, 1 for a zero row or group; codes round to nearest
+ * even and saturate at 448) and
  * multiplies on the fp8 matrix cores; its per-(token, slot) down-projection results reach
  * the combine in fp16 with a power-of-two exponent per 32 outputs (at most 2^-11 relative
  * rounding each). Every path writes each (token, slot) result once and sums a token's
@@ -228,7 +236,7 @@ int moe_fp8_block_forward_static(const uint16_t* hidden, const float* logits, co
 typedef enum {
   MOE_K_ROUTE = 1,    /* top-k and weights */
   MOE_K_SORT = 2,     /* token-to-expert sort (one or three kernels) */
-  MOE_K_QUANT = 3,    /* per-token e4m3 activation quantisation (MFMA path) */
+  MOE_K_QUANT = 3,    /* e4m3 activation quantisation (MFMA path; group-fp8 on any path) */
   MOE_K_HQUANT = 4,   /* per-(token, slot) e4m3 quantisation of h before the down GEMM (MFMA path) */
   MOE_K_GEMM1 = 5,    /* gate/up GEMM with silu(gate)*up */
   MOE_K_GEMM2 = 6,    /* down GEMM (with the combine on GATHER) */
@@ -274,6 +282,26 @@ int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_b
                             void* stream);
 
 /*
+ * The same two halves with MOE_ACT_GROUP_FP8 (gaudi-cookbook "fp8-moe-gather", Who is
+ * affected: block-quantized checkpoints with dynamic activation scales). Workspace of a
+ * forward forced onto MFMA with act_mode MOE_ACT_GROUP_FP8; H and I multiples of 128, H up
+ * to 8192 and I up to 4096 (MOE_ERR_UNSUPPORTED otherwise).
+ *   mfma_up_groups:   x quantised per (token, 128-column group), GEMM1 on the matrix cores
+ *                     and h quantised per (pair, 128-feature group): codes h_codes
+ *                     [T*top_k, I] uint8 and scales h_scales [T*top_k, I/128] float (group
+ *                     amax/448, 1 for a zero group), row p the pair at sorted position p.
+ *   mfma_down_groups: h_codes and h_scales in that layout, multiplied by w2 on the matrix
+ *                     cores and combined into out [T, H], as the forward's second half.
+ * Pointers are device pointers, hidden/h_codes/out 16-byte aligned. T = 0 is a no-op.
+ */
+int moe_fp8_block_mfma_up_groups(const uint16_t* hidden, const float* logits, const moe_fp8_bank* w13, int T, int E,
+                                 int H, int I, int top_k, uint8_t* h_codes, float* h_scales, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+int moe_fp8_block_mfma_down_groups(const uint8_t* h_codes, const float* h_scales, const float* logits,
+                                   const moe_fp8_bank* w2, int T, int E, int H, int I, int top_k, void* out,
+                                   int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The activation preparation of the MFMA path on its own: per-row dynamic e4m3.
  *   x [rows, cols] bf16; codes [rows, cols] uint8 out; scales [rows] float out, with
  *   scale = amax/448 (float division; 1 for an all-zero row) and code = e4m3 of x/scale
@@ -282,6 +310,15 @@ int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_b
  */
 int moe_fp8_block_quantize_rows(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
                                 void* stream);
+
+/*
+ * The same with one scale per (row, 128-column group) (the group-fp8 activations of
+ * MOE_ACT_GROUP_FP8): codes [rows, cols] uint8 out, scales [rows, cols/128] float out, each
+ * group quantised as a row above. cols % 128 == 0 and cols <= 8192 (MOE_ERR_UNSUPPORTED
+ * otherwise), 16-byte aligned x/codes.
+ */
+int moe_fp8_block_quantize_groups(const uint16_t* x, int rows, int cols, uint8_t* codes, float* scales,
+                                  void* stream);
 
 /* Device decode of n e4m3 codes to float with the kernels' own conversion (codes and
  * out device, n >= 0). Exposed so tests can check the decode over all 256 codes. */

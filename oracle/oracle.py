@@ -371,19 +371,25 @@ def _h_group(act_mode: int, I: int) -> int:
 
 
 def _requantize_h(W13, X, g, u, h, group=None):
-    """act_modes 1 and 3: h re-quantised to e4m3 before the down GEMM, one scale per group
-    of `group` consecutive columns of a (token, slot) row (the whole row by default; scale
+    """act_modes 1 and 3: requantize_h with the drift bound h_drift of these tokens."""
+    return requantize_h(h, h_drift(W13, X, g, u, h), group)
+
+
+def requantize_h(h, d, group=None):
+    """h [n, I] (float64) re-quantised to e4m3 before the down GEMM, one scale per group of
+    `group` consecutive columns of a (token, slot) row (the whole row by default; scale
     group amax/448 in float32 emulation, quantize_groups), and the elements whose rounding
-    an implementation may decide either way flagged: |v - midpoint| <= drift(h_i)/s +
-    |v| * drift(h_r)/amax, with r the argmax of the element's group and s, amax that
-    group's scale and maximum (the second term is the scale moving with amax)."""
+    an implementation may decide either way flagged, d being the drift bound of each h:
+    |v - midpoint| <= d_i/s + |v| * d_r/amax, with r the argmax of the element's group and
+    s, amax that group's scale and maximum (the second term is the scale moving with amax).
+    Returns the dequantised h and a dict of codes, scales (per row, or [n, I/group]), flags,
+    the distance between each element's two neighbouring codes (step) and d."""
     h32 = h.astype(np.float32)
     n, I = h32.shape
     group = I if group is None else group
     q, s = quantize_groups(h32, group)
     s_el = np.repeat(s.astype(np.float64), group, axis=1)  # each element's scale
     h_deq = _LUT[q] * s_el
-    d = h_drift(W13, X, g, u, h)
     a = np.abs(h32).reshape(n, I // group, group)
     amax = a.max(axis=2).astype(np.float64)  # [n, groups]
     r = a.argmax(axis=2)

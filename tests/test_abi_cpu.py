@@ -239,22 +239,36 @@ def test_binding_refuses_a_missing_library(tmp_path):
 
 
 def test_group_fp8_activations_gate_and_checks(lib):
-    """MOE_ACT_GROUP_FP8 runs on GATHER and STREAM: the gate's MFMA choice becomes STREAM,
-    a forced MFMA is refused, and H must be a multiple of 128."""
+    """MOE_ACT_GROUP_FP8 takes the thresholds: GATHER at T=1, MFMA (reported as act_mode 3,
+    both GEMMs on groups) at T=4096. H must be a multiple of 128 on every path and I on
+    MFMA too: the gate's MFMA choice then moves to STREAM, a forced MFMA is refused."""
     st, info = _path(lib, 1, 256, 8, act_mode=2)
     assert st == 0 and (info.path, info.act_mode) == (1, 2)
     st, info = _path(lib, 4096, 256, 8, act_mode=2)
+    assert st == 0 and (info.path, info.act_mode) == (3, 3)
+    st, info = _path(lib, 4096, 256, 8, act_mode=2, I=528)
     assert st == 0 and (info.path, info.act_mode) == (2, 2)
+    st, info = _path(lib, 4096, 256, 8, act_mode=2, force_path=3, I=528)
+    assert st == -2
     st, info = _path(lib, 4096, 256, 8)
     assert st == 0 and (info.path, info.act_mode) == (3, 1)
+
+    def ws(act, path):
+        o = L.Opts()
+        lib.moe_fp8_block_default_opts(ctypes.byref(o))
+        o.act_mode, o.force_path = act, path
+        return lib.moe_fp8_block_workspace_size(4096, 256, 2048, 512, 8, ctypes.byref(o))
+    # group codes and scales on top of STREAM's buffers; on MFMA no float h
+    assert ws(2, 2) > ws(0, 2) > 0
+    assert 0 < ws(2, 3) < ws(0, 3)
     o = L.Opts()
     lib.moe_fp8_block_default_opts(ctypes.byref(o))
     o.act_mode = 2
-    assert lib.moe_fp8_block_workspace_size(4096, 256, 2048, 512, 8, ctypes.byref(o)) > \
-        lib.moe_fp8_block_workspace_size(4096, 256, 2048, 512, 8, ctypes.byref(L.Opts(2.0, 2, 2, 0)))
     o.force_path = 3
-    st, msg, _ = _forward(lib, T=64, opts=o)
-    assert st == -2 and "GROUP_FP8" in msg
+    st, msg, _ = _forward(lib, T=64, opts=o, ws_bytes=16)
+    assert st == -5  # accepted on MFMA; only the workspace is short
+    st, msg, _ = _forward(lib, T=64, I=80, w13=_bank(160, 256), w2=_bank(256, 80), opts=o)
+    assert st == -2 and "I % 128" in msg
     o.force_path = 0
     st, msg, _ = _forward(lib, H=144, I=80, w13=_bank(160, 144), w2=_bank(144, 80), opts=o)
     assert st == -2 and "128" in msg

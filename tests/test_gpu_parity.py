@@ -47,7 +47,7 @@ def check_out(out, res, act_mode, what):
     if out.dtype == torch.bfloat16:
         err = np.maximum(0.0, err - bf16_half_ulp(np.maximum(np.abs(o), np.abs(ref))))
     extra = ""
-    if act_mode == 1:
+    if act_mode in (1, 3):
         err = np.maximum(0.0, err - res["allowance"])
         extra = f"allowance max {float(np.max(res['allowance'])) / den:.3e} flagged {res['n_flagged'] / res['n_h']:.3%}"
     r = float(np.max(err)) / den
@@ -354,17 +354,24 @@ def test_mlp_bias_decode_and_prefill_sampled():
     check_out(out[torch.from_numpy(rows).to(DEV)], res, 1, "bias prefill T=4096 sampled")
 
 
-def test_group_quantisation_bit_exact():
-    """Activation codes and scales per (token, 128-column group) match the oracle bit for bit."""
-    say("group quantisation")
-    g = torch.Generator().manual_seed(5)
-    x = (torch.randn(9, 1024, generator=g) * torch.rand(9, 8, generator=g).repeat_interleave(128, 1) * 9)
-    x[2, 256:384] = 0
+@pytest.mark.parametrize("cols", [128, 640, 1024, 2048, 7168])
+def test_group_quantisation_bit_exact(cols):
+    """Activation codes and scales per (token, 128-column group) match the oracle bit for bit:
+    groups of very different magnitudes, an all-zero group (scale 1), a group of bf16
+    subnormals (a subnormal float scale) and exact rounding midpoints."""
+    say("group quantisation", cols)
+    g = torch.Generator().manual_seed(5 + cols)
+    ng = cols // 128
+    x = torch.randn(9, cols, generator=g) * torch.rand(9, ng, generator=g).repeat_interleave(128, 1) * 9
+    x[2, :128] = 0
+    x[3, -128:] = torch.randn(128, generator=g) * 1e-39
+    x[4, :8] = torch.tensor([448.0, 416.0, 432.0, 3.375, -3.125, 0.0, -0.0, 1.0])
     x = x.to(torch.bfloat16)
-    codes, scales = M.quantize_rows(x.to(DEV).view(-1, 128))
+    codes, scales = M.quantize_groups(x.to(DEV))
     q, sc = O.quantize_groups(O.bf16_to_f64(bf16_bits(x)).astype(np.float32))
-    assert np.array_equal(scales.cpu().numpy().reshape(9, 8), sc)
-    assert np.array_equal(codes.cpu().numpy().reshape(9, 1024), q)
+    assert sc[2, 0] == 1.0 and 0 < sc[3, -1] < np.finfo(np.float32).tiny
+    assert np.array_equal(scales.cpu().numpy(), sc)
+    assert np.array_equal(codes.cpu().numpy(), q)
 
 
 @pytest.mark.parametrize("path", ["gather", "stream"])
@@ -394,8 +401,8 @@ def test_group_fp8_in_register_quantisation_matches_row_quantiser(H):
 
 
 def test_group_fp8_decode_and_grouped():
-    """The decode workload (GATHER, bf16 out) and T=4096, where the gate takes STREAM instead
-    of MFMA (sampled rows)."""
+    """The decode workload (GATHER, bf16 out) and T=4096, where the gate takes MFMA with both
+    GEMMs on groups (sampled rows; every output equal on a second run)."""
     banks = W.make_banks("decode", seed=1, device=DEV)
     c = W.make_case("decode", T=1, seed=1, device=DEV, banks=banks)
     say("group fp8 decode")
@@ -407,11 +414,28 @@ def test_group_fp8_decode_and_grouped():
     say("group fp8 T=4096")
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16,
                           act_mode=M.ACT_GROUP_FP8)
+    again, _ = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.bfloat16,
+                         act_mode=M.ACT_GROUP_FP8)
     torch.cuda.synchronize()
-    assert (info["path"], info["act_mode"]) == ("stream", 2)
+    assert (info["path"], info["act_mode"]) == ("mfma", 3)
+    assert torch.equal(out, again)
     rows = np.array([0, 5, 2048, 4095])
-    check_out(out[torch.from_numpy(rows).to(DEV)], oracle_out(c, rows=rows, act_mode=2), 2,
-              "group fp8 T=4096 sampled")
+    res = oracle_out(c, rows=rows, act_mode=3)
+    assert res["n_flagged"] <= 0.05 * res["n_h"]
+    check_out(out[torch.from_numpy(rows).to(DEV)], res, 3, "group fp8 T=4096 mfma sampled")
+
+
+@pytest.mark.parametrize("T", [3, 40, 300])
+def test_group_fp8_mfma(T):
+    """MFMA with both GEMMs on groups (x per (token, 128 columns), h per (pair, 128
+    features) quantised inside GEMM1), with biases, against the oracle's act_mode 3 at every
+    output; forced, so that few tokens per expert leave partial tiles."""
+    c = W.make_case("decode", T=T, seed=71 + T, device=DEV, E=16, H=640, I=384, top_k=4, bias_std=0.2)
+    say("group fp8 mfma", T)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=M.PATH_MFMA, act_mode=M.ACT_GROUP_FP8)
+    assert (info["path"], info["act_mode"]) == ("mfma", 3)
+    check_out(out, oracle_out(c, act_mode=3), 3, f"group fp8 mfma T={T}")
 
 
 @pytest.mark.parametrize("T,path", [(1, None), (16, None), (16, "stream")])
@@ -570,6 +594,66 @@ def _staged_mfma_check(c, what):
     say(what, f"down: max err/max|ref| {err.max() / np.abs(ref).max():.3e}, max err/bound {(err / bound).max():.3f}")
     assert np.isfinite(o).all() and np.all(err <= bound)
     assert len(_tiles_of(offsets)) >= c.E
+
+
+def _staged_group_check(c, what):
+    """Both halves of the group-scaled MFMA path on their own, at every pair and output.
+    Up: the h codes GEMM1 writes decode to the values of the oracle's group quantisation of
+    the exact h except where the oracle flags the rounding as ambiguous (coarse drift bound), and each group
+    scale lies within the group's largest drift / 448 of the oracle's. Down: fed the oracle's
+    codes and scales, the down GEMM and the combine against the oracle's definition, within
+    the accumulation, fp16-y and combine bound per output."""
+    hid = bf16_bits(c.hidden)
+    ids, w, _ = O.route(c.logits.cpu().numpy(), c.top_k)
+    counts, offsets, sp = O.sort_pairs(ids, c.E)
+    w13, w2 = bank_numpy(c.w13), bank_numpy(c.w2)
+    h, d = O.up_w8a8(hid, ids, w13, coarse=True, act_mode=3)
+    _, ex = O.requantize_h(h, d, 128)
+    codes, scales = M.mfma_up_groups(c.hidden, c.logits, c.w13, c.top_k, c.I)
+    cg, sg = codes.cpu().numpy(), scales.cpu().numpy().astype(np.float64)
+    lut = O.e4m3_lut()
+    diff = lut[cg] != lut[ex["h_codes"][sp]]  # by value: +0 and -0 (an h within its drift of 0) are one
+    say(what, f"up: {int(diff.sum())} codes differ, {int(ex['flags'].sum())} flagged of {ex['flags'].size}")
+    assert not (diff & ~ex["flags"][sp]).any()
+    s_ref = ex["h_scale"][sp].astype(np.float64)
+    dmax = d[sp].reshape(len(sp), -1, 128).max(axis=2)
+    assert np.all(np.abs(sg - s_ref) <= dmax / 448.0 * 1.001 + 2.0 ** -22 * s_ref)
+    q, sh = O.quantize_groups(h.astype(np.float32))
+    out = M.mfma_down_groups(torch.from_numpy(q[sp]).to(DEV), torch.from_numpy(sh[sp]).to(DEV), c.logits, c.w2,
+                             c.top_k, c.H)
+    o = out.cpu().numpy().astype(np.float64)
+    ref = O.down_w8a8_groups(q, sh, ids, w, w2)
+    hd = O.dequant_groups(q, sh)
+    bound = np.zeros_like(ref)
+    nparts = -(-c.I // 512)
+    for e, pairs in OO._pairs_by_expert(ids).items():
+        W2 = O.dequant_expert(w2, e)
+        per = np.zeros((len(pairs), c.H))
+        for part in range(nparts):
+            ks = slice(512 * part, min(512 * (part + 1), c.I))
+            yp = hd[pairs][:, ks] @ W2[:, ks].T
+            g32 = np.repeat(np.abs(yp).reshape(len(pairs), -1, 32).max(axis=2), 32, axis=1)
+            per += (O.acc_bound(W2[:, ks], hd[pairs][:, ks], coarse=True) + 2.0 ** -11 * 1.01 * g32
+                    + 2.0 ** -21 * np.abs(yp))
+        bound[pairs // c.top_k] += np.abs(w.ravel()[pairs])[:, None] * per
+    err = np.abs(o - ref)
+    say(what, f"down: max err/max|ref| {err.max() / np.abs(ref).max():.3e}, max err/bound {(err / bound).max():.3f}")
+    assert np.isfinite(o).all() and np.all(err <= bound)
+    assert len(_tiles_of(offsets)) >= c.E
+
+
+@pytest.mark.parametrize("E,H,I,k,T", [(256, 2048, 512, 8, 4096), (16, 1024, 640, 4, 256), (16, 512, 1536, 4, 600),
+                                       (32, 7168, 2048, 4, 1024)])
+def test_mfma_groups_staged(E, H, I, k, T):
+    """The group-scaled MFMA halves at the prefill shape (decode banks, T=4096), with I past
+    one K part (640, 1536) and at the large-expert shape (H=7168, I=2048, fp32 scales)."""
+    name = "large" if H == 7168 else "decode"
+    if E == 256:
+        c = W.make_case("prefill", T=T, seed=9, device=DEV, banks=W.make_banks("decode", seed=1, device=DEV))
+    else:
+        c = W.make_case(name, T=T, seed=E + I + 1, device=DEV, E=E, H=H, I=I, top_k=k)
+    say("mfma groups staged", E, H, I, k, T)
+    _staged_group_check(c, f"groups H={H} I={I} T={T}")
 
 
 @pytest.mark.parametrize("E,H,I,k,T", [(16, 1024, 640, 4, 256), (16, 512, 1536, 4, 600), (32, 7168, 2048, 4, 1024),
