@@ -139,11 +139,14 @@ def traffic_record(args):
     f_scale = COPY_BYTES / (cf * 1024.0)
     w_scale = COPY_BYTES / (cw * 1024.0)
     sym = KERNEL_SYMBOLS[args.kernel]
+    if args.act == "group_fp8" and args.kernel == "quant":
+        sym = "quant_groups_bf16"
     kf, nf = _counter_per_dispatch(args.fetch_dir, "FETCH_SIZE", sym)
     kw, nw = _counter_per_dispatch(args.write_dir, "WRITE_SIZE", sym)
     rec = {
         "kernel": args.kernel,
         "workload": args.workload,
+        "act": args.act,
         "fetch_kib_per_launch": round(kf, 1),
         "write_kib_per_launch": round(kw, 1),
         "dispatches": [nf, nw],
@@ -154,7 +157,7 @@ def traffic_record(args):
         "bytes_per_launch": round(kf * 1024.0 * f_scale + kw * 1024.0 * w_scale),
         "source_digest": source_digest(),
     }
-    path = os.path.join(ROOT, "profiles", f"traffic_{args.kernel}_{traffic_key(args.workload, args.T)}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.kernel}_{traffic_key(args.workload, args.T, args.act)}.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -202,9 +205,11 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload: str, T) -> str:
-    """Name of a workload's traffic record: the workload, plus T when it is not the default."""
-    return workload if T is None or T == WORKLOADS[workload]["T"] else f"{workload}_T{T}"
+def traffic_key(workload: str, T, act: str = "path") -> str:
+    """Name of a workload's traffic record: the workload, plus T when it is not the default,
+    plus the activation mode when it is not the path's own."""
+    key = workload if T is None or T == WORKLOADS[workload]["T"] else f"{workload}_T{T}"
+    return key if act == "path" else f"{key}_{act}"
 
 
 def committed_traffic(kernel: str, workload: str):
@@ -374,7 +379,7 @@ def measure(wl, T, steps, warmup, sets, replicas, path, act, seed, kernel_steps,
         achieved = kb / (dom_ms * 1e-3) / 1e9 if kb else None
         roofline = dict(bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=HBM_PEAK_GBS,
                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
-    roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T))
+    roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T, act))
     roofline["kernel"] = dom
     roofline["kernel_ms"] = round(dom_ms, 5)
     roofline["kernels_ms"] = {n: round(v, 5) for n, v in per_kernel.items()}
@@ -392,6 +397,7 @@ def summary(m):
     d = {
         "workload": f"{m['wl']}: E={m['E']} H={m['H']} I={m['I']} top_k={m['k']} T={m['T']}",
         "path": m["info"]["path"],
+        "act_mode": m["info"]["act_mode"],
         "steps": m["steps"],
         "ms_per_step": round(ms_step, 6),
     }
@@ -407,12 +413,13 @@ def summary(m):
 
 
 # Secondary workloads reported beside the headline decode line: (name, workload, T, steps,
-# warmup, input sets, bank replicas). One replica suffices where a forward already touches
-# more than the 256 MB Infinity Cache holds.
+# warmup, input sets, bank replicas, activations). One replica suffices where a forward
+# already touches more than the 256 MB Infinity Cache holds.
 EXTRAS = [
-    ("prefill_T4096", "prefill", 4096, 40, 4, 4, 1),
-    ("prefill_T16384", "prefill", 16384, 12, 2, 2, 1),
-    ("large_T1", "large", 1, 64, 8, 16, 1),
+    ("prefill_T4096", "prefill", 4096, 40, 4, 4, 1, "path"),
+    ("prefill_T16384", "prefill", 16384, 12, 2, 2, 1, "path"),
+    ("prefill_T16384_group_fp8", "prefill", 16384, 12, 2, 2, 1, "group_fp8"),
+    ("large_T1", "large", 1, 64, 8, 16, 1, "path"),
 ]
 
 
@@ -439,9 +446,9 @@ def main():
 
     extras = {}
     if wl == "decode" and T == 1 and args.path == "auto" and args.act == "path" and not args.no_extra:
-        for name, ewl, eT, esteps, ewarm, esets, erep in EXTRAS:
+        for name, ewl, eT, esteps, ewarm, esets, erep, eact in EXTRAS:
             torch.cuda.empty_cache()
-            em = measure(ewl, eT, esteps, ewarm, esets, erep, "auto", "path", args.seed, 8)
+            em = measure(ewl, eT, esteps, ewarm, esets, erep, "auto", eact, args.seed, 8)
             extras[name] = summary(em)
             print(f"[bench] {name}: {json.dumps(extras[name])}", file=sys.stderr, flush=True)
             del em
