@@ -670,11 +670,13 @@ int moe_fp8_block_mfma_up(const uint16_t* hidden, const float* logits, const moe
   Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
   Layout L{};
   moe::Plan plan{};
+  if (T > 0) {  // every check before the routing is enqueued
+    if (!hidden || !h) return fail(MOE_ERR_ARG, "hidden and h must be non-NULL");
+    if (!aligned16(hidden) || !aligned16(h)) return fail(MOE_ERR_ALIGN, "hidden and h must be 16-byte aligned");
+  }
   int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, MOE_ACT_ROW_FP8, workspace,
                            workspace_bytes, &L, &plan);
   if (st != MOE_OK || T == 0) return st;
-  if (!hidden || !h) return fail(MOE_ERR_ARG, "hidden and h must be non-NULL");
-  if (!aligned16(hidden) || !aligned16(h)) return fail(MOE_ERR_ALIGN, "hidden and h must be 16-byte aligned");
   st = mfma_up(R, hidden, bank_arg(w13), plan, workspace, L, T, E, H, I, top_k, h);
   return st != MOE_OK ? st : ok();
 }
@@ -686,11 +688,13 @@ int moe_fp8_block_mfma_down(const float* h, const float* logits, const moe_fp8_b
   Layout L{};
   moe::Plan plan{};
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
+  if (T > 0) {
+    if (!h || !out) return fail(MOE_ERR_ARG, "h and out must be non-NULL");
+    if (!aligned16(h) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h and out must be 16-byte aligned");
+  }
   int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, MOE_ACT_ROW_FP8, workspace, workspace_bytes,
                            &L, &plan);
   if (st != MOE_OK || T == 0) return st;
-  if (!h || !out) return fail(MOE_ERR_ARG, "h and out must be non-NULL");
-  if (!aligned16(h) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h and out must be 16-byte aligned");
   st = mfma_down(R, h, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out, out_dtype == MOE_BF16);
   return st != MOE_OK ? st : ok();
 }
@@ -701,11 +705,14 @@ int moe_fp8_block_mfma_up_groups(const uint16_t* hidden, const float* logits, co
   Runner R{(hipStream_t)stream, nullptr, 0, nullptr};
   Layout L{};
   moe::Plan plan{};
+  if (T > 0) {
+    if (!hidden || !h_codes || !h_scales) return fail(MOE_ERR_ARG, "hidden, h_codes and h_scales must be non-NULL");
+    if (!aligned16(hidden) || !aligned16(h_codes))
+      return fail(MOE_ERR_ALIGN, "hidden and h_codes must be 16-byte aligned");
+  }
   int st = mfma_half_setup(R, logits, w13, "w13", 2 * (int64_t)I, H, T, E, H, I, top_k, MOE_ACT_GROUP_FP8_W8A8,
                            workspace, workspace_bytes, &L, &plan);
   if (st != MOE_OK || T == 0) return st;
-  if (!hidden || !h_codes || !h_scales) return fail(MOE_ERR_ARG, "hidden, h_codes and h_scales must be non-NULL");
-  if (!aligned16(hidden) || !aligned16(h_codes)) return fail(MOE_ERR_ALIGN, "hidden and h_codes must be 16-byte aligned");
   st = mfma_up_groups(R, hidden, bank_arg(w13), plan, workspace, L, T, E, H, I, top_k, h_codes, h_scales);
   return st != MOE_OK ? st : ok();
 }
@@ -717,11 +724,13 @@ int moe_fp8_block_mfma_down_groups(const uint8_t* h_codes, const float* h_scales
   Layout L{};
   moe::Plan plan{};
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return fail(MOE_ERR_ARG, "out_dtype %d is not F32/BF16", out_dtype);
+  if (T > 0) {
+    if (!h_codes || !h_scales || !out) return fail(MOE_ERR_ARG, "h_codes, h_scales and out must be non-NULL");
+    if (!aligned16(h_codes) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h_codes and out must be 16-byte aligned");
+  }
   int st = mfma_half_setup(R, logits, w2, "w2", H, I, T, E, H, I, top_k, MOE_ACT_GROUP_FP8_W8A8, workspace,
                            workspace_bytes, &L, &plan);
   if (st != MOE_OK || T == 0) return st;
-  if (!h_codes || !h_scales || !out) return fail(MOE_ERR_ARG, "h_codes, h_scales and out must be non-NULL");
-  if (!aligned16(h_codes) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "h_codes and out must be 16-byte aligned");
   st = mfma_down_groups(R, h_codes, h_scales, bank_arg(w2), plan, workspace, L, T, E, H, I, top_k, out,
                         out_dtype == MOE_BF16);
   return st != MOE_OK ? st : ok();

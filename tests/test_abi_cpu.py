@@ -223,9 +223,36 @@ def test_small_entry_checks(lib):
     assert lib.moe_fp8_block_quantize_rows(FAKE, 4, 8208, FAKE, FAKE, None) == -2
     assert lib.moe_fp8_block_quantize_rows(None, 4, 32, FAKE, FAKE, None) == -1
     assert lib.moe_fp8_block_quantize_rows(ctypes.c_void_p(0x10004), 4, 32, FAKE, FAKE, None) == -4
+    assert lib.moe_fp8_block_quantize_groups(FAKE, 4, 144, FAKE, FAKE, None) == -2  # not whole groups
+    assert lib.moe_fp8_block_quantize_groups(FAKE, 4, 8320, FAKE, FAKE, None) == -2
+    assert lib.moe_fp8_block_quantize_groups(FAKE, -1, 128, FAKE, FAKE, None) == -1
+    assert lib.moe_fp8_block_quantize_groups(None, 4, 128, FAKE, FAKE, None) == -1
+    assert lib.moe_fp8_block_quantize_groups(ctypes.c_void_p(0x10004), 4, 128, FAKE, FAKE, None) == -4
+    assert lib.moe_fp8_block_quantize_groups(None, 0, 128, None, None, None) == 0
     assert lib.moe_fp8_block_decode_e4m3(FAKE, FAKE, -1, None) == -1
     assert lib.moe_fp8_block_decode_e4m3(None, None, 0, None) == 0
     assert lib.moe_fp8_block_encode_e4m3(None, FAKE, 3, None) == -1
+
+
+def test_group_mfma_half_checks(lib):
+    """The MFMA halves (group-scaled and per-row) refuse shapes without whole 128-wide
+    groups, NULL buffers and a short workspace before any HIP call (the routing they enqueue
+    first comes after every check)."""
+    w13, w2 = _bank(2 * 80, 256), _bank(256, 80)
+    up, down = lib.moe_fp8_block_mfma_up_groups, lib.moe_fp8_block_mfma_down_groups
+    assert up(FAKE, FAKE, ctypes.byref(w13), 4, 8, 256, 80, 2, FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    assert down(FAKE, FAKE, FAKE, ctypes.byref(w2), 4, 8, 256, 80, 2, FAKE, 0, FAKE, 1 << 30, None) == -2
+    w13, w2 = _bank(256, 256), _bank(256, 128)
+    assert up(FAKE, FAKE, ctypes.byref(w13), 4, 8, 256, 128, 2, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert down(None, FAKE, FAKE, ctypes.byref(w2), 4, 8, 256, 128, 2, FAKE, 0, FAKE, 1 << 30, None) == -1
+    assert lib.moe_fp8_block_mfma_up(FAKE, FAKE, ctypes.byref(w13), 4, 8, 256, 128, 2, None, FAKE, 1 << 30,
+                                     None) == -1
+    assert lib.moe_fp8_block_mfma_down(FAKE, FAKE, ctypes.byref(w2), 4, 8, 256, 128, 2, None, 0, FAKE, 1 << 30,
+                                       None) == -1
+    assert up(FAKE, FAKE, ctypes.byref(w13), 4, 8, 256, 128, 2, FAKE, FAKE, FAKE, 16, None) == -5
+    assert down(FAKE, FAKE, FAKE, ctypes.byref(w2), 4, 8, 256, 128, 2, FAKE, 7, FAKE, 1 << 30, None) == -1
+    assert down(FAKE, FAKE, FAKE, ctypes.byref(w2), 4, 8, 256, 128, 2, FAKE, 0, FAKE, 16, None) == -5
+    assert up(None, None, ctypes.byref(w13), 0, 8, 256, 128, 2, None, None, None, 0, None) == 0
 
 
 def test_binding_refuses_a_missing_library(tmp_path):

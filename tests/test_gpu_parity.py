@@ -767,16 +767,20 @@ def test_graph_replays_match_eager(decode_banks, path, T):
         assert torch.equal(out, eager), f"replay {rep}"
 
 
-@pytest.mark.parametrize("path", ["gather", "stream", "mfma"])
+@pytest.mark.parametrize("path", ["gather", "stream", "mfma", "mfma_group"])
 @pytest.mark.parametrize("E,k,T", [(1, 1, 3), (4, 4, 2), (8, 8, 5)])
 def test_degenerate_routings(path, E, k, T):
     """One expert (a plain SwiGLU FFN) and top_k = E (every expert routed, a dense softmax
-    mixture), on every path."""
+    mixture), on every path (and MFMA with group-fp8 activations); the last token's hidden
+    state is all zero (activation scale 1, h = 0 in every group)."""
     c = W.make_case("decode", T=T, seed=71 + E, device=DEV, E=E, H=256, I=128, top_k=k, bias_std=0.1)
+    c.hidden[-1] = 0
     say("degenerate", path, E, k, T)
-    act = 1 if path == "mfma" else 0
+    act = {"mfma": 1, "mfma_group": 3}.get(path, 0)
     out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
-                          force_path=PATHS[path], return_routing=True)
+                          force_path=PATHS[path.split("_")[0]], return_routing=True,
+                          act_mode=M.ACT_GROUP_FP8 if path == "mfma_group" else M.ACT_PATH)
+    assert info["act_mode"] == act
     res = oracle_out(c, act_mode=act)
     assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
     check_out(out, res, act, f"degenerate {path} E={E} k={k}")
