@@ -20,11 +20,14 @@ Also reported on the same JSON line:
                 timed with HIP events the library attaches to that kernel's dispatch on
                 its own stream (moe_fp8_block_forward_timed), against the 8 TB/s HBM peak;
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded sample;
-  prefill_T4096, prefill_T16384, large_T1
-                the same measurement (fewer steps) at the prefill workload (E=256, H=2048,
-                I=512, top_k=8, uniform logits; tokens/s and % of fp8 MFMA peak) and the
-                large-expert decode workload (H=7168, I=2048; routed GB/s), each with its
-                dominant kernel's roofline (--no-extra skips them).
+  sweep_T4, sweep_T16, sweep_T64, prefill_T4096, prefill_T16384, prefill_T16384_group_fp8,
+  large_T1
+                the same measurement (fewer steps) at the decode banks with Zipf(1.1) expert
+                popularity at T = 4, 16, 64 (the path the gate picks; routed GB/s), the
+                prefill workload (E=256, H=2048, I=512, top_k=8, uniform logits; tokens/s and
+                % of fp8 MFMA peak; also with group-fp8 activations) and the large-expert
+                decode workload (H=7168, I=2048; routed GB/s), each with its dominant
+                kernel's roofline (--no-extra skips them).
 
   python bench.py [--steps K] [--warmup W] [--workload decode|sweep|large|prefill] [--T T]
                   [--path auto|gather|stream|mfma] [--act path|group_fp8]
@@ -83,7 +86,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and large-expert figures")
+    ap.add_argument("--no-extra", action="store_true", help="skip the sweep, prefill and large-expert figures")
     ap.add_argument("--kernel-steps", type=int, default=64, help="steps timed per kernel with events")
     ap.add_argument("--copy-calibration", action="store_true", help="copy 1 GiB three times and exit")
     ap.add_argument("--traffic-record", action="store_true", help="write profiles/traffic_<kernel>_<workload>.json")
@@ -260,6 +263,52 @@ def _forward_timed_kernels(M, L, hip, cases, outs, ws, fopts, T, E, H, I, k, nk,
     return {n: sum(v) for n, v in per_kernel.items()}
 
 
+def _pad128(n: int) -> int:
+    return (n + 127) // 128 * 128
+
+
+def kernel_work(kernel, path, act, T, H, I, k, mean_de, w13_b, w2_b):
+    """Algorithmic HBM bytes and flops of one launch of a GEMM kernel (None, None for the
+    others): the routed experts' codes and scales (mean_de of them), the activations it
+    reads and the results it writes, in the layout the path uses."""
+    P = T * k
+    if kernel not in ("gemm1", "gemm2"):
+        return None, None
+    flops = (4.0 if kernel == "gemm1" else 2.0) * P * H * I
+    if path != "mfma":  # W8A16: bf16 x, float h; GATHER's GEMM2 writes the output row
+        if kernel == "gemm1":
+            return mean_de * w13_b + T * H * 2 + P * I * 4, flops
+        return mean_de * w2_b + P * I * 4 + T * H * 2, flops
+    group = act == "group_fp8"
+    parts = -(-_pad128(I) // 512)
+    if kernel == "gemm1":
+        x = T * H + T * (H // 128) * 4 if group else T * _pad128(H) + T * 4
+        h = P * I + P * (I // 128) * 4 if group else P * I * 4
+        return mean_de * w13_b + x + h, flops
+    h = P * I + P * (I // 128) * 4 if group else P * _pad128(I) + P * 4
+    y = parts * P * (H * 2 + -(-H // 32))
+    return mean_de * w2_b + h + y, flops
+
+
+def roofline_of(nbytes, flops, ms):
+    """The roofline a kernel sits under: HBM if its bytes at 8 TB/s take longer than its
+    flops at the fp8 matrix-core peak, else the matrix cores; achieved = that quantity over
+    the measured duration. Both fractions are kept."""
+    if nbytes is None:
+        return dict(bound=None, achieved=None, peak=None, unit=None, frac=None)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (FP8_PEAK_TFLOPS * 1e12)
+    if hbm_bound:
+        r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        r = dict(bound="mfma", achieved=round(tfl, 2), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                 frac=round(tfl / FP8_PEAK_TFLOPS, 4))
+    r.update(hbm_frac=round(gbs / HBM_PEAK_GBS, 4), mfma_frac=round(tfl / FP8_PEAK_TFLOPS, 4),
+             algorithmic_bytes=round(nbytes), algorithmic_flops=round(flops))
+    return r
+
+
 def measure(wl, T, steps, warmup, sets, replicas, path, act, seed, kernel_steps, quiet=False):
     """Times `steps` whole forwards of one workload and returns its figures.
 
@@ -363,22 +412,8 @@ def measure(wl, T, steps, warmup, sets, replicas, path, act, seed, kernel_steps,
     dom_ms = per_kernel[dom]
     mean_de = float(np.mean(d_e))
     flops = 6.0 * T * k * H * I
-    if info["path"] == "mfma":
-        share = {"gemm1": 2.0 / 3.0, "gemm2": 1.0 / 3.0}.get(dom)
-        achieved = flops * share / (dom_ms * 1e-3) / 1e12 if share else None
-        roofline = dict(bound="mfma", achieved=round(achieved, 2) if achieved else None, peak=FP8_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4) if achieved else None)
-    else:
-        # algorithmic bytes of one launch of the dominant kernel
-        if dom == "gemm1":
-            kb = mean_de * w13_b + T * H * 2 + T * k * I * 4
-        elif dom == "gemm2":
-            kb = mean_de * w2_b + T * k * I * 4 + T * H * 2
-        else:
-            kb = None
-        achieved = kb / (dom_ms * 1e-3) / 1e9 if kb else None
-        roofline = dict(bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=HBM_PEAK_GBS,
-                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4) if achieved else None)
+    kb, kf = kernel_work(dom, info["path"], act, T, H, I, k, mean_de, w13_b, w2_b)
+    roofline = roofline_of(kb, kf, dom_ms)
     roofline["traffic"] = committed_traffic(dom, traffic_key(wl, T, act))
     roofline["kernel"] = dom
     roofline["kernel_ms"] = round(dom_ms, 5)
@@ -416,6 +451,9 @@ def summary(m):
 # warmup, input sets, bank replicas, activations). One replica suffices where a forward
 # already touches more than the 256 MB Infinity Cache holds.
 EXTRAS = [
+    ("sweep_T4", "sweep", 4, 512, 64, 32, 4, "path"),
+    ("sweep_T16", "sweep", 16, 256, 32, 16, 4, "path"),
+    ("sweep_T64", "sweep", 64, 128, 16, 8, 2, "path"),
     ("prefill_T4096", "prefill", 4096, 40, 4, 4, 1, "path"),
     ("prefill_T16384", "prefill", 16384, 12, 2, 2, 1, "path"),
     ("prefill_T16384_group_fp8", "prefill", 16384, 12, 2, 2, 1, "group_fp8"),
