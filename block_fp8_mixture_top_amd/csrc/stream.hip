@@ -328,8 +328,18 @@ __global__ __launch_bounds__(kThreads) void gemm2_gather_kernel(const float* __r
                                                                 const float* __restrict__ wts, int H, int I,
                                                                 int k, void* __restrict__ out, int out_bf16) {
   __shared__ float red[kThreads / kWave][ROWS];
-  const int t = blockIdx.y;
-  const int n0 = blockIdx.x * ROWS;
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order. When the row tiles come
+  // in multiples of 8, XCD x takes row tiles x, x + 8, ... and within one tile every token in
+  // turn, so the tokens that share an expert read that tile's w2 rows through one L2 one
+  // after another instead of a whole token's work apart.
+  int t = (int)blockIdx.y, tile = (int)blockIdx.x;
+  if (gridDim.x % 8 == 0) {
+    const int L = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    const int x = L & 7, i = L >> 3, T = (int)gridDim.y;
+    t = i % T;
+    tile = (i / T) * 8 + x;
+  }
+  const int n0 = tile * ROWS;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int CPR = I / 16;
   const int F = k * CPR;
