@@ -458,6 +458,7 @@ EXTRAS = [
     ("prefill_T16384", "prefill", 16384, 12, 2, 2, 1, "path"),
     ("prefill_T16384_group_fp8", "prefill", 16384, 12, 2, 2, 1, "group_fp8"),
     ("large_T1", "large", 1, 64, 8, 16, 1, "path"),
+    ("large_T16", "large", 16, 16, 2, 4, 1, "path"),
 ]
 
 

@@ -39,9 +39,11 @@ constexpr int kFuseMaxPairs = kFuseTokens * 32;
 // Workgroup (0, 0) writes the ids and weights for the down GEMM; the weights (double exp and
 // sum) are computed after the weight loads are issued, off the critical path.
 // PER == 0: the slot's expert and pairs come from the sorted plan in global memory.
-// XL (T == 1 with long rows only): the token's x is staged once per workgroup in LDS instead
-// of being held in every lane's registers, which leaves room for more waves per SIMD; one
-// barrier, after the weight reads are issued, publishes it.
+// XL (long rows only): x is staged per workgroup in LDS instead of being held in every
+// lane's registers, which leaves room for more waves per SIMD. With fused routing (T == 1
+// only) the token's x is read before routing and one barrier, after the weight reads are
+// issued, publishes it; with a plan (PER == 0) each pair's x row is read, once the weight
+// reads are issued, and staged between two barriers.
 // A8 (PER == 0 only): the activations are e4m3 codes xq with one scale xs per (token,
 // 128-column group); a 16-code chunk lies in one group, so its block product takes the
 // weight block scale times the group's activation scale.
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     cnt = plan.counts[e];
     pairs = plan.sorted + plan.offsets[e];
   }
-  if constexpr (XL) {
+  if constexpr (XL && PER > 0) {
     // routing waited for the logits, read after x, so x is here: to LDS, freeing registers
 #pragma unroll
     for (int j = 0; j < XQ; ++j) {
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
     sg[m] = scale_value(bg[m], w13.scale_bf16);
     su[m] = scale_value(bu[m], w13.scale_bf16);
   }
-  if constexpr (XL) __syncthreads();  // x in LDS (written before the weight reads were issued)
+  if constexpr (XL && PER > 0) __syncthreads();  // x in LDS (written before the weight reads were issued)
   if constexpr (PER > 0) {
     // the router weights, while the weight codes are in flight
     if (route_wave && blockIdx.x == 0 && blockIdx.y == 0) {
@@ -229,6 +231,19 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a16_kernel(const uint16_t* _
   }
   for (int q = 0; q < cnt; ++q) {
     const int p = single >= 0 ? single : pairs[q];
+    if constexpr (XL && PER == 0) {
+      // this pair's x row into LDS, once every lane is done with the previous one
+      const uint8_t* xb = (const uint8_t*)(hidden + (size_t)(p / k) * H);
+#pragma unroll
+      for (int j = 0; j < XQ; ++j) xr[j] = ld16(xb + (size_t)min((int)threadIdx.x + kThreads * j, 2 * NC - 1) * 16);
+      if (q > 0) __syncthreads();
+#pragma unroll
+      for (int j = 0; j < XQ; ++j) {
+        const int c = (int)threadIdx.x + kThreads * j;
+        if (c < 2 * NC) *(u32x4*)(s_x + c * 16) = xr[j];
+      }
+      __syncthreads();
+    }
     if (!XL && single < 0) {
       if constexpr (A8) {
         const uint8_t* xc = xq + (size_t)(p / k) * H;
@@ -544,8 +559,8 @@ hipError_t g1(const Gemm1Args& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if constexpr (PER > 0 && LPR == kWave && MCH >= 4) {
-    if (a.T == 1) {
+  if constexpr (LPR == kWave && MCH >= 4) {
+    if (PER == 0 || a.T == 1) {
       launch_kernel((gemm1_w8a16_kernel<LPR, MCH, RP, PER, true>), grid, dim3(kThreads), 0, s, a.hidden, a.logits,
                     a.T, a.E, a.w13, a.plan, a.H, a.I, a.k, a.h, a.ids_out, a.w_out, a.xq, a.xs);
       return hipGetLastError();
