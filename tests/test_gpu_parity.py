@@ -294,6 +294,23 @@ def test_odd_shapes_forced(path, H, I):
     check_out(out, oracle_out(c, act_mode=act), act, f"{path} H={H} I={I}")
 
 
+@pytest.mark.parametrize("path", ["gather", "stream"])
+@pytest.mark.parametrize("H,T", [(4096, 1), (4112, 1), (4112, 6), (7168, 9)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_long_rows_staged_x(path, H, T, bias):
+    """Rows of at least 256 chunks of 16 codes stage x in LDS: once per workgroup with fused
+    routing at T=1, and per pair between two barriers with a routing plan (GATHER above four
+    tokens, STREAM always), where a workgroup takes one to several pairs of its expert.
+    H=4112 leaves a last chunk group that only one lane owns."""
+    c = W.make_case("decode", T=T, seed=41, device=DEV, E=16, H=H, I=144, top_k=4,
+                   bias_std=0.3 if bias else None)
+    say("staged x", path, H, T, bias)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS[path])
+    assert info["path"] == path
+    check_out(out, oracle_out(c), 0, f"{path} H={H} T={T} bias={bias}")
+
+
 @pytest.mark.parametrize("path", [None, "gather", "stream", "mfma"])
 @pytest.mark.parametrize("H,I,T", [(144, 80, 1), (144, 80, 3), (2064, 528, 1), (2064, 528, 40), (2064, 528, 300)])
 def test_partial_scale_blocks(path, H, I, T):
