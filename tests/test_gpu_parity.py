@@ -845,6 +845,52 @@ def test_largest_expert_count_and_top_k(path):
     check_out(out[torch.from_numpy(rows).to(DEV)], res, act, f"E=1024 k=32 {path}")
 
 
+def _random_configs(n, seed):
+    """n configurations drawn from a fixed seed: workload style (bank kind and logit
+    distribution), E, top_k (up to 12: past 8 the round-based selection runs), H and I
+    (multiples of 16, or of 128 for group-fp8 activations), T (every fourth 64-160 tokens,
+    where more than 512 pairs take the multi-block sort), the path (or the gate),
+    activations, biases, scale dtype and scale padding."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        E = rng.choice([1, 3, 8, 16, 40, 64, 130])
+        group = rng.random() < 0.3
+        path = rng.choice([None, "gather", "stream", "mfma"])
+        I = 128 * rng.randint(1, 4) if group and (path == "mfma" or rng.random() < 0.5) else 16 * rng.randint(1, 40)
+        out.append(dict(
+            i=i, name=rng.choice(["tiny", "decode", "sweep", "large"]), E=E, k=rng.randint(1, min(E, 12)),
+            H=128 * rng.randint(1, 8) if group else 16 * rng.randint(1, 64), I=I,
+            T=rng.randint(64, 160) if i % 4 == 3 else rng.randint(1, 48),
+            path=path, group=group, bias=rng.random() < 0.3,
+            sdt=rng.choice([torch.float32, torch.bfloat16]), pad=rng.choice(["none", "row16", "slab16"])))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(40, 2027), ids=lambda c: f"cfg{c['i']}")
+def test_random_configurations(cfg):
+    """Seeded random configurations across every option the forward takes, each against the
+    oracle: ids and weights bit for bit, outputs to the float bar in the precision the
+    reported act_mode fixes."""
+    c = W.make_case(cfg["name"], T=cfg["T"], seed=300 + cfg["i"], device=DEV, E=cfg["E"], H=cfg["H"],
+                    I=cfg["I"], top_k=cfg["k"], scale_dtype=cfg["sdt"], pad=cfg["pad"],
+                    bias_std=0.2 if cfg["bias"] else None)
+    say("random", {k: v for k, v in cfg.items() if k != "sdt"}, cfg["sdt"])
+    kw = {} if cfg["path"] is None else {"force_path": PATHS[cfg["path"]]}
+    if cfg["group"]:
+        kw["act_mode"] = M.ACT_GROUP_FP8
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          return_routing=True, **kw)
+    if cfg["path"] is not None:
+        assert info["path"] == cfg["path"]
+    res = oracle_out(c, act_mode=info["act_mode"])
+    assert np.array_equal(info["ids"].cpu().numpy(), res["ids"])
+    assert np.array_equal(info["weights"].cpu().numpy(), res["w32"])
+    check_out(out, res, info["act_mode"], f"random cfg{cfg['i']} {info['path']} act {info['act_mode']}")
+
+
 def test_zero_tokens():
     c = W.make_case("tiny", T=1, seed=1).to(DEV)
     out, info = M.forward(c.hidden[:0], c.logits[:0], c.w13, c.w2, c.top_k, out_dtype=torch.float32)
