@@ -443,6 +443,9 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int fq = wave & 3, th = wave >> 2;  // feature quarter, token half
+  // a token half with no pair of the expert (in an expert's partial last tile) skips its
+  // products; it still copies, reads and meets the barriers like the others
+  const bool idle = th * 64 >= nvalid;  // wave-uniform
   const int r16 = lane & 15, kq = lane >> 4;
   const int lr = lane >> 3, lc = lane & 7;
   const uint8_t* wb = w13.codes + (size_t)e * w13.expert_stride;
@@ -561,7 +564,8 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
         if constexpr (GROUP) nxt.sx[t] = read_sx(rslot, t);
       }
       // gate tiles in group 0, up tiles in group 1
-      if constexpr (GROUP) {
+      if (idle) {
+      } else if constexpr (GROUP) {
         // the group's 8 products, each MFMA issued before the previous one's result is
         // scaled in (a zero block scale gives a zero factor: finite products add nothing)
         constexpr int NJ = 2 * NTT;
