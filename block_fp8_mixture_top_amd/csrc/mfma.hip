@@ -771,14 +771,26 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   __shared__ float s_hs[GROUP ? TP * KB : TP];  // GROUP: [pair][K block of this part]
   __shared__ int s_prow[TP];
 
-  const int nitems = plan.tile_off[E] * PARTS;
+  // Each 128-pair tile gets 2R workgroups (R = 2 where the grid, a bound on the tiles, has
+  // room for it, else 1). When both 64-pair halves of the tile hold pairs, R of them take
+  // each half; when only the first does (an expert's last, small tile, which is every tile
+  // of a small batch), all 2R take that half. The workgroups of a half split its chunks of
+  // output rows (chunk c goes to the one with c % RS == rsi), so a small batch does not
+  // leave each expert's whole w2 stream to one CU.
+  static_assert(PARTS == 2, "two half-tiles per tile");
+  const int ntiles = plan.tile_off[E];
+  const int R = max(1, min(2, (int)gridDim.x / max(2 * ntiles, 1)));
+  const int nitems = ntiles * 2 * R;
   const int L = xcd_item(blockIdx.x, nitems);  // consecutive items of an expert share its w2 in L2
   if (L >= nitems) return;
-  const int tile = L / PARTS, part = L - tile * PARTS;
+  const int tile = L / (2 * R), sub = L - tile * 2 * R;
   const int e = find_expert(plan.tile_off, E, tile);
-  const int pos0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM + part * TP;
-  if (pos0 >= plan.offsets[e + 1]) return;
+  const int t0 = plan.offsets[e] + (tile - plan.tile_off[e]) * kTM;  // the tile's first pair
   const int pos_end = plan.offsets[e + 1];
+  const bool two = pos_end - t0 > TP;  // both halves hold pairs
+  const int part = two ? sub / R : 0;
+  const int RS = two ? R : 2 * R, rsi = two ? sub - part * R : sub;
+  const int pos0 = t0 + part * TP;
   const int nvalid = pos_end - pos0 < TP ? pos_end - pos0 : TP;
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
@@ -826,9 +838,11 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   __syncthreads();                     // and everyone's, before the ring is refilled
 
   // chunks holding outputs of this wave: those with c * NCH + FW * wave < H (the last one
-  // may hold fewer than FW: H is a multiple of 16, so each feature tile is in range or out)
+  // may hold fewer than FW: H is a multiple of 16, so each feature tile is in range or out);
+  // this workgroup takes c = rsi, rsi + RS, ...
   const int nch = (H - wave * FW + NCH - 1) / NCH;
-  const int nst = nch * KB;
+  const int nchr = nch > rsi ? (nch - rsi + RS - 1) / RS : 0;
+  const int nst = nchr * KB;
   // w2 copy i covers rows 8i .. 8i+7 of the wave's FW; chunk c adds c * NCH rows. Rows past H
   // read the last row and chunks past a partial last K block the row's last chunk (finite
   // codes, multiplied by the zero h codes there); neither result is stored.
@@ -843,7 +857,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   const uint32_t ktail = (uint32_t)(I - (nkb_all - 1) * 128);  // bytes of the last K block
   uint8_t* myring = ring + wave * kRing2 * WB;
   auto issue = [&](int st) {
-    const int c = st / KB, kb = st - c * KB;
+    const int ci = st / KB, kb = st - ci * KB;
+    const int c = rsi + ci * RS;
     uint8_t* slot = myring + (st % kRing2) * WB;
     const bool ptail = kb0 + kb == nkb_all - 1 && ktail < 128;  // uniform
     if (!ptail && c * NCH + wave * FW + FW <= H) {
@@ -863,12 +878,13 @@ __global__ __launch_bounds__(256, 1) void gemm2_mfma_kernel(const uint8_t* __res
   for (int st = 0; st < kRing2 - 1; ++st)
     if (st < nst) issue(st);
   f32x4 acc[NF][NP];
-  // (chunk c, K block kb) is stage st = c * KB + kb; kb is unrolled so that the h operands
-  // are indexed statically and stay in registers
-  for (int c = 0; c < nch; ++c) {
+  // (this workgroup's chunk ci, K block kb) is stage st = ci * KB + kb; kb is unrolled so
+  // that the h operands are indexed statically and stay in registers
+  for (int ci = 0; ci < nchr; ++ci) {
+    const int c = rsi + ci * RS;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int st = c * KB + kb;
+      const int st = ci * KB + kb;
       // stage st has landed once at most min(kRing2 - 2, nst - 1 - st) younger stages remain
       wait_stage<NCP>(min(kRing2 - 2, nst - 1 - st));
       // the slot of stage st - 1 is refilled next, so this wave's reads of it must have
@@ -966,7 +982,10 @@ hipError_t g2m(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan
 template <bool GROUP>
 hipError_t gemm2_parts(const uint8_t* hq, const float* hs, const BankArg& w2, const Plan& plan, int E, int P, int H,
                        int I, _Float16* y, int8_t* yexp, hipStream_t s) {
-  const int nblocks = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
+  // two workgroups per half-tile at most; for small batches (few tiles, most of them an
+  // expert's only, small one) the grid leaves room for them
+  const int nb = (int)mfma_tiles_bound(P, E) * (kTM / (kG2PairTiles * 16));
+  const int nblocks = nb < 1024 ? 2 * nb : nb;
   const int nkb = mfma_pad(I) / 128;
   for (int part = 0; part < mfma_k_parts(I); ++part) {
     const int kb0 = part * kMfmaPartBlocks;
