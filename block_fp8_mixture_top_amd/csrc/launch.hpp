@@ -36,7 +36,7 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint
 
 // Pair counts up to this sort in one workgroup; larger ones use the three-pass sort (at
 // 4096 pairs the single workgroup took about 100 us more than the three passes).
-constexpr int kSmallSortPairs = 512;
+constexpr int kSmallSortPairs = 4096;  // pairs the one-workgroup sort takes
 
 // A bank as the kernels see it.
 struct BankArg {

@@ -103,12 +103,19 @@ __device__ void wave_active_list(const int* counts, int E, int slots, int32_t* a
   }
 }
 
-// Routing and the whole sort in one workgroup, for small P. ROUTE: 16 waves route the tokens
-// (each reading its next token's logits while it selects the current one's experts);
-// otherwise the ids come from route_topk_kernel, which spreads the tokens over many CUs (the
-// selection of many tokens on the one CU of this workgroup is bound by its VALU). Then counts
-// in LDS, offsets by a wave scan, and one wave walks the pairs in rounds of 64, placing each
-// by its rank among equal experts.
+// Routing and the whole sort in one workgroup, for P <= kSmallSortPairs. ROUTE: 16 waves
+// route the tokens (each reading its next token's logits while it selects the current one's
+// experts); otherwise the ids come from route_topk_kernel, which spreads the tokens over many
+// CUs (the selection of many tokens on the one CU of this workgroup is bound by its VALU).
+// Up to kWavePlacePairs pairs: counts by LDS atomics, offsets by a wave scan, and one wave
+// walks the pairs in rounds of 64, placing each by its rank among equal experts. More: the
+// counting sort of the multi-block kernels, in LDS: wave w takes the pairs of chunk w
+// (consecutive, in rounds of 64), counts them per expert by ballots, a scan over the waves
+// gives each (wave, expert) its base, a wave scan the expert offsets, and each wave places
+// its pairs by their rank among equal experts. Both are stable, and no atomics decide an
+// order.
+constexpr int kWavePlacePairs = 512;  // up to here one wave places all pairs
+
 template <int PER, bool ROUTE>
 __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ weights,
@@ -117,9 +124,11 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
                                                           int32_t* __restrict__ sorted, int32_t* act,
                                                           int32_t* n_act, int slots, int tile_m,
                                                           int32_t* tile_off) {
+  constexpr int NW = 1024 / kWave;
   __shared__ int cnt[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS];
   __shared__ int sid[kSmallSortPairs];
+  __shared__ int wcnt[NW][MAX_EXPERTS];  // pairs of wave w's chunk per expert, then their base
   __shared__ __align__(16) uint64_t s_cand[ROUTE ? 1024 / kWave : 1][kWave];
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int nwaves = blockDim.x / kWave;
@@ -147,8 +156,64 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
     }
   }
   }
+  if (P <= kWavePlacePairs) {
+    // few pairs: counts by LDS atomics, one wave places them all in rounds of 64
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[sid[p]], 1);
+    __syncthreads();
+    if (wave == 0) {
+      wave_exclusive_offsets(cnt, E, off);
+    } else if (wave == 1) {
+      wave_active_list(cnt, E, slots, act, n_act, tile_m, tile_off);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      counts[e] = cnt[e];
+      offsets[e] = off[e];
+    }
+    if (threadIdx.x == 0) offsets[E] = P;
+    __syncthreads();
+    if (wave == 0) {
+      // off[] becomes the running insertion point of each expert
+      for (int base = 0; base < P; base += kWave) {
+        const int p = base + lane;
+        const bool valid = p < P;
+        const int e = valid ? sid[p] : 0;
+        const uint64_t m = match_lanes(e, valid);
+        const int rank = __popcll(m & ((1ull << lane) - 1ull));
+        const int pos = valid ? off[e] + rank : 0;
+        if (valid) sorted[pos] = p;
+        // the highest lane of each group advances the insertion point
+        const bool last = valid && (m >> lane) == 1ull;
+        if (last) off[e] = pos + 1;
+      }
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < NW * E; i += blockDim.x) wcnt[i / E][i % E] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += blockDim.x) atomicAdd(&cnt[sid[p]], 1);
+  // wave w's chunk: pairs [w * C, min(P, (w + 1) * C)), C a multiple of 64
+  const int C = (P + NW * kWave - 1) / (NW * kWave) * kWave;
+  const int lo = wave * C, hi = min(P, lo + C);
+  for (int base = lo; base < hi; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < hi;
+    const int e = valid ? sid[p] : 0;
+    const uint64_t m = match_lanes(e, valid);
+    // the highest lane of each group adds the group's size
+    if (valid && (m >> lane) == 1ull) wcnt[wave][e] += __popcll(m);
+  }
+  __syncthreads();
+  // per expert: the total, and each wave's base within the expert (exclusive over waves)
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = wcnt[w][e];
+      wcnt[w][e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
   __syncthreads();
   if (wave == 0) {
     wave_exclusive_offsets(cnt, E, off);
@@ -161,21 +226,20 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(const float* __restric
     offsets[e] = off[e];
   }
   if (threadIdx.x == 0) offsets[E] = P;
-  __syncthreads();
-  if (wave == 0) {
-    // off[] becomes the running insertion point of each expert
-    for (int base = 0; base < P; base += kWave) {
-      const int p = base + lane;
-      const bool valid = p < P;
-      const int e = valid ? sid[p] : 0;
-      const uint64_t m = match_lanes(e, valid);
-      const int rank = __popcll(m & ((1ull << lane) - 1ull));
-      const int pos = valid ? off[e] + rank : 0;
-      if (valid) sorted[pos] = p;
-      // the highest lane of each group advances the insertion point
-      const bool last = valid && (m >> lane) == 1ull;
-      if (last) off[e] = pos + 1;
-    }
+  // wcnt[wave][] becomes this wave's running insertion point of each expert (only this wave
+  // reads or writes its row from here on)
+  for (int e = lane; e < E; e += kWave) wcnt[wave][e] += off[e];
+  for (int base = lo; base < hi; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < hi;
+    const int e = valid ? sid[p] : 0;
+    const uint64_t m = match_lanes(e, valid);
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    const int pos = valid ? wcnt[wave][e] + rank : 0;
+    if (valid) sorted[pos] = p;
+    // the highest lane of each group advances the insertion point
+    const bool last = valid && (m >> lane) == 1ull;
+    if (last) wcnt[wave][e] = pos + 1;
   }
 }
 

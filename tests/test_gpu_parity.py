@@ -186,10 +186,12 @@ def test_route_ties_and_extremes():
     _route_check(flat.repeat(10, 1), 8, "E=256 equal rows, T=40")
 
 
-@pytest.mark.parametrize("T,E,k", [(16, 256, 8), (17, 256, 8), (64, 64, 8), (512, 128, 1), (40, 1024, 12)])
+@pytest.mark.parametrize("T,E,k", [(16, 256, 8), (17, 256, 8), (64, 64, 8), (512, 128, 1), (40, 1024, 12),
+                                   (512, 256, 8), (513, 256, 8), (4096, 1024, 1), (342, 1024, 12), (100, 3, 3)])
 def test_route_plan_boundaries(T, E, k):
     """Around the routing split: up to 16 tokens are routed inside the one-workgroup sort,
-    more are routed by one wave per token first; up to 512 pairs use the one-workgroup sort."""
+    more are routed by one wave per token first; up to 4096 pairs use the one-workgroup sort
+    (16 waves, each counting and placing a chunk), more the multi-block one."""
     g = torch.Generator().manual_seed(T * 1000 + E + k)
     _route_check(torch.randn(T, E, generator=g) * 1.5, k, f"T={T} E={E} k={k}")
 
