@@ -144,6 +144,10 @@ def traffic_record(args):
     sym = KERNEL_SYMBOLS[args.kernel]
     if args.act == "group_fp8" and args.kernel == "quant":
         sym = "quant_groups_bf16"
+    if args.act == "path" and args.kernel == "route" and args.workload == "prefill":
+        # the MFMA forward's routing kernel, which also quantises x; the plain top-k launches
+        # that count each input set's routed experts before timing are left out
+        sym = "route_topk_quant"
     kf, nf = _counter_per_dispatch(args.fetch_dir, "FETCH_SIZE", sym)
     kw, nw = _counter_per_dispatch(args.write_dir, "WRITE_SIZE", sym)
     rec = {

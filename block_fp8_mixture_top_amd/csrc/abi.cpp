@@ -286,7 +286,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
                  moe_run_info* info, void* stream, void* const* events, int n_events, int32_t* kinds,
                  size_t* checks_only = nullptr);
 int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
-            const Layout& L, int T, int E, int H, int I, int top_k, float* hf);
+            const Layout& L, int T, int E, int H, int I, int top_k, float* hf, bool xq_ready = false);
 int mfma_down(Runner& R, const float* hf, const moe::BankArg& b2, const moe::Plan& plan, void* workspace,
               const Layout& L, int T, int E, int H, int I, int top_k, void* out, int out_bf16);
 int mfma_up_groups(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
@@ -494,12 +494,23 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
                      (act_mode == MOE_ACT_PATH ? moe::gemm1_fused_route_ok(T, top_k)
                                                : act_mode == MOE_ACT_GROUP_FP8 && moe::gemm1_fused_qx_ok(T, top_k, H));
   const int tile_m = path == MOE_PATH_MFMA ? moe::kMfmaTileM : 0;
+  // per-row MFMA activations: where the routing starts with a top-k kernel of one wave per
+  // token, that kernel also quantises the token's row of x
+  const bool xq_route = path == MOE_PATH_MFMA && act_mode == MOE_ACT_ROW_FP8 && moe::route_topk_first(T, top_k);
   if (!fused) {
-    for (int st = 0; st < moe::route_kernel_count(T, top_k); ++st)
+    for (int st = 0; st < moe::route_kernel_count(T, top_k); ++st) {
+      if (st == 0 && xq_route) {
+        RUN(MOE_K_ROUTE,
+            moe::launch_route_topk_quant(logits, hidden, T, E, top_k, H, moe::mfma_pad(H), ids, w,
+                                         at<uint8_t>(workspace, L.xq), at<float>(workspace, L.xs), s),
+            "route launch");
+        continue;
+      }
       RUN(st == 0 ? MOE_K_ROUTE : MOE_K_SORT,
           moe::launch_route_stage(st, logits, T, E, top_k, ids, w, counts, offsets, sorted, act, n_act, slots,
                                   tile_m, tile_off, at<void>(workspace, L.scratch), s),
           "route launch");
+    }
   }
   const moe::Plan plan{ids, w, counts, offsets, sorted, act, tile_off};
 
@@ -532,7 +543,7 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
     if (st2 != MOE_OK) return st2;
   } else {
     float* hf = at<float>(workspace, L.h);
-    int st2 = mfma_up(R, hidden, b13, plan, workspace, L, T, E, H, I, top_k, hf);
+    int st2 = mfma_up(R, hidden, b13, plan, workspace, L, T, E, H, I, top_k, hf, xq_route);
     if (st2 == MOE_OK) st2 = mfma_down(R, hf, b2, plan, workspace, L, T, E, H, I, top_k, out, out_bf16);
     if (st2 != MOE_OK) return st2;
   }
@@ -540,15 +551,15 @@ int forward_impl(const uint16_t* hidden, const float* logits, const moe_fp8_bank
   return ok();
 }
 
-// The MFMA path's first half: x quantised per token, then GEMM1 + silu*up into hf (float,
-// [P, I] in sorted-position order).
+// The MFMA path's first half: x quantised per token (unless the routing kernel did it:
+// xq_ready), then GEMM1 + silu*up into hf (float, [P, I] in sorted-position order).
 int mfma_up(Runner& R, const uint16_t* hidden, const moe::BankArg& b13, const moe::Plan& plan, void* workspace,
-            const Layout& L, int T, int E, int H, int I, int top_k, float* hf) {
+            const Layout& L, int T, int E, int H, int I, int top_k, float* hf, bool xq_ready) {
   hipStream_t s = R.s;
   const int64_t P = (int64_t)T * top_k;
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
   float* xs = at<float>(workspace, L.xs);
-  RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, moe::mfma_pad(H), xq, xs, s), "quant launch");
+  if (!xq_ready) RUN(MOE_K_QUANT, moe::launch_quant_rows_bf16(hidden, T, H, moe::mfma_pad(H), xq, xs, s), "quant launch");
   RUN(MOE_K_GEMM1, moe::launch_gemm1_mfma(xq, xs, b13, plan, E, (int)P, H, I, top_k, hf, s), "gemm1 mfma launch");
   return MOE_OK;
 }

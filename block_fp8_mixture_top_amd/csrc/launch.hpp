@@ -64,6 +64,13 @@ size_t sort_scratch_bytes(int P, int E);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 
+// route_topk_kernel's routing with x's rows quantised as launch_quant_rows_bf16 quantises
+// them (codes[T, ostride], scales[T]), in one kernel; it stands in for stage 0 of
+// launch_route_stage when route_topk_first(T, k).
+bool route_topk_first(int T, int k);
+hipError_t launch_route_topk_quant(const float* logits, const uint16_t* x, int T, int E, int k, int H, int ostride,
+                                   int32_t* ids, float* w, uint8_t* codes, float* scales, hipStream_t s);
+
 // Routing plus the sort: 1 kernel (route and sort in one workgroup) for P <= kSmallSortPairs,
 // else 4 (top-k, then histogram, chunk scan and scatter); stage picks which.
 int route_kernel_count(int T, int k);

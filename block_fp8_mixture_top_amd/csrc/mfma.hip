@@ -25,6 +25,7 @@
 // combine kernel sums the slots of a token in slot order with the router weights.
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant.hpp"
 
 namespace moe {
 
@@ -40,71 +41,16 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
 
 // ---------------------------------------------------------------- per-row quantisation
 
-// x / s rounded to float, for a float x and a positive float s given as rs = 1 / (double)s:
-// the double product float((double)x * rs) is within 2^-52 of x / s, and x / s is never a
-// float rounding midpoint (an odd 25-bit significand times s cannot fit the 24 bits of x)
-// and otherwise lies at least 2^-49 from one (x - m * s is a multiple of the 49-bit product's
-// ulp), so it rounds to the correctly rounded float quotient that a division gives, at the
-// cost of one double multiply per value and one double division per row. Quotients small
-// enough to be float subnormals round to the e4m3 zero either way.
-__device__ __forceinline__ float quot(float x, double rs) { return (float)((double)x * rs); }
-
-// Zero codes for columns cols .. ostride - 1 of a code row (ostride - cols < 512, both
-// multiples of 8): the padding that makes a partial last 128-wide K block multiply zeros.
-__device__ __forceinline__ void zero_tail(uint8_t* row, int cols, int ostride, int lane) {
-  const int c = cols + lane * 8;
-  if (c < ostride) *(uint2*)(row + c) = make_uint2(0u, 0u);
-}
-
-// One wave per row of bf16: amax, scale = amax/448 (1 if zero), codes = e4m3(x/scale).
-// Lane l holds the 8-value pieces l, l + 64, ... of the row: IT of them, all read up front
-// (pieces past the row end read its last piece and are ignored), so the row is read from
-// memory once and every read is in flight together. Code rows are ostride bytes apart, the
-// columns past cols zero.
+// One wave per row of bf16 (quant_row_bf16).
 template <int IT>
 __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int rows, int cols,
                                                               int ostride, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
   const int row = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
   if (row >= rows) return;
-  const int lane = lane_id();
-  const uint16_t* xr = x + (size_t)row * cols;
   u32x4 v[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int c = lane * 8 + it * kWave * 8;
-    v[it] = *(const u32x4*)(xr + (c < cols ? c : cols - 8));
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const bool in = lane * 8 + it * kWave * 8 < cols;
-    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_lo(w[q])) : 0.0f);
-      amax = __builtin_fmaxf(amax, in ? __builtin_fabsf(bf16_hi(w[q])) : 0.0f);
-    }
-  }
-  amax = wave_max(amax);
-  const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
-  const double rs = 1.0 / (double)s;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int c = lane * 8 + it * kWave * 8;
-    if (c >= cols) continue;
-    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-    uint32_t out[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t a = enc2(quot(bf16_lo(w[2 * q]), rs), quot(bf16_hi(w[2 * q]), rs));
-      const uint32_t b = enc2(quot(bf16_lo(w[2 * q + 1]), rs), quot(bf16_hi(w[2 * q + 1]), rs));
-      out[q] = a | (b << 16);
-    }
-    *(uint2*)(codes + (size_t)row * ostride + c) = make_uint2(out[0], out[1]);
-  }
-  zero_tail(codes + (size_t)row * ostride, cols, ostride, lane);
-  if (lane == 0) scales[row] = s;
+  quant_row_bf16_load<IT>(x, row, cols, v);
+  quant_row_bf16_store<IT>(v, row, cols, ostride, codes, scales);
 }
 
 // The same with one scale per 128-column group (cols a multiple of 128): a 512-column piece
@@ -713,23 +659,27 @@ __global__ __launch_bounds__(512, 1) void gemm1_mfma_kernel(const uint8_t* __res
 
 // ---------------------------------------------------------------- GEMM2
 
-// One workgroup per (expert, 64-pair half of a 128-pair tile), 4 waves, one per SIMD; the
-// two halves of a tile are consecutive items on one XCD, so the second reads the expert's w2
-// from L2. A = w2 rows (features), B = the half's h codes (pairs as rows; e4m3 per (token,
+// A work item is one 64-pair half of an expert's 128-pair tile, or a share of its output
+// chunks when the grid has room (a tile's workgroups are consecutive items on one XCD, so
+// they read the expert's w2 from L2 after the first): R = min(2, grid / (2 * tiles)) workgroups
+// per half of a tile with two non-empty halves, 2R on the one half of a tile that has a
+// single one, taking chunks c with c % (workgroups of the half) == their index. 4 waves, one
+// per SIMD. A = w2 rows (features), B = the half's h codes (pairs as rows; e4m3 per (token,
 // slot) row, scale amax/448, from the row quantiser), so lane (r16, kq) of a 16x16 result
 // holds outputs 4kq..4kq+3 of pair r16: four consecutive outputs of one pair, written with
 // one 8-byte store. The H outputs go in chunks of 256; wave w multiplies outputs 64w ..
-// 64w+63 of each chunk (4 feature tiles) by the half's 64 pairs (4 pair tiles, whose h codes
-// stay in registers for every K block). Each wave streams its own w2 rows, (chunk, K block)
-// after (chunk, K block), through a private kRing2-deep LDS ring with kRing2 - 1 stages in
-// flight and no barriers. The workgroups of an expert read its w2 rows in the same order at
-// about the same time, so one fetch into L2 serves all of them (measured on gfx950: starting
-// each at a different chunk fetched 2.4 times the bytes from beyond L2 for no clear gain). Each MFMA starts from zero and its block product is scaled into
-// the accumulator on the VALU while the next MFMA runs. Each pair's y row = s_h * W2 h is
-// written once, in fp16 with one power-of-two exponent per kYGroup (32) outputs; the combine
-// kernel applies the router weights. (Measured on gfx950: 128 pairs per workgroup, a ring
-// shared by the four waves, or two waves per SIMD were no faster; the w2 stream is held back
-// by the vector memory path's pending-miss stalls, not by the bytes per MFMA.)
+// 64w+63 of each of its chunks (4 feature tiles) by the half's 64 pairs (4 pair tiles, whose
+// h codes stay in registers for every K block). Each wave streams its own w2 rows, (chunk, K
+// block) after (chunk, K block), through a private kRing2-deep LDS ring with kRing2 - 1
+// stages in flight and no barriers. The workgroups of an expert read its w2 rows in the same
+// order at about the same time, so one fetch into L2 serves all of them (measured on gfx950:
+// starting each at a different chunk fetched 2.4 times the bytes from beyond L2 for no clear
+// gain). Each MFMA starts from zero and its block product is scaled into the accumulator on
+// the VALU while the next MFMA runs. Each pair's y row = s_h * W2 h is written once, in fp16
+// with one power-of-two exponent per kYGroup (32) outputs; the combine kernel applies the
+// router weights. (Measured on gfx950: 128 pairs per workgroup, a ring shared by the four
+// waves, or two waves per SIMD were no faster; the w2 stream is held back by the vector
+// memory path's pending-miss stalls, not by the bytes per MFMA.)
 constexpr int kRing2 = 4;
 constexpr int kG2PairTiles = 4;  // pair tiles per workgroup (16 pairs each)
 

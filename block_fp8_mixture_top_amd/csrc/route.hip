@@ -9,6 +9,7 @@
 // in which atomics land.
 #include "common.hpp"
 #include "launch.hpp"
+#include "quant.hpp"
 #include "topk.hpp"
 
 namespace moe {
@@ -30,6 +31,36 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     ids[(size_t)t * k + lane] = id;
     weights[(size_t)t * k + lane] = w;
   }
+}
+
+// The same, and the token's row of x (bf16, H columns) quantised to e4m3 with one scale
+// per row, codes ostride bytes apart (the MFMA path's activations). The logits are read
+// first, then the row, and the selection waits for the logits only, so the row's reads are
+// in flight while the experts are chosen.
+template <int PER, int IT>
+__global__ __launch_bounds__(256) void route_topk_quant_kernel(const float* __restrict__ logits,
+                                                               const uint16_t* __restrict__ x, int T, int E, int k,
+                                                               int H, int ostride, int32_t* __restrict__ ids,
+                                                               float* __restrict__ weights,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+  __shared__ __align__(16) uint64_t s_cand[256 / kWave][kWave];
+  const int lane = lane_id();
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+  if (t >= T) return;
+  float f[PER];
+  wave_topk_load<PER, false>(logits + (size_t)t * E, E, f);
+  u32x4 v[IT];
+  quant_row_bf16_load<IT>(x, t, H, v);
+  int id;
+  float l;
+  wave_topk_select_lds<PER>(f, E, k, s_cand[threadIdx.x / kWave], id, l);
+  const float w = wave_topk_weight(l, k);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    weights[(size_t)t * k + lane] = w;
+  }
+  quant_row_bf16_store<IT>(v, t, H, ostride, codes, scales);
 }
 
 // Lanes of the wave whose 10-bit key equals this lane's key (E <= 1024).
@@ -341,6 +372,34 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 // Up to this many tokens (one per wave of the plan kernel) are routed inside it; more go to
 // route_topk_kernel first.
 constexpr int kPlanRouteTokens = 16;
+
+template <int PER>
+static void launch_route_topk_quant_per(int it, dim3 grid, const float* logits, const uint16_t* x, int T, int E,
+                                        int k, int H, int ostride, int32_t* ids, float* w, uint8_t* codes,
+                                        float* scales, hipStream_t s) {
+#define MOE_RTQ(IT)                                                                                            \
+  launch_kernel((route_topk_quant_kernel<PER, IT>), grid, dim3(256), 0, s, logits, x, T, E, k, H, ostride, ids, \
+                w, codes, scales)
+  if (it <= 1) MOE_RTQ(1);
+  else if (it <= 2) MOE_RTQ(2);
+  else if (it <= 4) MOE_RTQ(4);
+  else if (it <= 8) MOE_RTQ(8);
+  else MOE_RTQ(16);
+#undef MOE_RTQ
+}
+
+bool route_topk_first(int T, int k) { return T * k > kSmallSortPairs || T > kPlanRouteTokens; }
+
+hipError_t launch_route_topk_quant(const float* logits, const uint16_t* x, int T, int E, int k, int H, int ostride,
+                                   int32_t* ids, float* w, uint8_t* codes, float* scales, hipStream_t s) {
+  const int it = (H + kWave * 8 - 1) / (kWave * 8);
+  if (H <= 0 || H % 8 != 0 || it > 16 || ostride < H || ostride - H >= kWave * 8 || ostride % 8 != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid((T + 3) / 4);
+  MOE_TOPK_DISPATCH(E, launch_route_topk_quant_per<PER>(it, grid, logits, x, T, E, k, H, ostride, ids, w, codes,
+                                                        scales, s));
+  return hipGetLastError();
+}
 
 int route_kernel_count(int T, int k) {
   const int P = T * k;

@@ -234,9 +234,11 @@ int moe_fp8_block_forward_static(const uint16_t* hidden, const float* logits, co
 
 /* Kernel kinds named by moe_fp8_block_forward_timed. */
 typedef enum {
-  MOE_K_ROUTE = 1,    /* top-k and weights */
+  MOE_K_ROUTE = 1,    /* top-k and weights (on MFMA with per-row activations, when a top-k
+                         kernel starts the routing, it also quantises x) */
   MOE_K_SORT = 2,     /* token-to-expert sort (one or three kernels) */
-  MOE_K_QUANT = 3,    /* e4m3 activation quantisation (MFMA path; group-fp8 on any path) */
+  MOE_K_QUANT = 3,    /* e4m3 activation quantisation (MFMA path, where the routing kernel
+                         does not; group-fp8 on any path) */
   MOE_K_HQUANT = 4,   /* per-(token, slot) e4m3 quantisation of h before the down GEMM (MFMA path) */
   MOE_K_GEMM1 = 5,    /* gate/up GEMM with silu(gate)*up */
   MOE_K_GEMM2 = 6,    /* down GEMM (with the combine on GATHER) */

@@ -315,6 +315,25 @@ def test_long_rows_staged_x(path, H, T, bias):
     check_out(out, oracle_out(c), 0, f"{path} H={H} T={T} bias={bias}")
 
 
+@pytest.mark.parametrize("E,H,T,k", [(40, 16, 17, 4), (100, 528, 40, 6), (300, 1040, 17, 8), (1024, 528, 20, 8),
+                                     (200, 4112, 17, 4), (64, 8192, 17, 2), (64, 2064, 600, 8)])
+def test_mfma_route_quantises_x(E, H, T, k):
+    """On MFMA with per-row activations, the kernel that selects each token's experts also
+    quantises the token's row of x whenever the routing starts with a top-k kernel (more
+    than 16 tokens, or more than 4096 pairs as at T=600, k=8). Its logit widths (64 to 1024
+    experts per wave) and row lengths (one to sixteen 512-column pieces, partial last ones):
+    ids and weights bit for bit against the oracle's routing, the output within the bar."""
+    c = W.make_case("decode", T=T, seed=61 + E, device=DEV, E=E, H=H, I=144, top_k=k)
+    say("route+quant", E, H, T, k)
+    out, info = M.forward(c.hidden, c.logits, c.w13, c.w2, c.top_k, out_dtype=torch.float32,
+                          force_path=PATHS["mfma"], return_routing=True)
+    assert info["path"] == "mfma"
+    ids, _, w32 = O.route(c.logits.cpu().numpy(), k)
+    assert np.array_equal(info["ids"].cpu().numpy(), ids)
+    assert np.array_equal(info["weights"].cpu().numpy(), w32)
+    check_out(out, oracle_out(c, act_mode=1), 1, f"E={E} H={H} T={T} k={k}")
+
+
 @pytest.mark.parametrize("path", [None, "gather", "stream", "mfma"])
 @pytest.mark.parametrize("H,I,T", [(144, 80, 1), (144, 80, 3), (2064, 528, 1), (2064, 528, 40), (2064, 528, 300)])
 def test_partial_scale_blocks(path, H, I, T):
