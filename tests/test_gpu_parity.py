@@ -892,7 +892,7 @@ def _random_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("cfg", _random_configs(40, 2027), ids=lambda c: f"cfg{c['i']}")
+@pytest.mark.parametrize("cfg", _random_configs(200, 2027), ids=lambda c: f"cfg{c['i']}")
 def test_random_configurations(cfg):
     """Seeded random configurations across every option the forward takes, each against the
     oracle: ids and weights bit for bit, outputs to the float bar in the precision the
