@@ -892,7 +892,29 @@ def _random_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("cfg", _random_configs(200, 2027), ids=lambda c: f"cfg{c['i']}")
+def _random_large_configs(n, seed):
+    """As _random_configs at larger sizes: E from 64 to 1000, T from 17 to 1200 (routing by a
+    top-k kernel; more than 4096 pairs take the multi-block sort), H and I up to 1024 and
+    768."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        E = rng.choice([64, 200, 256, 512, 1000])
+        group = rng.random() < 0.3
+        path = rng.choice([None, "gather", "stream", "mfma"])
+        I = 128 * rng.randint(1, 4) if group and (path == "mfma" or rng.random() < 0.5) else 16 * rng.randint(1, 48)
+        out.append(dict(
+            i=i, big=True, name=rng.choice(["decode", "sweep", "large"]), E=E, k=rng.randint(1, min(E, 12)),
+            H=128 * rng.randint(1, 8) if group else 16 * rng.randint(1, 64), I=I, T=rng.randint(17, 1200),
+            path=path, group=group, bias=rng.random() < 0.3,
+            sdt=rng.choice([torch.float32, torch.bfloat16]), pad=rng.choice(["none", "row16", "slab16"])))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(200, 2027) + _random_large_configs(16, 2029),
+                         ids=lambda c: f"{'big' if c.get('big') else 'cfg'}{c['i']}")
 def test_random_configurations(cfg):
     """Seeded random configurations across every option the forward takes, each against the
     oracle: ids and weights bit for bit, outputs to the float bar in the precision the
